@@ -1,0 +1,190 @@
+"""Python access to the CPU oracle (oracle/q8ref.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may use it; the HIP library never does.  The
+oracle is plain scalar C with no code shared with the HIP path; this module
+only marshals numpy arrays into it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "q8ref.c")
+LIB = os.path.join(HERE, "libq8ref.so")
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+LAYOUT_ROWS = 0
+LAYOUT_PACKED = 1
+LAYOUT_ACT = 2
+QK = 32
+BLOCK_BYTES = 34
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    cmd = ["gcc", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm", "-lpthread"]
+    out = subprocess.run(cmd, capture_output=True, text=True)
+    if out.returncode != 0:
+        raise RuntimeError("oracle build failed:\n" + out.stderr)
+    if verbose and out.stderr:
+        print(out.stderr)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.q8ref_f32_to_f16.argtypes = [ctypes.c_float]
+        L.q8ref_f32_to_f16.restype = ctypes.c_uint16
+        L.q8ref_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.q8ref_f16_to_f32.restype = ctypes.c_float
+        L.q8ref_f32_to_f16_n.argtypes = [P, P, I64]
+        L.q8ref_f16_to_f32_n.argtypes = [P, P, I64]
+        L.q8ref_quantize_block.argtypes = [P, P, P]
+        L.q8ref_quantize_block.restype = ctypes.c_uint16
+        L.q8ref_quantize_rows.argtypes = [P, I64, I64, I64, I, P]
+        L.q8ref_pack.argtypes = [P, I64, I64, P]
+        L.q8ref_unpack.argtypes = [P, I64, I64, P]
+        L.q8ref_block_terms.argtypes = [P, I64, P, I64, I64, P, P]
+        L.q8ref_matmul.argtypes = [P, I64, P, I64, I64, P, I64, P, I]
+        L.q8ref_matmul_points.argtypes = [P, I64, P, I64, I64, P, P, I64, P, P]
+        L.q8ref_grouped_matmul.argtypes = [P, I64, I, P, I64, I, P, I64, I64, I64, I64, P, P, I]
+        for name in ("q8ref_quantize_rows", "q8ref_pack", "q8ref_unpack", "q8ref_block_terms",
+                     "q8ref_matmul", "q8ref_matmul_points", "q8ref_grouped_matmul"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} returned {rc}")
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().q8ref_f32_to_f16_n(_p(x), _p(out), x.size)
+    return out
+
+
+def f16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().q8ref_f16_to_f32_n(_p(h), _p(out), h.size)
+    return out
+
+
+def quantize_block(x: np.ndarray):
+    """-> (q int8[32], stored fp16 bits, fp32 d)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.size == QK
+    q = np.empty(QK, dtype=np.int8)
+    d = np.empty(1, dtype=np.float32)
+    bits = lib().q8ref_quantize_block(_p(x), _p(q), _p(d))
+    return q, int(bits), float(d[0])
+
+
+def quantized_bytes(rows: int, k: int) -> int:
+    return rows * (k // QK) * BLOCK_BYTES
+
+
+def quantize_rows(x: np.ndarray, layout: int = LAYOUT_ACT) -> np.ndarray:
+    """fp32 [rows][k] (any row stride) -> uint8 buffer in layout ROWS or ACT."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    if x.strides[1] != 4:
+        x = np.ascontiguousarray(x)
+    rows, k = x.shape
+    ld = x.strides[0] // 4
+    out = np.empty(quantized_bytes(rows, k), dtype=np.uint8)
+    _check(lib().q8ref_quantize_rows(_p(x), ld, rows, k, layout, _p(out)), "quantize_rows")
+    return out
+
+
+def act_planes(buf: np.ndarray, rows: int, k: int):
+    """Split an ACT buffer into (int8 [rows][k], fp16 bits [rows][k/32])."""
+    q = buf[: rows * k].view(np.int8).reshape(rows, k)
+    d = buf[rows * k: rows * k + rows * (k // QK) * 2].view(np.uint16).reshape(rows, k // QK)
+    return q, d
+
+
+def rows_planes(buf: np.ndarray, n: int, k: int):
+    """Split a ROWS buffer into (int8 [n][k], fp16 bits [n][k/32])."""
+    blocks = buf.reshape(n, k // QK, BLOCK_BYTES)
+    d = np.ascontiguousarray(blocks[:, :, :2]).view(np.uint16).reshape(n, k // QK)
+    q = np.ascontiguousarray(blocks[:, :, 2:]).view(np.int8).reshape(n, k)
+    return q, d
+
+
+def pack(w_rows: np.ndarray, n: int, k: int) -> np.ndarray:
+    w_rows = np.ascontiguousarray(w_rows, dtype=np.uint8)
+    out = np.empty(quantized_bytes(n, k), dtype=np.uint8)
+    _check(lib().q8ref_pack(_p(w_rows), n, k, _p(out)), "pack")
+    return out
+
+
+def unpack(w_packed: np.ndarray, n: int, k: int) -> np.ndarray:
+    w_packed = np.ascontiguousarray(w_packed, dtype=np.uint8)
+    out = np.empty(quantized_bytes(n, k), dtype=np.uint8)
+    _check(lib().q8ref_unpack(_p(w_packed), n, k, _p(out)), "unpack")
+    return out
+
+
+def block_terms(x_act: np.ndarray, m: int, w_rows: np.ndarray, n: int, k: int):
+    """-> (s int32 [m][n][k/32], t float32 [m][n][k/32])."""
+    nb = k // QK
+    s = np.empty((m, n, nb), dtype=np.int32)
+    t = np.empty((m, n, nb), dtype=np.float32)
+    _check(lib().q8ref_block_terms(_p(np.ascontiguousarray(x_act)), m, _p(np.ascontiguousarray(w_rows)),
+                                   n, k, _p(s), _p(t)), "block_terms")
+    return s, t
+
+
+def matmul(x_act: np.ndarray, m: int, w_rows: np.ndarray, n: int, k: int, threads: int = 1):
+    """-> (y float32 [m][n], S float64 [m][n] = sum of |block terms|)."""
+    y = np.empty((m, n), dtype=np.float32)
+    S = np.empty((m, n), dtype=np.float64)
+    _check(lib().q8ref_matmul(_p(np.ascontiguousarray(x_act)), m, _p(np.ascontiguousarray(w_rows)),
+                              n, k, _p(y), n, _p(S), threads), "matmul")
+    return y, S
+
+
+def matmul_points(x_act: np.ndarray, m: int, w_rows: np.ndarray, n: int, k: int, mi, ni):
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    y = np.empty(mi.size, dtype=np.float32)
+    S = np.empty(mi.size, dtype=np.float64)
+    _check(lib().q8ref_matmul_points(_p(np.ascontiguousarray(x_act)), m, _p(np.ascontiguousarray(w_rows)),
+                                     n, k, _p(mi), _p(ni), mi.size, _p(y), _p(S)), "matmul_points")
+    return y, S
+
+
+def grouped_matmul(x_act: np.ndarray, x_rows: int, x_per_pair: bool, ids: np.ndarray, w_rows: np.ndarray,
+                   n_experts: int, expert_stride: int, n: int, k: int, threads: int = 1):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    tokens, topk = ids.shape
+    y = np.empty((tokens * topk, n), dtype=np.float32)
+    S = np.empty((tokens * topk, n), dtype=np.float64)
+    _check(lib().q8ref_grouped_matmul(_p(np.ascontiguousarray(x_act)), x_rows, int(bool(x_per_pair)), _p(ids),
+                                      tokens, topk, _p(np.ascontiguousarray(w_rows)), n_experts, expert_stride,
+                                      n, k, _p(y), _p(S), threads), "grouped_matmul")
+    return y, S

@@ -1,0 +1,312 @@
+/*
+ * q8ref.c: the CPU oracle.  TEST INFRASTRUCTURE ONLY (see q8ref.h for what it
+ * follows and for the readings it takes where the pages are silent).
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * (x86-64 evaluates float arithmetic in SSE single precision, so every fp32
+ * operation below is one IEEE-754 rounding; -ffp-contract=off forbids fused
+ * multiply-adds).
+ */
+#include "q8ref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QK 32        /* values per block */
+#define BLK 34       /* bytes per block: fp16 scale + 32 int8 */
+#define PR 64        /* rows per packed record */
+#define PB 8         /* blocks per packed record */
+#define REC (PR * PB * BLK) /* 17408 bytes */
+
+/* ------------------------------------------------------------------------ */
+/* binary16 codec                                                           */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* fp32 -> fp16, round to nearest, ties to even; results too large become
+ * infinity, results too small become subnormal or zero. */
+uint16_t q8ref_f32_to_f16(float f) {
+    uint32_t u = f2u(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t e32 = (u >> 23) & 0xffu;
+    uint32_t man = u & 0x7fffffu;
+    if (e32 == 0xffu) {
+        if (man == 0) return sign | 0x7c00u;              /* infinity */
+        return (uint16_t)(sign | 0x7e00u | (man >> 13));   /* quiet NaN, payload kept */
+    }
+    if (e32 == 0) return sign;  /* fp32 zero/subnormal: below half the smallest fp16 subnormal */
+    int e = (int)e32 - 127;     /* unbiased exponent, value = 1.man * 2^e */
+    if (e > 15) return sign | 0x7c00u;
+    uint32_t full = man | 0x800000u; /* 24-bit significand, value = full * 2^(e-23) */
+    if (e >= -14) {
+        /* normal fp16: keep 11 significant bits */
+        uint32_t h = ((uint32_t)(e + 15) << 10) | (man >> 13);
+        uint32_t rem = man & 0x1fffu;
+        if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1; /* carry may reach inf: correct */
+        return (uint16_t)(sign | h);
+    }
+    /* subnormal fp16: value / 2^-24 = full * 2^(e+1); shift right by s = -(e+1) */
+    int s = -(e + 1);
+    if (s > 25) return sign;
+    uint32_t kq = full >> s;
+    uint32_t rem = full & ((1u << s) - 1u);
+    uint32_t half = 1u << (s - 1);
+    if (rem > half || (rem == half && (kq & 1u))) kq += 1; /* may become the smallest normal: correct */
+    return (uint16_t)(sign | kq);
+}
+
+float q8ref_f16_to_f32(uint16_t h) {
+    uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1fu;
+    uint32_t man = h & 0x3ffu;
+    if (e == 0x1fu) return u2f(sign | 0x7f800000u | (man << 13));
+    if (e == 0) {
+        if (man == 0) return u2f(sign);
+        /* subnormal: man * 2^-24; normalise into an fp32 normal */
+        int shift = 0;
+        while (!(man & 0x400u)) { man <<= 1; shift++; }
+        man &= 0x3ffu;
+        uint32_t e32 = (uint32_t)(127 - 15 - shift + 1);
+        return u2f(sign | (e32 << 23) | (man << 13));
+    }
+    return u2f(sign | ((e - 15 + 127) << 23) | (man << 13));
+}
+
+void q8ref_f32_to_f16_n(const float *in, uint16_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; i++) out[i] = q8ref_f32_to_f16(in[i]);
+}
+
+void q8ref_f16_to_f32_n(const uint16_t *in, float *out, int64_t n) {
+    for (int64_t i = 0; i < n; i++) out[i] = q8ref_f16_to_f32(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* quantization                                                             */
+/* ------------------------------------------------------------------------ */
+
+uint16_t q8ref_quantize_block(const float *x, int8_t *q, float *d_out) {
+    float amax = 0.0f;
+    for (int j = 0; j < QK; j++) {
+        float a = fabsf(x[j]);
+        if (a > amax) amax = a;
+    }
+    float d = amax / 127.0f;
+    for (int j = 0; j < QK; j++) {
+        if (d == 0.0f) {
+            q[j] = 0;
+        } else {
+            float r = x[j] / d;       /* one correctly rounded division */
+            q[j] = (int8_t)roundf(r); /* nearest integer, halves away from zero */
+        }
+    }
+    if (d_out) *d_out = d;
+    return q8ref_f32_to_f16(d);
+}
+
+static void put16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)(v & 0xffu); p[1] = (uint8_t)(v >> 8); }
+static uint16_t get16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int layout, uint8_t *out) {
+    if (!x || !out || rows < 0 || k <= 0 || ld_x < k) return Q8REF_EARG;
+    if (k % QK) return Q8REF_ESHAPE;
+    if (layout != 0 && layout != 2) return Q8REF_EARG;
+    int64_t nb = k / QK;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            int8_t q[QK];
+            uint16_t d = q8ref_quantize_block(x + r * ld_x + b * QK, q, NULL);
+            if (layout == 0) {
+                uint8_t *blk = out + (r * nb + b) * BLK;
+                put16(blk, d);
+                memcpy(blk + 2, q, QK);
+            } else {
+                memcpy(out + r * k + b * QK, q, QK);
+                put16(out + rows * k + (r * nb + b) * 2, d);
+            }
+        }
+    }
+    return Q8REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* packed layout                                                            */
+/* ------------------------------------------------------------------------ */
+
+static int64_t packed_q_offset(int64_t row, int64_t col, int64_t k) {
+    int64_t T = row / PR, r = row % PR;
+    int64_t G = col / (QK * PB), c = col % (QK * PB);
+    int64_t bb = c / QK, h = (c % QK) / 16, j = c % 16;
+    return (T * (k / (QK * PB)) + G) * REC + bb * 2048 + h * 1024 + r * 16 + j;
+}
+
+static int64_t packed_d_offset(int64_t row, int64_t block, int64_t k) {
+    int64_t T = row / PR, r = row % PR;
+    int64_t G = block / PB, bb = block % PB;
+    return (T * (k / (QK * PB)) + G) * REC + PR * PB * QK + r * 16 + bb * 2;
+}
+
+int q8ref_pack(const uint8_t *w_rows, int64_t n, int64_t k, uint8_t *w_packed) {
+    if (!w_rows || !w_packed || n <= 0 || k <= 0) return Q8REF_EARG;
+    if (n % PR || k % (QK * PB)) return Q8REF_ESHAPE;
+    int64_t nb = k / QK;
+    for (int64_t row = 0; row < n; row++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = w_rows + (row * nb + b) * BLK;
+            memcpy(w_packed + packed_d_offset(row, b, k), blk, 2);
+            for (int64_t j = 0; j < QK; j++)
+                w_packed[packed_q_offset(row, b * QK + j, k)] = blk[2 + j];
+        }
+    }
+    return Q8REF_OK;
+}
+
+int q8ref_unpack(const uint8_t *w_packed, int64_t n, int64_t k, uint8_t *w_rows) {
+    if (!w_rows || !w_packed || n <= 0 || k <= 0) return Q8REF_EARG;
+    if (n % PR || k % (QK * PB)) return Q8REF_ESHAPE;
+    int64_t nb = k / QK;
+    for (int64_t row = 0; row < n; row++) {
+        for (int64_t b = 0; b < nb; b++) {
+            uint8_t *blk = w_rows + (row * nb + b) * BLK;
+            memcpy(blk, w_packed + packed_d_offset(row, b, k), 2);
+            for (int64_t j = 0; j < QK; j++)
+                blk[2 + j] = w_packed[packed_q_offset(row, b * QK + j, k)];
+        }
+    }
+    return Q8REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* block dot and matmul                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Integer dot of block b of activation row mi with block b of weight row ni. */
+static int32_t block_dot(const uint8_t *x_act, int64_t k, int64_t mi, const uint8_t *w_rows, int64_t ni, int64_t b) {
+    const int8_t *qx = (const int8_t *)(x_act + mi * k + b * QK);
+    const int8_t *qw = (const int8_t *)(w_rows + (ni * (k / QK) + b) * BLK + 2);
+    int32_t s = 0;
+    for (int j = 0; j < QK; j++) s += (int32_t)qx[j] * (int32_t)qw[j];
+    return s;
+}
+
+/* t = fp32(s * (Dw * Dx)): Dw * Dx is exact in fp32, so one rounding. */
+static float block_term(const uint8_t *x_act, int64_t m, int64_t k, int64_t mi, const uint8_t *w_rows, int64_t ni,
+                        int64_t b, int32_t *s_out) {
+    int64_t nb = k / QK;
+    int32_t s = block_dot(x_act, k, mi, w_rows, ni, b);
+    float dx = q8ref_f16_to_f32(get16(x_act + m * k + (mi * nb + b) * 2));
+    float dw = q8ref_f16_to_f32(get16(w_rows + (ni * nb + b) * BLK));
+    float scale = dw * dx;
+    if (s_out) *s_out = s;
+    return (float)s * scale;
+}
+
+static void output(const uint8_t *x_act, int64_t m, const uint8_t *w_rows, int64_t k, int64_t mi, int64_t ni,
+                   float *y, double *S) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t b = 0; b < k / QK; b++) {
+        float t = block_term(x_act, m, k, mi, w_rows, ni, b, NULL);
+        acc += (double)t;
+        mag += fabs((double)t);
+    }
+    *y = (float)acc;
+    if (S) *S = mag;
+}
+
+int q8ref_block_terms(const uint8_t *x_act, int64_t m, const uint8_t *w_rows, int64_t n, int64_t k,
+                      int32_t *s, float *t) {
+    if (!x_act || !w_rows || m <= 0 || n <= 0 || k <= 0) return Q8REF_EARG;
+    if (k % QK) return Q8REF_ESHAPE;
+    int64_t nb = k / QK;
+    for (int64_t mi = 0; mi < m; mi++)
+        for (int64_t ni = 0; ni < n; ni++)
+            for (int64_t b = 0; b < nb; b++) {
+                int32_t sv;
+                float tv = block_term(x_act, m, k, mi, w_rows, ni, b, &sv);
+                if (s) s[(mi * n + ni) * nb + b] = sv;
+                if (t) t[(mi * n + ni) * nb + b] = tv;
+            }
+    return Q8REF_OK;
+}
+
+typedef struct {
+    const uint8_t *x_act;
+    int64_t m;
+    const uint8_t *w_rows;
+    int64_t n, k, ld_y;
+    float *y;
+    double *S;
+    int64_t n0, n1;
+} mm_job;
+
+static void *mm_worker(void *arg) {
+    mm_job *j = (mm_job *)arg;
+    for (int64_t ni = j->n0; ni < j->n1; ni++)
+        for (int64_t mi = 0; mi < j->m; mi++)
+            output(j->x_act, j->m, j->w_rows, j->k, mi, ni, &j->y[mi * j->ld_y + ni],
+                   j->S ? &j->S[mi * j->n + ni] : NULL);
+    return NULL;
+}
+
+int q8ref_matmul(const uint8_t *x_act, int64_t m, const uint8_t *w_rows, int64_t n, int64_t k,
+                 float *y, int64_t ld_y, double *S, int threads) {
+    if (!x_act || !w_rows || !y || m <= 0 || n <= 0 || k <= 0 || ld_y < n) return Q8REF_EARG;
+    if (k % QK) return Q8REF_ESHAPE;
+    if (threads < 1) threads = 1;
+    if (threads > n) threads = (int)n;
+    mm_job *jobs = (mm_job *)calloc((size_t)threads, sizeof(mm_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!jobs || !tid) { free(jobs); free(tid); return Q8REF_EARG; }
+    for (int i = 0; i < threads; i++) {
+        mm_job jb = {x_act, m, w_rows, n, k, ld_y, y, S, n * i / threads, n * (i + 1) / threads};
+        jobs[i] = jb;
+    }
+    for (int i = 1; i < threads; i++) pthread_create(&tid[i], NULL, mm_worker, &jobs[i]);
+    mm_worker(&jobs[0]);
+    for (int i = 1; i < threads; i++) pthread_join(tid[i], NULL);
+    free(jobs);
+    free(tid);
+    return Q8REF_OK;
+}
+
+int q8ref_matmul_points(const uint8_t *x_act, int64_t m, const uint8_t *w_rows, int64_t n, int64_t k,
+                        const int64_t *mi, const int64_t *ni, int64_t count, float *y, double *S) {
+    if (!x_act || !w_rows || !mi || !ni || !y || m <= 0 || n <= 0 || k <= 0 || count < 0) return Q8REF_EARG;
+    if (k % QK) return Q8REF_ESHAPE;
+    for (int64_t i = 0; i < count; i++) {
+        if (mi[i] < 0 || mi[i] >= m || ni[i] < 0 || ni[i] >= n) return Q8REF_EARG;
+        output(x_act, m, w_rows, k, mi[i], ni[i], &y[i], S ? &S[i] : NULL);
+    }
+    return Q8REF_OK;
+}
+
+int q8ref_grouped_matmul(const uint8_t *x_act, int64_t x_rows, int x_per_pair, const int32_t *ids,
+                         int64_t tokens, int topk, const uint8_t *w_rows, int64_t n_experts,
+                         int64_t expert_stride, int64_t n, int64_t k, float *y, double *S, int threads) {
+    if (!x_act || !ids || !w_rows || !y || tokens <= 0 || topk <= 0 || n_experts <= 0 || n <= 0 || k <= 0)
+        return Q8REF_EARG;
+    if (k % QK) return Q8REF_ESHAPE;
+    int64_t pairs = tokens * topk;
+    if (x_rows != (x_per_pair ? pairs : tokens)) return Q8REF_ESHAPE;
+    if (threads < 1) threads = 1;
+    int64_t nb = k / QK;
+    /* One single-row activation view per pair: the row's int8 values and its
+     * scales, copied into a 1-row ACT buffer so the matmul above applies. */
+    uint8_t *one = (uint8_t *)malloc((size_t)(nb * BLK));
+    if (!one) return Q8REF_EARG;
+    for (int64_t p = 0; p < pairs; p++) {
+        int32_t e = ids[p];
+        if (e < 0 || e >= n_experts) { free(one); return Q8REF_EARG; }
+        int64_t xr = x_per_pair ? p : p / topk;
+        memcpy(one, x_act + xr * k, (size_t)k);
+        memcpy(one + k, x_act + x_rows * k + xr * nb * 2, (size_t)(nb * 2));
+        int rc = q8ref_matmul(one, 1, w_rows + (int64_t)e * expert_stride, n, k, y + p * n, n,
+                              S ? S + p * n : NULL, threads);
+        if (rc) { free(one); return rc; }
+    }
+    free(one);
+    return Q8REF_OK;
+}

@@ -1,0 +1,98 @@
+/*
+ * q8ref: the CPU oracle for the Q8_0 block-quantized matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Plain, slow, scalar C that states the method's
+ * definition directly.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load it.  It shares no code, header,
+ * table or constant with the HIP library, and the HIP library never calls it.
+ *
+ * Sources of the definition (the three pages studied for this project):
+ *  - Q8_0 block: one fp16 scale followed by 32 int8 values, 34 bytes
+ *    ("Ember packed Q8 decode" post, row-contiguous source diagram).
+ *  - Quantization: per 32-value block, scale d = amax / 127, values rounded to
+ *    the nearest integer; activations are quantized with the same per-block
+ *    scheme as the weights ("ferro" README, "How the iGPU path is fast",
+ *    item 1; weights converted to Q8_0 at load time, "Using LFM2.5").
+ *  - Block dot: exact int32 sum of 32 int8 products scaled by both fp16
+ *    scales, block results reduced in fp32 per output row.
+ *  - Packed tiles hold the same bytes as the row-contiguous blocks, only
+ *    reordered: 544 bytes per 16 blocks ("Ember packed Q8 decode" post).
+ *
+ * Readings where the pages are silent (each is listed in the project's
+ * design notes):
+ *  - "round to nearest" ties go away from zero (C roundf);
+ *  - x / d is one correctly rounded fp32 division by the fp32 scale d; the
+ *    stored scale is d rounded to fp16 (round to nearest even, gradual
+ *    underflow);
+ *  - an all-zero block has d = 0, every q = 0 and a +0 stored scale;
+ *  - the oracle's output is sum_b t_b accumulated in fp64 and rounded once to
+ *    fp32, where t_b = fp32(s_b * (D_w * D_x)) (the fp16 x fp16 product is
+ *    exact in fp32, so t_b carries one rounding); any fp32 summation order is
+ *    within |err| <= 1e-5 * sum_b |t_b|, which is the acceptance bound.
+ *
+ * Layout codes (the oracle's own copies of the format definitions):
+ *  0 ROWS   : row-contiguous Q8_0, rows x (k/32) blocks of [fp16 d][32 x int8].
+ *  1 PACKED : records of 64 rows x 8 blocks (17,408 bytes = 512 blocks x 34),
+ *             record (T, G) at byte (T * (k/256) + G) * 17408; inside it the
+ *             int8 value of row 64T+r, column 256G + 32bb + 16h + j sits at
+ *             bb*2048 + h*1024 + r*16 + j, and the fp16 scale of (r, bb) at
+ *             16384 + r*16 + bb*2.  Needs n % 64 == 0 and k % 256 == 0.
+ *  2 ACT    : planar activations, int8 [rows][k] followed by fp16
+ *             [rows][k/32]; rows * k / 32 * 34 bytes in all.
+ */
+#ifndef Q8REF_H
+#define Q8REF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define Q8REF_OK 0
+#define Q8REF_EARG 1
+#define Q8REF_ESHAPE 2
+
+/* IEEE binary16 <-> binary32 from the bit definitions. */
+uint16_t q8ref_f32_to_f16(float f);
+float q8ref_f16_to_f32(uint16_t h);
+void q8ref_f32_to_f16_n(const float *in, uint16_t *out, int64_t n);
+void q8ref_f16_to_f32_n(const uint16_t *in, float *out, int64_t n);
+
+/* One 32-value block: writes q[32], returns the stored fp16 scale bits and
+ * (if d_out) the fp32 scale d used for the division. */
+uint16_t q8ref_quantize_block(const float *x, int8_t *q, float *d_out);
+
+/* rows x k fp32 (row stride ld_x elements) -> layout 0 (ROWS) or 2 (ACT). */
+int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int layout, uint8_t *out);
+
+/* ROWS <-> PACKED byte permutations. */
+int q8ref_pack(const uint8_t *w_rows, int64_t n, int64_t k, uint8_t *w_packed);
+int q8ref_unpack(const uint8_t *w_packed, int64_t n, int64_t k, uint8_t *w_rows);
+
+/* Per-block integer dots s[m][n][b] and terms t[m][n][b] (tiny shapes). */
+int q8ref_block_terms(const uint8_t *x_act, int64_t m, const uint8_t *w_rows, int64_t n, int64_t k,
+                      int32_t *s, float *t);
+
+/* y[m][n] (row stride ld_y) and S[m][n] = sum_b |t_b| (may be NULL),
+ * threads >= 1 split the output rows n; results do not depend on threads. */
+int q8ref_matmul(const uint8_t *x_act, int64_t m, const uint8_t *w_rows, int64_t n, int64_t k,
+                 float *y, int64_t ld_y, double *S, int threads);
+
+/* Selected outputs: y[i] = output (mi[i], ni[i]) for i < count. */
+int q8ref_matmul_points(const uint8_t *x_act, int64_t m, const uint8_t *w_rows, int64_t n, int64_t k,
+                        const int64_t *mi, const int64_t *ni, int64_t count, float *y, double *S);
+
+/* Routed experts: pair p = t * topk + j uses expert ids[p] and activation
+ * row (x_per_pair ? p : t); y is [tokens * topk][n].  Expert e's ROWS
+ * weights start at byte e * expert_stride of w_rows. */
+int q8ref_grouped_matmul(const uint8_t *x_act, int64_t x_rows, int x_per_pair, const int32_t *ids,
+                         int64_t tokens, int topk, const uint8_t *w_rows, int64_t n_experts,
+                         int64_t expert_stride, int64_t n, int64_t k, float *y, double *S, int threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
