@@ -1,0 +1,138 @@
+// C ABI of libq8: argument validation, device check and dispatch.
+//
+// Every check that can be made from the arguments alone runs before the
+// first HIP call, so a caller learns about a bad request even without a GPU.
+// The device check then confirms the current device is gfx950 (cached per
+// device); other hardware is rejected rather than served by a fallback.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/q8.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int8_t> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return Q8_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int8_t known = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (known == 1) return Q8_OK;
+        if (known == -1) return Q8_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return Q8_ERR_DEVICE;
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? Q8_OK : Q8_ERR_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+uint32_t q8_abi_version(void) { return Q8_ABI_VERSION; }
+
+const char *q8_status_str(int status) {
+    switch (status) {
+        case Q8_OK: return "Q8_OK";
+        case Q8_ERR_ARG: return "Q8_ERR_ARG: invalid argument";
+        case Q8_ERR_SHAPE: return "Q8_ERR_SHAPE: unsupported shape";
+        case Q8_ERR_ALIGN: return "Q8_ERR_ALIGN: misaligned pointer or stride";
+        case Q8_ERR_WORKSPACE: return "Q8_ERR_WORKSPACE: workspace missing or too small";
+        case Q8_ERR_DEVICE: return "Q8_ERR_DEVICE: no gfx950 device";
+        case Q8_ERR_LAUNCH: return "Q8_ERR_LAUNCH: kernel launch failed";
+        default: return "Q8_ERR_UNKNOWN";
+    }
+}
+
+size_t q8_quantized_bytes(int64_t rows, int64_t k) {
+    if (rows < 0 || k < 0 || k % Q8_BLOCK) return 0;
+    return (size_t)rows * (size_t)(k / Q8_BLOCK) * Q8_BLOCK_BYTES;
+}
+
+int q8_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int layout, void *q_out,
+                     hipStream_t stream) {
+    if (!x || !q_out || rows < 0 || k <= 0 || ld_x < k) return Q8_ERR_ARG;
+    if (layout != Q8_LAYOUT_ROWS && layout != Q8_LAYOUT_ACT) return Q8_ERR_ARG;
+    if (k % Q8_BLOCK) return Q8_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q_out) || ld_x % 4) return Q8_ERR_ALIGN;
+    if (rows == 0) return Q8_OK;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_quantize(x, ld_x, rows, k, layout, q_out, stream));
+}
+
+int q8_repack_weights(const void *w_rows, int64_t n, int64_t k, void *w_packed, hipStream_t stream) {
+    if (!w_rows || !w_packed || n <= 0 || k <= 0) return Q8_ERR_ARG;
+    if (n % Q8_TILE_ROWS || k % (Q8_BLOCK * Q8_TILE_BLOCKS)) return Q8_ERR_SHAPE;
+    if (!aligned16(w_rows) || !aligned16(w_packed)) return Q8_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_repack(w_rows, n, k, w_packed, stream));
+}
+
+size_t q8_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    if (m <= 0 || n <= 0 || k <= 0 || k % (Q8_BLOCK * Q8_TILE_BLOCKS)) return 0;
+    if (m > Q8_GEMV_MAX_ROWS) return 0;
+    return q8k::gemv_workspace_bytes(m, n, k);
+}
+
+int q8_matmul(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y, int64_t ld_y,
+              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!x_q || !w || !y || m <= 0 || n <= 0 || k <= 0 || ld_y < n) return Q8_ERR_ARG;
+    if (layout != Q8_LAYOUT_ROWS && layout != Q8_LAYOUT_PACKED) return Q8_ERR_ARG;
+    if (k % (Q8_BLOCK * Q8_TILE_BLOCKS)) return Q8_ERR_SHAPE;
+    if (layout == Q8_LAYOUT_PACKED && n % Q8_TILE_ROWS) return Q8_ERR_SHAPE;
+    if (m > Q8_GEMV_MAX_ROWS && layout != Q8_LAYOUT_PACKED) return Q8_ERR_SHAPE;
+    if (!aligned16(x_q) || !aligned16(w) || !aligned16(y)) return Q8_ERR_ALIGN;
+    const size_t need = q8_matmul_workspace_bytes(m, n, k);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return Q8_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return Q8_ERR_ALIGN;
+    }
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    if (m <= Q8_GEMV_MAX_ROWS)
+        return launched(q8k::launch_gemv(x_q, m, w, layout, n, k, y, ld_y, workspace, stream));
+    return launched(q8k::launch_gemm(x_q, m, w, n, k, y, ld_y, stream));
+}
+
+size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k) {
+    (void)n;
+    (void)k;
+    if (tokens <= 0 || topk <= 0 || n_experts <= 0) return 0;
+    return q8k::grouped_workspace_bytes(tokens, topk, n_experts);
+}
+
+int q8_grouped_matmul(const void *x_q, int64_t x_rows, int x_per_pair, const int32_t *topk_ids, int64_t tokens,
+                      int topk, const void *w_experts, int64_t n_experts, int64_t expert_stride_bytes, int64_t n,
+                      int64_t k, float *y, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!x_q || !topk_ids || !w_experts || !y || tokens <= 0 || topk <= 0 || n_experts <= 0 || n <= 0 || k <= 0)
+        return Q8_ERR_ARG;
+    if (x_per_pair != 0 && x_per_pair != 1) return Q8_ERR_ARG;
+    if (x_rows != (x_per_pair ? tokens * topk : tokens)) return Q8_ERR_ARG;
+    if (n % Q8_TILE_ROWS || k % (Q8_BLOCK * Q8_TILE_BLOCKS)) return Q8_ERR_SHAPE;
+    if (topk > n_experts || n_experts > 1024 || tokens * topk > 65536) return Q8_ERR_SHAPE;
+    if (expert_stride_bytes < (int64_t)q8_quantized_bytes(n, k) || expert_stride_bytes % 16) return Q8_ERR_SHAPE;
+    if (!aligned16(x_q) || !aligned16(w_experts) || !aligned16(y) || ((uintptr_t)topk_ids & 3u)) return Q8_ERR_ALIGN;
+    const size_t need = q8_grouped_workspace_bytes(tokens, topk, n_experts, n, k);
+    if (!workspace || workspace_bytes < need) return Q8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return Q8_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_grouped(x_q, x_rows, x_per_pair, topk_ids, tokens, topk, w_experts, n_experts,
+                                        expert_stride_bytes, n, k, y, workspace, stream));
+}
+
+}  // extern "C"

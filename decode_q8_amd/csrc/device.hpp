@@ -1,0 +1,45 @@
+// Device-side helpers shared by the gfx950 kernels of libq8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8k {
+
+constexpr int QK = 32;            // values per block
+constexpr int BLOCK_BYTES = 34;   // fp16 scale + 32 int8
+constexpr int TILE_ROWS = 64;     // rows per packed record = lanes per wave
+constexpr int GROUP_BLOCKS = 8;   // blocks per packed record and per summation group
+constexpr int GROUP_K = GROUP_BLOCKS * QK;              // 256 values
+constexpr int RECORD_BYTES = TILE_ROWS * GROUP_BLOCKS * BLOCK_BYTES;  // 17408
+constexpr int RECORD_Q_BYTES = TILE_ROWS * GROUP_K;     // 16384
+constexpr int ROW_GROUP_BYTES = GROUP_BLOCKS * BLOCK_BYTES;           // 272
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// fp32 -> fp16 bits, round to nearest even, subnormals kept (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Component c (0..3) of a uint4, c known at compile time after unrolling.
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int c) {
+    return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
+// Index of this wave in its workgroup, as a wave-uniform (SGPR) value so that
+// everything derived from it stays scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Sum of the 8 block terms of one group, in the fixed tree order
+// ((t0+t1)+(t2+t3))+((t4+t5)+(t6+t7)).
+__device__ __forceinline__ float tree8(const float (&t)[8]) {
+    return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+}
+
+}  // namespace q8k

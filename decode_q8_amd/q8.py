@@ -1,0 +1,162 @@
+"""ctypes binding of libq8 (include/q8.h), one Python function per C entry point
+with the same name.
+
+Marshalling only: tensors become device pointers (``data_ptr()``), streams
+become ``hipStream_t`` handles (default: torch's current stream), and a
+non-zero status raises ``Q8Error``.  Every step of the computation runs in the
+library's HIP kernels; there is no Python or CPU implementation behind these
+functions, and importing fails loudly if the library cannot be loaded.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq8.so")
+
+Q8_OK, Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE, Q8_ERR_DEVICE, Q8_ERR_LAUNCH = range(7)
+Q8_LAYOUT_ROWS, Q8_LAYOUT_PACKED, Q8_LAYOUT_ACT = 0, 1, 2
+Q8_BLOCK = 32
+Q8_BLOCK_BYTES = 34
+Q8_TILE_ROWS = 64
+Q8_GEMV_MAX_ROWS = 8
+
+# The C entry points declared in include/q8.h, with their ctypes signatures.
+_P, _I64, _I, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32
+SIGNATURES = {
+    "q8_abi_version": ([], _U32),
+    "q8_status_str": ([_I], ctypes.c_char_p),
+    "q8_quantized_bytes": ([_I64, _I64], _SZ),
+    "q8_quantize_rows": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
+    "q8_repack_weights": ([_P, _I64, _I64, _P, _P], _I),
+    "q8_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "q8_matmul": ([_P, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
+    "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
+    "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
+}
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libq8.so (building it first if no build exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int, what: str) -> int:
+    if status != Q8_OK:
+        raise Q8Error(status, what)
+    return status
+
+
+def status_str(status: int) -> str:
+    return lib().q8_status_str(status).decode()
+
+
+def q8_abi_version() -> int:
+    return lib().q8_abi_version()
+
+
+def q8_status_str(status: int) -> str:
+    return status_str(status)
+
+
+def q8_quantized_bytes(rows: int, k: int) -> int:
+    return lib().q8_quantized_bytes(rows, k)
+
+
+def q8_matmul_workspace_bytes(m: int, n: int, k: int) -> int:
+    return lib().q8_matmul_workspace_bytes(m, n, k)
+
+
+def q8_grouped_workspace_bytes(tokens: int, topk: int, n_experts: int, n: int, k: int) -> int:
+    return lib().q8_grouped_workspace_bytes(tokens, topk, n_experts, n, k)
+
+
+def q8_quantize_rows(x, ld_x: int, rows: int, k: int, layout: int, q_out, stream=None) -> int:
+    return _check(lib().q8_quantize_rows(_ptr(x), ld_x, rows, k, layout, _ptr(q_out), _stream(stream)),
+                  "q8_quantize_rows")
+
+
+def q8_repack_weights(w_rows, n: int, k: int, w_packed, stream=None) -> int:
+    return _check(lib().q8_repack_weights(_ptr(w_rows), n, k, _ptr(w_packed), _stream(stream)), "q8_repack_weights")
+
+
+def q8_matmul(x_q, m: int, w, layout: int, n: int, k: int, y, ld_y: int, workspace=None, workspace_bytes: int = 0,
+              stream=None) -> int:
+    return _check(lib().q8_matmul(_ptr(x_q), m, _ptr(w), layout, n, k, _ptr(y), ld_y, _ptr(workspace),
+                                  workspace_bytes, _stream(stream)), "q8_matmul")
+
+
+def q8_grouped_matmul(x_q, x_rows: int, x_per_pair: int, topk_ids, tokens: int, topk: int, w_experts,
+                      n_experts: int, expert_stride_bytes: int, n: int, k: int, y, workspace, workspace_bytes: int,
+                      stream=None) -> int:
+    return _check(lib().q8_grouped_matmul(_ptr(x_q), x_rows, int(x_per_pair), _ptr(topk_ids), tokens, topk,
+                                          _ptr(w_experts), n_experts, expert_stride_bytes, n, k, _ptr(y),
+                                          _ptr(workspace), workspace_bytes, _stream(stream)), "q8_grouped_matmul")
+
+
+# --- torch conveniences (allocation + one call each) -------------------------
+
+def quantize(x, layout: int = Q8_LAYOUT_ACT, stream=None):
+    """fp32 [rows][k] CUDA tensor (unit column stride) -> new uint8 tensor."""
+    import torch
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    rows, k = x.shape
+    out = torch.empty(q8_quantized_bytes(rows, k), dtype=torch.uint8, device=x.device)
+    q8_quantize_rows(x, x.stride(0), rows, k, layout, out, stream)
+    return out
+
+
+def repack(w_rows, n: int, k: int, stream=None):
+    import torch
+    out = torch.empty_like(w_rows)
+    q8_repack_weights(w_rows, n, k, out, stream)
+    return out
+
+
+def matmul(x_q, m: int, w, layout: int, n: int, k: int, workspace=None, stream=None):
+    """-> new fp32 [m][n] tensor; allocates a workspace if none is given."""
+    import torch
+    y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    need = q8_matmul_workspace_bytes(m, n, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
+    q8_matmul(x_q, m, w, layout, n, k, y, n, workspace, need if workspace is not None else 0, stream)
+    return y

@@ -1,0 +1,175 @@
+/*
+ * q8.h: C ABI of libq8, the MI355X (gfx950) Q8_0 block-quantized matmul.
+ *
+ * What is computed (the method of the pages this library implements):
+ *  - Q8_0 block: 32 values stored as one fp16 scale followed by 32 int8, 34
+ *    bytes ("Ember packed Q8 decode" post, row-contiguous source diagram).
+ *  - Quantization of weights and activations alike: per 32-value block,
+ *    d = amax / 127 (fp32), q = nearest integer to x / d with ties away from
+ *    zero, stored scale = fp16(d) ("ferro" README, "How the iGPU path is
+ *    fast", item 1: activations quantized per 32-block; "Using LFM2.5":
+ *    weights converted to Q8_0 at load).
+ *  - Block dot: s = exact int32 sum of the 32 products, term
+ *    t = fp32(s * (Dw * Dx)) (Dw * Dx is exact in fp32, so one rounding).
+ *  - Output: the terms of a row summed in fp32 in one fixed order that
+ *    depends on k only: groups of 8 consecutive blocks are summed as the tree
+ *    ((t0+t1)+(t2+t3))+((t4+t5)+(t6+t7)), then the group sums are added left
+ *    to right starting from the first group.  Every entry point that produces
+ *    GEMV outputs (m <= 8, and every routed pair) uses exactly this order, so
+ *    a row's output is bit-identical alone, in any batch of up to 8 rows, in
+ *    any row order, in either weight layout, for any n, and in the routed
+ *    expert path (the batch-invariance contract of the "ferro" README,
+ *    "Exactness contract").  The prefill GEMM (m > 8) accumulates each group
+ *    with fused multiply-adds instead; its rows are bit-identical for any m
+ *    and row order, but need not equal the GEMV bitwise ("ferro" README,
+ *    "Exactness contract": decode rows and prefill rows take different
+ *    kernels).  Any correct fp32 order lies within
+ *    |y - exact| <= 1e-5 * sum_b |t_b| of the exact sum.
+ *
+ * Conventions:
+ *  - Every data pointer is a device pointer that the caller allocates and
+ *    owns; the library allocates no memory and keeps no state except a
+ *    per-device architecture check.
+ *  - Every call is asynchronous on the caller's stream (0 = the null
+ *    stream).  The returned status covers host-side validation and the
+ *    launch only.  Validation happens before any HIP call, so argument
+ *    errors are reported without a GPU.
+ *  - Pointers must be 16-byte aligned; sizes are in elements unless named
+ *    *_bytes.  Unsupported requests fail with a status; there is no
+ *    fallback path ("Ferrule" README, "Core features" and "System vision":
+ *    missing capabilities and other hardware fail explicitly).
+ *  - Calls are stateless and may run concurrently on different streams as
+ *    long as their output and workspace buffers do not overlap.
+ *
+ * Layouts (byte formats):
+ *  Q8_LAYOUT_ROWS   row-contiguous Q8_0: rows x (k/32) blocks of
+ *                   [fp16 d][32 x int8], 34 bytes each.
+ *  Q8_LAYOUT_PACKED weights for gfx950: records of 64 rows x 8 blocks,
+ *                   17,408 bytes (= 512 blocks x 34 = 32 x 544: the same
+ *                   bytes, reordered; "Ember packed Q8 decode" post: a packed
+ *                   record holds exactly the bytes of the blocks it covers).
+ *                   Record (T, G) starts at byte (T * (k/256) + G) * 17408;
+ *                   inside it, the int8 value of row 64T + r, column
+ *                   256G + 32bb + 16h + j is at bb*2048 + h*1024 + r*16 + j
+ *                   (so one 16-byte load per lane, 64 lanes = 64 rows, reads
+ *                   1 KB contiguous), and the fp16 scale of (row r, block bb)
+ *                   is at 16384 + r*16 + bb*2 (one 16-byte load per lane gives
+ *                   a row's 8 scales).  Needs n % 64 == 0 and k % 256 == 0.
+ *  Q8_LAYOUT_ACT    quantized activations: int8 [rows][k] followed by fp16
+ *                   [rows][k/32]; rows * k/32 * 34 bytes in all.
+ */
+#ifndef DECODE_Q8_AMD_Q8_H
+#define DECODE_Q8_AMD_Q8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8_ABI_VERSION 1u
+#define Q8_BLOCK 32          /* values per block */
+#define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
+#define Q8_TILE_ROWS 64      /* rows per packed record */
+#define Q8_TILE_BLOCKS 8     /* blocks per packed record and per summation group */
+#define Q8_RECORD_BYTES 17408
+#define Q8_GEMV_MAX_ROWS 8   /* m <= 8 takes the GEMV */
+
+typedef enum {
+    Q8_OK = 0,
+    Q8_ERR_ARG = 1,       /* null pointer, size <= 0, unknown enum, ld too small  */
+    Q8_ERR_SHAPE = 2,     /* k % 32 (quantize), k % 256, n % 64 (packed), ...     */
+    Q8_ERR_ALIGN = 3,     /* pointer not 16-byte aligned, fp32 row stride % 4      */
+    Q8_ERR_WORKSPACE = 4, /* workspace missing or smaller than required            */
+    Q8_ERR_DEVICE = 5,    /* no HIP device, or the current device is not gfx950   */
+    Q8_ERR_LAUNCH = 6     /* the kernel launch failed                              */
+} q8_status;
+
+typedef enum { Q8_LAYOUT_ROWS = 0, Q8_LAYOUT_PACKED = 1, Q8_LAYOUT_ACT = 2 } q8_layout;
+
+/* Version of this ABI (Q8_ABI_VERSION). */
+uint32_t q8_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *q8_status_str(int status);
+
+/* Bytes of rows x k values in any of the three layouts: rows * k/32 * 34.
+ * Returns 0 if k % 32 != 0 or a size is negative. */
+size_t q8_quantized_bytes(int64_t rows, int64_t k);
+
+/* Quantize fp32 rows.
+ *  x       device, rows x k fp32, row stride ld_x elements (ld_x >= k,
+ *          ld_x % 4 == 0), 16-byte aligned.  Not modified.
+ *  layout  Q8_LAYOUT_ROWS (weights, GGUF-style blocks) or Q8_LAYOUT_ACT
+ *          (activations for q8_matmul / q8_grouped_matmul).
+ *  q_out   device, q8_quantized_bytes(rows, k) bytes, 16-byte aligned; must
+ *          not overlap x.
+ *  k % 32 == 0; rows == 0 is a no-op.  Quantized values and scales are
+ *  bit-identical to the definition above (one wavefront-reduction per block).
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int layout, void *q_out,
+                     hipStream_t stream);
+
+/* Reorder row-contiguous Q8_0 weights (Q8_LAYOUT_ROWS, n x k) into
+ * Q8_LAYOUT_PACKED.  A pure byte permutation: the output has the same size,
+ * q8_quantized_bytes(n, k).  Needs n % 64 == 0, k % 256 == 0; buffers must
+ * not overlap ("Ember packed Q8 decode" post: packing at prepare time).
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_repack_weights(const void *w_rows, int64_t n, int64_t k, void *w_packed, hipStream_t stream);
+
+/* Workspace bytes q8_matmul needs for this shape (0 when none).  Depends on
+ * (m, n, k) only. */
+size_t q8_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* y[i][j] = sum over blocks of x_q row i against weight row j (the Q8_0
+ * block dot product, "ferro" README, "How the iGPU path is fast", item 1).
+ *  x_q     device, Q8_LAYOUT_ACT, m rows of k.
+ *  w       device, n x k weights in Q8_LAYOUT_PACKED (n % 64 == 0) or
+ *          Q8_LAYOUT_ROWS (any n; only for m <= 8).
+ *  y       device fp32, m x n with row stride ld_y >= n (elements).
+ *  workspace, workspace_bytes: device scratch of at least
+ *          q8_matmul_workspace_bytes(m, n, k) (may be NULL when that is 0);
+ *          contents on entry do not matter; must not overlap y.
+ *  Routing is by m alone: m <= 8 runs the GEMV, m > 8 the MFMA GEMM.
+ *  k % 256 == 0.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
+ *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_matmul(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y,
+              int64_t ld_y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes q8_grouped_matmul needs. */
+size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k);
+
+/* Routed-expert matmul (the expert GEMVs of a mixture-of-experts layer;
+ * "Ferrule" README, routed-expert roofline: each selected expert's weights
+ * are streamed once per pass).  For token t and slot j (pair p = t*topk + j):
+ *   y[p][:] = GEMV of activation row (x_per_pair ? p : t) with expert
+ *             topk_ids[t][j]'s weights,
+ * bit-identical to q8_matmul with m = 1 on that row and that expert.
+ * Pairs are grouped by expert on the device (stable in p), each active
+ * expert's weights are streamed once per 8 pairs.
+ *  x_q        device, Q8_LAYOUT_ACT with x_rows rows of k
+ *             (x_rows == tokens, or tokens*topk when x_per_pair).
+ *  topk_ids   device int32 [tokens][topk].
+ *  w_experts  device, expert e in Q8_LAYOUT_PACKED (n x k) at byte
+ *             e * expert_stride_bytes (expert_stride_bytes >=
+ *             q8_quantized_bytes(n, k), multiple of 16).
+ *  y          device fp32 [tokens*topk][n].
+ *  workspace  device, >= q8_grouped_workspace_bytes(...); its first 4 bytes
+ *             receive an int32 status after the call completes: 0, or
+ *             Q8_ERR_ARG if some id was outside [0, n_experts) (those pairs'
+ *             outputs are left unwritten).
+ *  n % 64 == 0, k % 256 == 0, tokens*topk <= 65536, topk <= n_experts <= 1024.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
+ *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_grouped_matmul(const void *x_q, int64_t x_rows, int x_per_pair, const int32_t *topk_ids, int64_t tokens,
+                      int topk, const void *w_experts, int64_t n_experts, int64_t expert_stride_bytes, int64_t n,
+                      int64_t k, float *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

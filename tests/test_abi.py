@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/q8.h declares, and rejects bad requests on the host before any HIP
+call (the pages' boundary style: unsupported requests fail explicitly at the
+API boundary, "Ferrule" README, "Core features").  Nothing here launches a
+kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_q8_amd import q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8.h")
+
+# Fake but 16-byte aligned device addresses: every call below fails validation
+# before it could touch them.
+A = 0x7F0000000000
+B = 0x7F0000100000
+C = 0x7F0000200000
+D = 0x7F0000300000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(q8_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 9, names
+    assert sorted(q8.SIGNATURES) == names
+    L = ctypes.CDLL(q8.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings():
+    assert q8.q8_abi_version() == 1
+    for s in range(7):
+        assert q8.status_str(s).startswith("Q8_")
+    assert q8.status_str(99) == "Q8_ERR_UNKNOWN"
+
+
+def test_sizes():
+    assert q8.q8_quantized_bytes(1, 2048) == 2176
+    assert q8.q8_quantized_bytes(2048, 2048) == 4456448
+    assert q8.q8_quantized_bytes(128256, 2048) == 128256 * 64 * 34
+    assert q8.q8_quantized_bytes(3, 33) == 0
+    assert q8.q8_quantized_bytes(-1, 32) == 0
+    # workspace: narrow matrices split by group, wide ones and the GEMM need none
+    assert q8.q8_matmul_workspace_bytes(1, 2048, 8192) == 32 * 1 * 2048 * 4
+    assert q8.q8_matmul_workspace_bytes(8, 2048, 2048) == 8 * 8 * 2048 * 4
+    assert q8.q8_matmul_workspace_bytes(1, 128256, 2048) == 0
+    assert q8.q8_matmul_workspace_bytes(188, 2048, 2048) == 0
+    assert q8.q8_grouped_workspace_bytes(16, 8, 256, 2048, 7168) >= 4 * (16 + 2 * 256 + 1 + 128)
+
+
+def _raw(name, *args):
+    return getattr(q8.lib(), name)(*args)
+
+
+def test_quantize_validation():
+    f = "q8_quantize_rows"
+    assert _raw(f, None, 64, 1, 64, 2, B, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 64, 1, 64, 2, None, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 32, 1, 64, 2, B, None) == q8.Q8_ERR_ARG       # ld_x < k
+    assert _raw(f, A, 64, 1, 64, 1, B, None) == q8.Q8_ERR_ARG       # PACKED is not a quantizer output
+    assert _raw(f, A, 64, 1, 0, 2, B, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 64, -1, 64, 2, B, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 64, 1, 48, 2, B, None) == q8.Q8_ERR_SHAPE     # k % 32
+    assert _raw(f, A + 4, 64, 1, 64, 2, B, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 66, 1, 64, 2, B, None) == q8.Q8_ERR_ALIGN     # ld_x % 4
+    assert _raw(f, A, 64, 0, 64, 2, B, None) == q8.Q8_OK            # no rows: no-op, no launch
+
+
+def test_repack_validation():
+    f = "q8_repack_weights"
+    assert _raw(f, None, 64, 256, B, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 0, 256, B, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 32, 256, B, None) == q8.Q8_ERR_SHAPE          # n % 64
+    assert _raw(f, A, 64, 224, B, None) == q8.Q8_ERR_SHAPE          # k % 256
+    assert _raw(f, A + 2, 64, 256, B, None) == q8.Q8_ERR_ALIGN
+
+
+def test_matmul_validation():
+    f = "q8_matmul"
+    ok = dict(x=A, m=1, w=B, layout=1, n=2048, k=2048, y=C, ld=2048, ws=D, wsb=1 << 30)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return _raw(f, a["x"], a["m"], a["w"], a["layout"], a["n"], a["k"], a["y"], a["ld"], a["ws"], a["wsb"], None)
+
+    assert call(x=None) == q8.Q8_ERR_ARG
+    assert call(m=0) == q8.Q8_ERR_ARG
+    assert call(ld=2047) == q8.Q8_ERR_ARG
+    assert call(layout=2) == q8.Q8_ERR_ARG
+    assert call(k=2080) == q8.Q8_ERR_SHAPE                          # k % 256
+    assert call(n=2000) == q8.Q8_ERR_SHAPE                          # packed needs n % 64
+    assert call(m=16, layout=0) == q8.Q8_ERR_SHAPE                  # GEMM reads packed weights only
+    assert call(w=B + 8) == q8.Q8_ERR_ALIGN
+    assert call(ws=None) == q8.Q8_ERR_WORKSPACE                     # 2048 x 2048 splits by group
+    assert call(wsb=100) == q8.Q8_ERR_WORKSPACE
+    assert call(ws=D + 4) == q8.Q8_ERR_ALIGN
+
+
+def test_grouped_validation():
+    f = "q8_grouped_matmul"
+    ok = dict(x=A, xr=16, pp=0, ids=B, t=16, topk=8, w=C, E=256, stride=2048 * 7168 // 32 * 34, n=2048, k=7168,
+              y=D, ws=D + (1 << 20), wsb=1 << 20)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return _raw(f, a["x"], a["xr"], a["pp"], a["ids"], a["t"], a["topk"], a["w"], a["E"], a["stride"], a["n"],
+                    a["k"], a["y"], a["ws"], a["wsb"], None)
+
+    assert call(ids=None) == q8.Q8_ERR_ARG
+    assert call(xr=128) == q8.Q8_ERR_ARG                            # rows must be tokens when not per pair
+    assert call(pp=1) == q8.Q8_ERR_ARG                              # ... and tokens*topk when per pair
+    assert call(pp=2) == q8.Q8_ERR_ARG
+    assert call(topk=300) == q8.Q8_ERR_SHAPE
+    assert call(E=2048) == q8.Q8_ERR_SHAPE
+    assert call(stride=100) == q8.Q8_ERR_SHAPE
+    assert call(n=2000) == q8.Q8_ERR_SHAPE
+    assert call(wsb=16) == q8.Q8_ERR_WORKSPACE
+    assert call(ids=B + 2) == q8.Q8_ERR_ALIGN
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device error; would launch on a GPU host")
+def test_valid_request_without_device_reports_device_error():
+    assert _raw("q8_quantize_rows", A, 64, 1, 64, 2, B, None) == q8.Q8_ERR_DEVICE
+    assert _raw("q8_matmul", A, 1, B, 1, 131072, 2048, C, 131072, None, 0, None) == q8.Q8_ERR_DEVICE

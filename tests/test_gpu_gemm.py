@@ -1,0 +1,64 @@
+"""Prefill GEMM (q8_matmul with m > 8, int8 MFMA) against the oracle, and its
+row invariance: a row's output does not depend on m or on the row order."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from decode_q8_amd import q8
+from tests.gpu_helpers import bits_equal, check_tol, down, quantize, require_gpu, weights_packed
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _gemm(xq, m, wp, n, k):
+    return down(q8.matmul(xq, m, wp, q8.Q8_LAYOUT_PACKED, n, k))
+
+
+@pytest.mark.parametrize("m,n,k", [(9, 64, 256), (32, 128, 256), (40, 192, 512), (130, 256, 2048),
+                                   (188, 320, 1024), (257, 128, 7168)])
+def test_parity(m, n, k):
+    x = wl.activation(wl.PREFILL, 50 + m, m, k, outliers=True)
+    w = wl.weight(wl.PREFILL, 50 + n, n, k)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    wr, wp = weights_packed(w)
+    y_ref, S = oracle.matmul(down(xq), m, down(wr), n, k, threads=8)
+    check_tol(_gemm(xq, m, wp, n, k), y_ref, S, f"gemm m={m} n={n} k={k}")
+
+
+def test_row_invariance_across_m_and_order():
+    n, k = 256, 2048
+    x = wl.activation(wl.PREFILL, 60, 752, k, outliers=True)
+    _, wp = weights_packed(wl.weight(wl.PREFILL, 60, n, k))
+    y752 = _gemm(quantize(x, q8.Q8_LAYOUT_ACT), 752, wp, n, k)
+    y188 = _gemm(quantize(x[:188], q8.Q8_LAYOUT_ACT), 188, wp, n, k)
+    assert bits_equal(y188, y752[:188])
+    y9 = _gemm(quantize(x[100:109], q8.Q8_LAYOUT_ACT), 9, wp, n, k)
+    assert bits_equal(y9, y752[100:109])
+    perm = wl.permutation(wl.PREFILL, 188)
+    yp = _gemm(quantize(x[:188][perm], q8.Q8_LAYOUT_ACT), 188, wp, n, k)
+    assert bits_equal(yp, y188[perm])
+
+
+@pytest.mark.parametrize("m", wl.PREFILL_M)
+@pytest.mark.parametrize("n,k", wl.PREFILL_NK)
+def test_prefill_full_size_sampled(m, n, k):
+    """Every prefill configuration at full size: 1024 sampled outputs against
+    the oracle (which computes them one by one)."""
+    x = wl.activation(wl.PREFILL, m, m, k, outliers=True)
+    w = wl.weight(wl.PREFILL, n + k, n, k)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    wr, wp = weights_packed(w)
+    y = _gemm(xq, m, wp, n, k)
+    rng = np.random.default_rng(m * n + k)
+    mi = rng.integers(0, m, 1024)
+    ni = rng.integers(0, n, 1024)
+    mi[:4] = [0, m - 1, 0, m - 1]
+    ni[:4] = [0, n - 1, n - 1, 0]
+    y_ref, S = oracle.matmul_points(down(xq), m, down(wr), n, k, mi, ni)
+    check_tol(y[mi, ni], y_ref, S, f"prefill m={m} n={n} k={k}")

@@ -1,0 +1,149 @@
+"""Decode GEMV (q8_matmul with m <= 8) against the oracle, and the invariance
+contract: a row's output is bit-identical alone or in any batch of up to 8
+rows, in any row order, in either weight layout, inside a larger (fused)
+matrix, and across repeated calls ("ferro" README, "Exactness contract")."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from decode_q8_amd import q8
+from tests.gpu_helpers import bits_equal, check_tol, down, quantize, require_gpu, up, weights_packed
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _gemv(xq, m, w, layout, n, k):
+    return down(q8.matmul(xq, m, w, layout, n, k))
+
+
+def _case(m, n, k, seed):
+    x = wl.activation(wl.BATCHED, seed, m, k)
+    w = wl.weight(wl.BATCHED, seed, n, k)
+    return x, w
+
+
+# (n, k): one tile; several tiles and groups (split by group); ragged group
+# count k = 7168; a matrix wide enough to run whole rows per wave.
+SHAPES = [(64, 256), (192, 512), (512, 2048), (640, 7168), (65536, 256)]
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+def test_parity_packed_and_rows(m, n, k):
+    x, w = _case(m, n, k, seed=n + m)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    wr, wp = weights_packed(w)
+    y_ref, S = oracle.matmul(down(xq), m, down(wr), n, k, threads=8)
+    yp = _gemv(xq, m, wp, q8.Q8_LAYOUT_PACKED, n, k)
+    check_tol(yp, y_ref, S, f"packed m={m} n={n} k={k}")
+    yr = _gemv(xq, m, wr, q8.Q8_LAYOUT_ROWS, n, k)
+    assert bits_equal(yp, yr), "packed and row-contiguous layouts differ"
+
+
+@pytest.mark.parametrize("n", [1, 50, 100, 1000])
+def test_rows_layout_ragged_n(n):
+    k = 512
+    x, w = _case(3, n, k, seed=n)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    wr = quantize(w, q8.Q8_LAYOUT_ROWS)
+    y_ref, S = oracle.matmul(down(xq), 3, down(wr), n, k)
+    check_tol(_gemv(xq, 3, wr, q8.Q8_LAYOUT_ROWS, n, k), y_ref, S, f"rows n={n}")
+
+
+@pytest.mark.parametrize("n,k", [(512, 2048), (65536, 256), (2048, 8192)])
+def test_batch_invariance_and_permutation(n, k):
+    x, w = _case(8, n, k, seed=7)
+    _, wp = weights_packed(w)
+    singles = np.stack([_gemv(quantize(x[i:i + 1], q8.Q8_LAYOUT_ACT), 1, wp, 1, n, k)[0] for i in range(8)])
+    for m in (2, 4, 6, 8):
+        ym = _gemv(quantize(x[:m], q8.Q8_LAYOUT_ACT), m, wp, 1, n, k)
+        assert bits_equal(ym, singles[:m]), f"m={m}"
+        perm = wl.permutation(wl.BATCHED, m)
+        yp = _gemv(quantize(x[:m][perm], q8.Q8_LAYOUT_ACT), m, wp, 1, n, k)
+        assert bits_equal(yp, ym[perm]), f"permuted m={m}"
+
+
+def test_fused_matrix_rows_equal_parts():
+    """Rows of a fused [W1; W2] matrix equal those of W1 and W2 alone, although
+    the fused matrix runs whole rows per wave and the parts split by group."""
+    k = 256
+    x, w1 = _case(2, 512, k, seed=11)
+    _, w2 = _case(2, 65536, k, seed=12)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    _, p1 = weights_packed(w1)
+    _, p2 = weights_packed(w2)
+    _, pf = weights_packed(np.concatenate([w1, w2]))
+    yf = _gemv(xq, 2, pf, 1, 512 + 65536, k)
+    assert bits_equal(yf[:, :512], _gemv(xq, 2, p1, 1, 512, k))
+    assert bits_equal(yf[:, 512:], _gemv(xq, 2, p2, 1, 65536, k))
+
+
+def test_repeatable():
+    x, w = _case(4, 2048, 8192, seed=13)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    _, wp = weights_packed(w)
+    a = _gemv(xq, 4, wp, 1, 2048, 8192)
+    b = _gemv(xq, 4, wp, 1, 2048, 8192)
+    assert bits_equal(a, b)
+
+
+def test_ld_y_and_workspace_reuse():
+    """Output row stride larger than n; a dirty, oversized workspace."""
+    m, n, k = 3, 512, 2048
+    x, w = _case(m, n, k, seed=14)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    _, wp = weights_packed(w)
+    y = torch.full((m, n + 64), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.full((q8.q8_matmul_workspace_bytes(m, n, k) + 4096,), 255, dtype=torch.uint8, device="cuda")
+    q8.q8_matmul(xq, m, wp, 1, n, k, y, n + 64, ws, ws.numel())
+    got = down(y)
+    assert np.all(got[:, n:] == 7.0)
+    assert bits_equal(got[:, :n], _gemv(xq, m, wp, 1, n, k))
+
+
+def test_single_gemv_full_size():
+    """The 2048 x 2048 single GEMV: every output against the oracle."""
+    n = k = 2048
+    w = wl.weight(wl.SINGLE, 0, n, k)
+    x = wl.activation(wl.SINGLE, 0, 1, k)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    wr, wp = weights_packed(w)
+    y_ref, S = oracle.matmul(down(xq), 1, down(wr), n, k, threads=8)
+    yp = _gemv(xq, 1, wp, 1, n, k)
+    check_tol(yp, y_ref, S, "single 2048x2048")
+    assert bits_equal(yp, _gemv(xq, 1, wr, 0, n, k))
+
+
+@pytest.mark.parametrize("name,n,k", [m[:3] for m in wl.LLAMA_LAYER_MATS] + [wl.LLAMA_HEAD])
+def test_decode_shapes_full_size_sampled(name, n, k):
+    """Full decode-step shapes (fused QKV, O, gate||up, down, LM head) at m = 1
+    and m = 8: 512 sampled outputs per m against the oracle; every row of the
+    m = 8 batch bit-identical to its m = 1 run; both layouts bit-identical."""
+    w = wl.weight(wl.BATCHED, 1000 + n + k, n, k)
+    x = wl.activation(wl.BATCHED, 1000 + n + k, 8, k)
+    wr, wp = weights_packed(w)
+    wr_h = down(wr)
+    rng = np.random.default_rng(n + k)
+    y1 = None
+    for m in (1, 8):
+        xq = quantize(x[:m], q8.Q8_LAYOUT_ACT)
+        y = _gemv(xq, m, wp, 1, n, k)
+        mi = rng.integers(0, m, 512)
+        ni = rng.integers(0, n, 512)
+        y_ref, S = oracle.matmul_points(down(xq), m, wr_h, n, k, mi, ni)
+        check_tol(y[mi, ni], y_ref, S, f"{name} m={m}")
+        if m == 1:
+            y1 = y
+            assert bits_equal(y, _gemv(xq, 1, wr, 0, n, k)), f"{name}: layouts differ"
+        else:
+            assert bits_equal(y[:1], y1)
+            for i in range(1, 8):
+                yi = _gemv(quantize(x[i:i + 1], q8.Q8_LAYOUT_ACT), 1, wp, 1, n, k)
+                assert bits_equal(y[i:i + 1], yi), f"{name}: row {i} differs alone"
