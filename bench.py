@@ -3,19 +3,25 @@
 Default workload (``--workload decode``): one decode step of a
 Llama-3.2-1B-shaped model at batch 1 -- 16 layers of fused QKV [3072x2048],
 O [2048x2048], fused gate||up [16384x2048], down [2048x8192], then the LM head
-[128256x2048]; every distinct input is an fp32 N(0,1) row that is quantized
-(q8_quantize_rows) right before the GEMV(s) that read it (q8_matmul).  Weights
-are N(0, 0.02) fp32, quantized and repacked on the device before timing.  The
-1.31 GB weight set exceeds every on-chip cache, so each step streams it from
-HBM.  A step is captured once into a HIP graph and replayed.
+[128256x2048].  Every distinct input is an fp32 N(0,1) row; each matrix runs
+one q8_quantize_matmul launch (activation quantization fused into the GEMV,
+bit-identical to q8_quantize_rows + q8_matmul).  ``--unfused`` runs the two
+calls separately instead.  Weights are N(0, 0.02) fp32, quantized
+(q8_quantize_rows) and repacked (q8_repack_weights) on the device before
+timing.  The 1.31 GB weight set is larger than every on-chip cache, so each
+step streams it from HBM.  A step is captured once into a HIP graph and
+replayed.
 
 Other workloads (same JSON line format): ``single`` (one 2048x2048 GEMV),
-``batched`` (the decode step at m = 1..8 rows), ``prefill`` (the MFMA GEMM
-shapes), ``moe`` (the routed-expert GEMVs).
+``batched`` (the decode step with ``--m`` rows per GEMV), ``prefill`` (the
+int8-MFMA GEMM at M in {188, 752, 2048} x (N, K) in {(2048, 2048),
+(8192, 2048), (2048, 8192)}), ``moe`` (routed-expert GEMVs: 256 experts,
+16 tokens, top-8; gate, up and down), ``copy`` (a device copy of 1 GiB, used
+to calibrate rocprofv3's byte counters).
 
-Output: one JSON line with the metric, the roofline of the dominant kernel
-(its average launch duration measured with HIP events on its own stream) and
-the CPU oracle timed on the host on a bounded sample of the same workload.
+The JSON line carries the metric, the roofline of the dominant kernel (its
+average launch duration measured with HIP events on the stream it runs on)
+and the CPU oracle timed on the host on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -40,20 +46,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "single", "batched", "prefill", "moe"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "single", "batched", "prefill", "moe", "copy"])
     ap.add_argument("--m", type=int, default=1, help="rows per GEMV for --workload batched")
+    ap.add_argument("--unfused", action="store_true", help="decode: separate quantize and GEMV launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     return ap.parse_args()
 
 
-def _sync():
-    import torch
-    torch.cuda.synchronize()
-
-
 class Timer:
-    """HIP events on one stream."""
+    """A pair of HIP events recorded on one stream."""
 
     def __init__(self, stream):
         import torch
@@ -72,74 +75,63 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-# --------------------------------------------------------------------------
-# decode step (and its batched variant)
-# --------------------------------------------------------------------------
-
-class DecodeStep:
-    def __init__(self, m: int, threads: int, keep_host_rows: bool):
-        import torch
-
-        import oracle
-        import workloads as wl
-        from decode_q8_amd import q8
-
-        self.torch, self.q8, self.wl = torch, q8, wl
-        self.m = m
-        self.mats = wl.decode_matrices()
-        dev = torch.device("cuda", 0)
-        self.w_packed, self.host_rows = [], []
-        # weights: host fp32 (threaded generation) -> device -> quantize -> repack
-        chunk = 8
-        for c0 in range(0, len(self.mats), chunk):
-            group = self.mats[c0:c0 + chunk]
-            ws = wl.many(lambda mt: wl.weight(wl.BATCHED if m > 1 else wl.DECODE, mt.index, mt.n, mt.k,
-                                              group=mt.layer), [(mt,) for mt in group], threads)
-            for mt, w in zip(group, ws):
-                wt = torch.from_numpy(w).to(dev)
-                wr = q8.quantize(wt, q8.Q8_LAYOUT_ROWS)
-                self.w_packed.append(q8.repack(wr, mt.n, mt.k))
-                del wt, wr
-                if keep_host_rows:
-                    self.host_rows.append(_oracle_quantize(w, threads))
-            del ws
-        # activations: one fp32 input per distinct input, resident on the device
-        self.inputs = []   # (fp32 device [m][k], quantized device buffer)
-        self.host_x = []
-        for layer in range(wl.LLAMA_LAYERS + 1):
-            mats = [mt for mt in self.mats if mt.layer == layer]
-            for mt in mats:
-                x = wl.activation(wl.BATCHED if m > 1 else wl.DECODE, mt.act, m, mt.k, group=layer)
-                xt = torch.from_numpy(x).to(dev)
-                qb = torch.empty(q8.q8_quantized_bytes(m, mt.k), dtype=torch.uint8, device=dev)
-                self.inputs.append((xt, qb))
-                self.host_x.append(x)
-        self.y = [torch.empty((m, mt.n), dtype=torch.float32, device=dev) for mt in self.mats]
-        need = max(q8.q8_matmul_workspace_bytes(m, mt.n, mt.k) for mt in self.mats)
-        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        self.weight_bytes = sum(mt.n * (mt.k // 32) * 34 for mt in self.mats)
-        self.act_bytes = sum(m * (mt.k // 32) * 34 for mt in self.mats)
-        self.out_bytes = sum(4 * m * mt.n for mt in self.mats)
-
-    def run(self, stream, gemv_timers=None):
-        q8 = self.q8
-        s = stream.cuda_stream
-        for i, mt in enumerate(self.mats):
-            xt, qb = self.inputs[i]
-            q8.q8_quantize_rows(xt, mt.k, self.m, mt.k, q8.Q8_LAYOUT_ACT, qb, s)
-            if gemv_timers is not None:
-                gemv_timers[i].start()
-            q8.q8_matmul(qb, self.m, self.w_packed[i], q8.Q8_LAYOUT_PACKED, mt.n, mt.k, self.y[i], mt.n,
-                         self.ws, self.ws.numel(), s)
-            if gemv_timers is not None:
-                gemv_timers[i].stop()
-
-    def gemv_bytes(self, i):
-        mt = self.mats[i]
-        return mt.n * (mt.k // 32) * 34 + self.m * (mt.k // 32) * 34 + 4 * self.m * mt.n
+def base_record(args, metric, value, unit, ms_per_step, dtype, config, roofline, cpu):
+    return {
+        "metric": metric,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": config,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
 
 
-def _oracle_quantize(w: np.ndarray, threads: int) -> np.ndarray:
+def hbm_roofline(kernel, bytes_per_launch, avg_ms):
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    return {
+        "kernel": kernel,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "avg_launch_us": round(avg_ms * 1e3, 3),
+        "algorithmic_bytes_per_launch": int(bytes_per_launch),
+    }
+
+
+def graph_time(run, stream, steps, warmup):
+    """Capture run(stream) into a graph, replay warmup + steps times; returns
+    (ms per replay, graph)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run(stream)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t = Timer(torch.cuda.current_stream())
+    t.start()
+    for _ in range(steps):
+        g.replay()
+    t.stop()
+    ms = t.ms() / steps
+    torch.cuda.synchronize()
+    return ms, g
+
+
+def oracle_rows(w: np.ndarray, threads: int) -> np.ndarray:
     """Oracle quantization of a weight matrix into ROWS layout, split over row
     chunks on a thread pool (the C call releases the GIL)."""
     import oracle
@@ -157,46 +149,109 @@ def _oracle_quantize(w: np.ndarray, threads: int) -> np.ndarray:
     return out
 
 
-def bench_decode(args):
+def timed_repeat(fn, min_seconds=2.0, max_reps=50):
+    """Run fn until min_seconds have passed; returns seconds per call."""
+    reps, t0 = 0, time.time()
+    while True:
+        fn()
+        reps += 1
+        dt = time.time() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            return dt / reps, reps
+
+
+# --------------------------------------------------------------------------
+# decode step (batch m) and the single GEMV
+# --------------------------------------------------------------------------
+
+class DecodeStep:
+    def __init__(self, mats, workload, m, threads, keep_host_rows, fused):
+        import torch
+
+        import workloads as wl
+        from decode_q8_amd import q8
+
+        self.q8, self.m, self.mats, self.fused = q8, m, mats, fused
+        dev = torch.device("cuda", 0)
+        self.w_packed, self.host_rows = [], []
+        chunk = 8
+        for c0 in range(0, len(mats), chunk):
+            group = mats[c0:c0 + chunk]
+            ws = wl.many(lambda mt: wl.weight(workload, mt.index, mt.n, mt.k, group=mt.layer),
+                         [(mt,) for mt in group], threads)
+            for mt, w in zip(group, ws):
+                wt = torch.from_numpy(w).to(dev)
+                wr = q8.quantize(wt, q8.Q8_LAYOUT_ROWS)
+                self.w_packed.append(q8.repack(wr, mt.n, mt.k))
+                del wt, wr
+                if keep_host_rows:
+                    self.host_rows.append(oracle_rows(w, threads))
+            del ws
+        self.inputs, self.host_x = [], []
+        for mt in mats:
+            x = wl.activation(workload, mt.act, m, mt.k, group=mt.layer)
+            xt = torch.from_numpy(x).to(dev)
+            qb = torch.empty(q8.q8_quantized_bytes(m, mt.k), dtype=torch.uint8, device=dev)
+            self.inputs.append((xt, qb))
+            self.host_x.append(x)
+        self.y = [torch.empty((m, mt.n), dtype=torch.float32, device=dev) for mt in mats]
+        self.weight_bytes = sum(mt.n * (mt.k // 32) * 34 for mt in mats)
+        torch.cuda.synchronize()
+
+    def run(self, stream, gemv_timers=None):
+        q8 = self.q8
+        s = stream.cuda_stream
+        for i, mt in enumerate(self.mats):
+            xt, qb = self.inputs[i]
+            if not self.fused:
+                q8.q8_quantize_rows(xt, mt.k, self.m, mt.k, q8.Q8_LAYOUT_ACT, qb, s)
+            if gemv_timers is not None:
+                gemv_timers[i].start()
+            if self.fused:
+                q8.q8_quantize_matmul(xt, mt.k, self.m, self.w_packed[i], q8.Q8_LAYOUT_PACKED, mt.n, mt.k,
+                                      self.y[i], mt.n, s)
+            else:
+                q8.q8_matmul(qb, self.m, self.w_packed[i], q8.Q8_LAYOUT_PACKED, mt.n, mt.k, self.y[i], mt.n,
+                             None, 0, s)
+            if gemv_timers is not None:
+                gemv_timers[i].stop()
+
+    def gemv_bytes(self, i):
+        """Algorithmic bytes of matrix i's GEMV launch: weights once, the
+        activation once (fp32 when quantized inside the kernel, Q8_0 bytes
+        otherwise), the outputs once."""
+        mt = self.mats[i]
+        act = 4 * self.m * mt.k if self.fused else self.m * (mt.k // 32) * 34
+        return mt.n * (mt.k // 32) * 34 + act + 4 * self.m * mt.n
+
+    def oracle_step(self, threads):
+        import oracle
+        for i, mt in enumerate(self.mats):
+            xa = oracle.quantize_rows(self.host_x[i], oracle.LAYOUT_ACT)
+            oracle.matmul(xa, self.m, self.host_rows[i], mt.n, mt.k, threads=threads)
+
+
+def bench_gemv_workload(args, mats, workload, m, label):
     import torch
-    m = args.m if args.workload == "batched" else 1
     t0 = time.time()
-    step = DecodeStep(m, args.threads, keep_host_rows=not args.no_cpu_baseline)
+    step = DecodeStep(mats, workload, m, args.threads, keep_host_rows=not args.no_cpu_baseline,
+                      fused=not args.unfused)
     prep_s = time.time() - t0
     stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
 
-    # eager reference outputs
     with torch.cuda.stream(stream):
         step.run(stream)
     torch.cuda.synchronize()
     eager = [y.clone() for y in step.y]
-
-    # capture one step into a graph
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        step.run(stream)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    t = Timer(torch.cuda.current_stream())
-    t.start()
-    for _ in range(args.steps):
-        g.replay()
-    t.stop()
-    total_ms = t.ms()
-    torch.cuda.synchronize()
-    ms_per_step = total_ms / args.steps
-    # every replay wrote the same bits as the eager step
+    ms_per_step, _ = graph_time(step.run, stream, args.steps, args.warmup)
     for i, y in enumerate(step.y):
         if not torch.equal(y.view(torch.int32), eager[i].view(torch.int32)):
             raise RuntimeError(f"graph replay output {i} differs from the eager step")
 
-    # dominant kernel: the GEMV, timed per launch with events on its stream
+    # the dominant kernel (the GEMV), each launch bracketed by events on its stream
     timers = [Timer(stream) for _ in step.mats]
     gemv_ms = np.zeros(len(step.mats))
-    reps = max(1, min(args.steps, 5))
+    reps = max(1, min(args.steps, 10))
     for _ in range(reps):
         with torch.cuda.stream(stream):
             step.run(stream, timers)
@@ -204,80 +259,245 @@ def bench_decode(args):
         gemv_ms += np.array([tm.ms() for tm in timers])
     gemv_ms /= reps
     gemv_bytes = np.array([step.gemv_bytes(i) for i in range(len(step.mats))], dtype=np.float64)
-    avg_ms = float(gemv_ms.mean())
-    achieved = float(gemv_bytes.mean() / (avg_ms * 1e-3) / 1e9)
 
     value = step.weight_bytes / (ms_per_step * 1e-3) / 1e9
-    per_mat = {}
+    per = {}
     for i, mt in enumerate(step.mats):
-        key = mt.name
-        b, ms = per_mat.get(key, (0.0, 0.0))
-        per_mat[key] = (b + gemv_bytes[i], ms + gemv_ms[i])
-    per_shape = {k: round(b / (ms * 1e-3) / 1e9, 1) for k, (b, ms) in per_mat.items()}
+        b, ms = per.get(mt.name, (0.0, 0.0))
+        per[mt.name] = (b + gemv_bytes[i], ms + gemv_ms[i])
+    per_matrix = {k: round(b / (ms * 1e-3) / 1e9, 1) for k, (b, ms) in per.items()}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_decode(step, args.threads)
+        sec, reps_c = timed_repeat(lambda: step.oracle_step(args.threads))
+        cpu = {"value": round(step.weight_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": args.threads,
+               "kind": "oracle",
+               "sample": f"the whole {label} ({len(mats)} matrices, quantize + matmul), {reps_c} runs, "
+                         f"{sec:.3f} s each"}
 
-    out = {
-        "metric": "Q8_0 matmul weight GB/s (%HBM peak) at M=1" if m == 1 else f"Q8_0 matmul weight GB/s at M={m}",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "int8xint8->int32, fp32 scale/sum",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
-        "config": {
-            "workload": f"Llama-3.2-1B-shaped decode step, batch {m}: 16 x (QKV 3072x2048, O 2048x2048, "
-                        "gate||up 16384x2048, down 2048x8192) + LM head 128256x2048, Q8_0 packed",
-            "m": m,
-            "weight_bytes": step.weight_bytes,
-            "launches_per_step": "%d quantize + %d GEMV (+ chain passes)" % (len(step.mats), len(step.mats)),
-            "hip_graph": True,
-            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-            "gemv_GBs_by_matrix": per_shape,
-            "prep_seconds": round(prep_s, 1),
-        },
-        "roofline": {
-            "kernel": f"q8k::gemv_kernel<{m}, packed>",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "avg_launch_us": round(avg_ms * 1e3, 3),
-            "algorithmic_bytes_per_launch": int(gemv_bytes.mean()),
-        },
-        "cpu_baseline": cpu,
+    kname = "q8k::gemv_kernel<%d, packed, %s>" % (m, "fp32 in" if step.fused else "int8 in")
+    config = {
+        "workload": label,
+        "m": m,
+        "weight_bytes": step.weight_bytes,
+        "launches_per_step": (f"{len(mats)} fused quantize+GEMV" if step.fused
+                              else f"{len(mats)} quantize + {len(mats)} GEMV"),
+        "hip_graph": True,
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "gemv_GBs_by_matrix": per_matrix,
+        "gemv_us_by_matrix": {mt.name: round(float(gemv_ms[i]) * 1e3, 2) for i, mt in enumerate(step.mats)
+                              if mt.layer == 0 or mt.name == "lm_head"},
+        "prep_seconds": round(prep_s, 1),
     }
-    return out
+    metric = ("Q8_0 matmul weight GB/s (%HBM peak) at M=1" if m == 1 else f"Q8_0 matmul weight GB/s at M={m}")
+    return base_record(args, metric, value, "GB/s", ms_per_step, "int8xint8->int32, fp32 scale/sum", config,
+                       hbm_roofline(kname, float(gemv_bytes.mean()), float(gemv_ms.mean())), cpu)
 
 
-def cpu_baseline_decode(step, threads):
-    """The oracle (quantize each input, then its matmul with fp64
-    accumulation) over the whole decode step on the host cores."""
-    import oracle
-    t0 = time.time()
-    for i, mt in enumerate(step.mats):
-        xa = oracle.quantize_rows(step.host_x[i], oracle.LAYOUT_ACT)
-        oracle.matmul(xa, step.m, step.host_rows[i], mt.n, mt.k, threads=threads)
-    dt = time.time() - t0
-    return {
-        "value": round(step.weight_bytes / dt / 1e9, 3),
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": "one whole decode step (all 65 matrices, quantize + matmul), %.2f s" % dt,
-    }
+def bench_decode(args):
+    import workloads as wl
+    m = args.m if args.workload == "batched" else 1
+    label = (f"Llama-3.2-1B-shaped decode step, batch {m}: 16 x (QKV 3072x2048, O 2048x2048, "
+             "gate||up 16384x2048, down 2048x8192) + LM head 128256x2048, Q8_0 packed")
+    return bench_gemv_workload(args, wl.decode_matrices(), wl.BATCHED if m > 1 else wl.DECODE, m, label)
+
+
+def bench_single(args):
+    import workloads as wl
+    mats = [wl.Matrix("w", 2048, 2048, 0, 0, 0)]
+    return bench_gemv_workload(args, mats, wl.SINGLE, 1, "single Q8_0 GEMV, W 2048x2048, one activation row")
 
 
 # --------------------------------------------------------------------------
+# prefill GEMM
+# --------------------------------------------------------------------------
+
+def bench_prefill(args):
+    import torch
+
+    import oracle
+    import workloads as wl
+    from decode_q8_amd import q8
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.Stream()
+    cases = []
+    for (n, k) in wl.PREFILL_NK:
+        w = wl.weight(wl.PREFILL, n + k, n, k)
+        wr = q8.quantize(torch.from_numpy(w).to(dev), q8.Q8_LAYOUT_ROWS)
+        wp = q8.repack(wr, n, k)
+        host_rows = None if args.no_cpu_baseline else oracle_rows(w, args.threads)
+        for m in wl.PREFILL_M:
+            x = wl.activation(wl.PREFILL, m, m, k, outliers=True)
+            xq = q8.quantize(torch.from_numpy(x).to(dev), q8.Q8_LAYOUT_ACT)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            cases.append(dict(m=m, n=n, k=k, xq=xq, wp=wp, y=y, x=x, rows=host_rows))
+    torch.cuda.synchronize()
+
+    def run(s, timers=None):
+        for i, c in enumerate(cases):
+            if timers is not None:
+                timers[i].start()
+            q8.q8_matmul(c["xq"], c["m"], c["wp"], q8.Q8_LAYOUT_PACKED, c["n"], c["k"], c["y"], c["n"], None, 0,
+                         s.cuda_stream)
+            if timers is not None:
+                timers[i].stop()
+
+    ms_per_step, _ = graph_time(run, stream, args.steps, args.warmup)
+    timers = [Timer(stream) for _ in cases]
+    ms = np.zeros(len(cases))
+    reps = max(1, min(args.steps, 10))
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            run(stream, timers)
+        torch.cuda.synchronize()
+        ms += np.array([t.ms() for t in timers])
+    ms /= reps
+    ops = np.array([2.0 * c["m"] * c["n"] * c["k"] for c in cases])
+    value = ops.sum() / (ms_per_step * 1e-3) / 1e12
+    per_case = {f"M{c['m']}_N{c['n']}_K{c['k']}": round(ops[i] / (ms[i] * 1e-3) / 1e12, 1)
+                for i, c in enumerate(cases)}
+    achieved = float(ops.mean() / (ms.mean() * 1e-3) / 1e12)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # bounded sample: 2048 outputs of every case, computed one by one
+        rng = np.random.default_rng(0)
+        pts = []
+        for c in cases:
+            xa = oracle.quantize_rows(c["x"], oracle.LAYOUT_ACT)
+            pts.append((c, xa, rng.integers(0, c["m"], 2048), rng.integers(0, c["n"], 2048)))
+        t0 = time.time()
+        for c, xa, mi, ni in pts:
+            oracle.matmul_points(xa, c["m"], c["rows"], c["n"], c["k"], mi, ni)
+        dt = time.time() - t0
+        cpu_ops = sum(2.0 * 2048 * c["k"] for c in cases)
+        cpu = {"value": round(cpu_ops / dt / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+               "sample": f"2048 outputs of each of the 9 prefill cases, single-threaded, {dt:.2f} s"}
+    config = {
+        "workload": "prefill GEMM: M in {188, 752, 2048} x (N, K) in {(2048, 2048), (8192, 2048), (2048, 8192)}, "
+                    "Q8_0 packed weights, activations with 1% outlier channels x20",
+        "ops_per_step": int(ops.sum()),
+        "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
+        "tops_by_case": per_case,
+        "hip_graph": True,
+    }
+    roof = {"kernel": "q8k::gemm_kernel", "bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+            "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+            "avg_launch_us": round(float(ms.mean()) * 1e3, 3), "algorithmic_ops_per_launch": int(ops.mean())}
+    return base_record(args, "Q8_0 prefill GEMM int8 TOPS (%MFMA peak)", value, "TOPS", ms_per_step,
+                       "int8xint8->int32 (MFMA), fp32 scale/sum", config, roof, cpu)
+
+
+# --------------------------------------------------------------------------
+# routed experts
+# --------------------------------------------------------------------------
+
+def bench_moe(args):
+    import torch
+
+    import oracle
+    import workloads as wl
+    from decode_q8_amd import q8
+    dev = torch.device("cuda", 0)
+    E, T, K8 = wl.MOE_EXPERTS, wl.MOE_TOKENS, wl.MOE_TOPK
+    ids = wl.routing(wl.MOE, T, E, K8)
+    ids_d = torch.from_numpy(ids).to(dev)
+    used = sorted(set(int(e) for e in np.unique(ids)))
+    mats = []
+    for mi, (name, n, k) in enumerate(wl.MOE_MATS):
+        stride = q8.q8_quantized_bytes(n, k)
+        buf = torch.empty(E * stride, dtype=torch.uint8, device=dev)
+        host = {}
+        for e0 in range(0, E, 16):
+            es = list(range(e0, min(E, e0 + 16)))
+            ws = wl.many(lambda e: wl.weight(wl.MOE, e, n, k, group=mi), [(e,) for e in es], args.threads)
+            for e, w in zip(es, ws):
+                wr = q8.quantize(torch.from_numpy(w).to(dev), q8.Q8_LAYOUT_ROWS)
+                q8.q8_repack_weights(wr, n, k, buf[e * stride:(e + 1) * stride])
+                if not args.no_cpu_baseline and e in used[:2]:
+                    host[e] = oracle_rows(w, args.threads)
+            del ws
+        per_pair = 1 if name == "down" else 0
+        rows = T * K8 if per_pair else T
+        x = wl.activation(wl.MOE, 100 + mi, rows, k)
+        xq = q8.quantize(torch.from_numpy(x).to(dev), q8.Q8_LAYOUT_ACT)
+        need = q8.q8_grouped_workspace_bytes(T, K8, E, n, k)
+        mats.append(dict(name=name, n=n, k=k, stride=stride, buf=buf, rows=rows, per_pair=per_pair, x=x, xq=xq,
+                         y=torch.empty((T * K8, n), dtype=torch.float32, device=dev),
+                         ws=torch.empty(need, dtype=torch.uint8, device=dev), need=need, host=host))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+
+    def run(s, timers=None):
+        for i, c in enumerate(mats):
+            if timers is not None:
+                timers[i].start()
+            q8.q8_grouped_matmul(c["xq"], c["rows"], c["per_pair"], ids_d, T, K8, c["buf"], E, c["stride"], c["n"],
+                                 c["k"], c["y"], c["ws"], c["need"], s.cuda_stream)
+            if timers is not None:
+                timers[i].stop()
+
+    ms_per_step, _ = graph_time(run, stream, args.steps, args.warmup)
+    timers = [Timer(stream) for _ in mats]
+    ms = np.zeros(len(mats))
+    reps = max(1, min(args.steps, 10))
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            run(stream, timers)
+        torch.cuda.synchronize()
+        ms += np.array([t.ms() for t in timers])
+    ms /= reps
+    U = len(used)
+    wbytes = np.array([U * c["stride"] for c in mats], dtype=np.float64)
+    abytes = np.array([wbytes[i] + c["rows"] * (c["k"] // 32) * 34 + 4 * T * K8 * c["n"] for i, c in enumerate(mats)])
+    value = wbytes.sum() / (ms_per_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        # bounded sample: every pair routed to the first two used experts
+        t0 = time.time()
+        nb = 0
+        for c in mats:
+            xa = oracle.quantize_rows(c["x"], oracle.LAYOUT_ACT)
+            for e, rows_e in c["host"].items():
+                pairs = [p for p in range(T * K8) if ids.reshape(-1)[p] == e]
+                for p in pairs:
+                    xr = p if c["per_pair"] else p // K8
+                    one = oracle.quantize_rows(c["x"][xr:xr + 1], oracle.LAYOUT_ACT)
+                    oracle.matmul(one, 1, rows_e, c["n"], c["k"], threads=args.threads)
+                    nb += c["stride"]
+        dt = time.time() - t0
+        cpu = {"value": round(nb / dt / 1e9, 3), "unit": "GB/s", "cores": args.threads, "kind": "oracle",
+               "sample": f"every routed pair of 2 experts per matrix (one matmul per pair), {dt:.2f} s"}
+    config = {
+        "workload": "MoE grouped GEMV: 256 experts (gate, up 2048x7168; down 7168x2048), 16 tokens, top-8 of "
+                    "uniform logits",
+        "distinct_experts": U,
+        "expected_distinct_experts": round(256 * (1 - (1 - 8 / 256) ** 16), 2),
+        "weight_bytes_per_step": int(wbytes.sum()),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "GBs_by_matrix": {c["name"]: round(wbytes[i] / (ms[i] * 1e-3) / 1e9, 1) for i, c in enumerate(mats)},
+        "hip_graph": True,
+    }
+    roof = hbm_roofline("q8k::grouped_gemv_kernel", float(abytes.mean()), float(ms.mean()))
+    roof["note"] = "launch time includes the expert-grouping kernel that precedes the GEMV in each call"
+    return base_record(args, "Q8_0 routed-expert GEMV weight GB/s (%HBM peak)", value, "GB/s", ms_per_step,
+                       "int8xint8->int32, fp32 scale/sum", config, roof, cpu)
+
+
+# --------------------------------------------------------------------------
+
+def bench_copy(args):
+    """1 GiB device-to-device copy: known bytes for calibrating byte counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    stream = torch.cuda.Stream()
+    ms_per_step, _ = graph_time(lambda s: b.copy_(a), stream, args.steps, args.warmup)
+    value = 2.0 * n / (ms_per_step * 1e-3) / 1e9
+    return base_record(args, "device copy GB/s (read + write)", value, "GB/s", ms_per_step, "u8",
+                       {"workload": "copy 1 GiB", "bytes_read": n, "bytes_written": n}, None, None)
+
 
 def main():
     args = parse()
@@ -289,11 +509,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
-    if args.workload in ("decode", "batched"):
-        out = bench_decode(args)
-    else:
-        raise SystemExit(f"workload {args.workload} not implemented yet")
-    print(json.dumps(out), flush=True)
+    fn = {"decode": bench_decode, "batched": bench_decode, "single": bench_single, "prefill": bench_prefill,
+          "moe": bench_moe, "copy": bench_copy}[args.workload]
+    print(json.dumps(fn(args)), flush=True)
 
 
 if __name__ == "__main__":

@@ -25,10 +25,12 @@ from .q8 import (  # noqa: F401
     q8_grouped_workspace_bytes,
     q8_matmul,
     q8_matmul_workspace_bytes,
+    q8_quantize_matmul,
     q8_quantize_rows,
     q8_quantized_bytes,
     q8_repack_weights,
     q8_status_str,
     quantize,
+    quantize_matmul,
     repack,
 )

@@ -108,6 +108,18 @@ int q8_matmul(const void *x_q, int64_t m, const void *w, int layout, int64_t n, 
     return launched(q8k::launch_gemm(x_q, m, w, n, k, y, ld_y, stream));
 }
 
+int q8_quantize_matmul(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
+                       float *y, int64_t ld_y, hipStream_t stream) {
+    if (!x || !w || !y || m <= 0 || n <= 0 || k <= 0 || ld_x < k || ld_y < n) return Q8_ERR_ARG;
+    if (layout != Q8_LAYOUT_ROWS && layout != Q8_LAYOUT_PACKED) return Q8_ERR_ARG;
+    if (m > Q8_GEMV_MAX_ROWS || k % (Q8_BLOCK * Q8_TILE_BLOCKS)) return Q8_ERR_SHAPE;
+    if (layout == Q8_LAYOUT_PACKED && n % Q8_TILE_ROWS) return Q8_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || ld_x % 4) return Q8_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_gemv_f32(x, ld_x, m, w, layout, n, k, y, ld_y, stream));
+}
+
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k) {
     (void)n;
     (void)k;

@@ -15,9 +15,10 @@
 //    (64 rows x 16 values); a row's 8 scales arrive in one 16-byte load;
 //  - activations are wave-uniform: the compiler reads them with scalar loads
 //    into SGPRs, which feed v_dot4c directly (no LDS traffic);
-//  - narrow matrices (fewer than 1024 row tiles) run one group per wave and a
-//    second pass chains the group sums in order, which yields the same bits
-//    as one wave walking all groups.
+//  - one workgroup per tile; narrow matrices (fewer than 1024 tiles) give
+//    the tile to up to 8 waves that split its groups and chain the group sums
+//    in LDS in the same left-to-right order a single wave uses, so the bits
+//    do not depend on the split.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -106,62 +107,115 @@ __device__ __forceinline__ void group_sums(const GroupRegs &g, const int8_t *con
     }
 }
 
-// Walk groups [g0, g1) of one lane's row and chain the group sums.
+// Group sums with the activation quantization fused in: xf[m] points at the
+// group's 256 fp32 values of row m.  Lane l quantizes values 4l..4l+3 (block
+// l / 8) with exactly the arithmetic of the standalone quantizer (amax over
+// the block by an exact max butterfly, d = amax / 127, q = round-half-away of
+// x / d, stored scale fp16(d)), so the codes and scales are bit-identical to
+// q8_quantize_rows.  The packed codes and scales are then broadcast from their
+// lane to the whole wave (v_readlane) as v_dot4c's scalar operand.
+template <int M>
+__device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float *const (&xf)[M], int lane,
+                                               float (&u)[M]) {
+    float dw[8];
+#pragma unroll
+    for (int bb = 0; bb < 8; bb++) dw[bb] = half_bits_to_float(half_of(g.c[16], bb));
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const float4 v = *reinterpret_cast<const float4 *>(xf[m] + 4 * lane);
+        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const float d = amax / 127.0f;
+        int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+        if (d != 0.0f) {
+            q0 = (int)roundf(v.x / d);
+            q1 = (int)roundf(v.y / d);
+            q2 = (int)roundf(v.z / d);
+            q3 = (int)roundf(v.w / d);
+        }
+        const int qd = (int)(((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
+                             ((uint32_t)q3 << 24));
+        const float dxl = half_bits_to_float(float_to_half_bits(d));
+        float t[8];
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) {
+            int s = 0;
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    s = __builtin_amdgcn_sdot4((int)word_of(g.c[2 * bb + h], c),
+                                               __builtin_amdgcn_readlane(qd, 8 * bb + 4 * h + c), s, false);
+            const float dx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dxl), 8 * bb));
+            t[bb] = (float)s * (dw[bb] * dx);
+        }
+        u[m] = tree8(t);
+    }
+}
+
+// Walk groups [g0, g1) of one lane's row.  TO_LDS = false: chain the group
+// sums into acc (the wave owns the whole row).  TO_LDS = true: store each
+// group sum u_g at lds[(g * M + m) * 64 + lane] for a later in-order chain.
 // wbase/gstride: address of group 0 of this lane and the step between groups.
-template <int M, int LAYOUT>
-__device__ __forceinline__ void row_chain(const uint8_t *wbase, int64_t gstride, int64_t g0, int64_t g1,
-                                          const int8_t *const (&xrow)[M], const uint16_t *const (&srow)[M],
-                                          float (&acc)[M]) {
+template <int M, int LAYOUT, bool TO_LDS, typename ACT>
+__device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride, int64_t g0, int64_t g1,
+                                           const ACT *const (&xrow)[M], const uint16_t *const (&srow)[M],
+                                           float (&acc)[M], float *lds, int lane) {
+    if (g0 >= g1) return;
     GroupRegs cur, nxt;
     load_group<LAYOUT>(cur, wbase + g0 * gstride);
     for (int64_t g = g0; g < g1; g++) {
         if (g + 1 < g1) load_group<LAYOUT>(nxt, wbase + (g + 1) * gstride);
         if (LAYOUT == 0) rows_to_packed(cur);
-        const int8_t *xg[M];
-        const uint16_t *sg[M];
+        const ACT *xg[M];
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            xg[m] = xrow[m] + g * GROUP_K;
-            sg[m] = srow[m] + g * GROUP_BLOCKS;
-        }
+        for (int m = 0; m < M; m++) xg[m] = xrow[m] + g * GROUP_K;
         float u[M];
-        group_sums<M>(cur, xg, sg, u);
+        if constexpr (sizeof(ACT) == 1) {
+            const uint16_t *sg[M];
 #pragma unroll
-        for (int m = 0; m < M; m++) acc[m] = (g == g0) ? u[m] : acc[m] + u[m];
+            for (int m = 0; m < M; m++) sg[m] = srow[m] + g * GROUP_BLOCKS;
+            group_sums<M>(cur, xg, sg, u);
+        } else {
+            group_sums_f32<M>(cur, xg, lane, u);
+        }
+        if (TO_LDS) {
+#pragma unroll
+            for (int m = 0; m < M; m++) lds[(g * M + m) * TILE_ROWS + lane] = u[m];
+        } else {
+#pragma unroll
+            for (int m = 0; m < M; m++) acc[m] = (g == g0) ? u[m] : acc[m] + u[m];
+        }
         cur = nxt;
     }
 }
 
-template <int M, int LAYOUT>
-__global__ __launch_bounds__(256) void gemv_kernel(const int8_t *__restrict__ xq, const uint16_t *__restrict__ xs,
-                                                   const uint8_t *__restrict__ w, int64_t n, int64_t k,
-                                                   float *__restrict__ y, int64_t ld_y, float *__restrict__ part,
-                                                   int split) {
+// One workgroup per 64-row tile; its W waves take contiguous, balanced ranges
+// of the k/256 groups.  With W = 1 the single wave chains in registers; with
+// W > 1 every group sum goes to LDS and, after a barrier, the workgroup chains
+// them left to right.  Either way each output is ((u_0 + u_1) + u_2) + ...
+template <int M, int LAYOUT, typename ACT>
+__global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, int64_t ld_x,
+                                                   const uint16_t *__restrict__ xs, const uint8_t *__restrict__ w,
+                                                   int64_t n, int64_t k, float *__restrict__ y, int64_t ld_y) {
+    extern __shared__ float lds_u[];  // [G][M][64] when W > 1
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + wave_id();
+    const int wv = wave_id();
+    const int W = blockDim.x >> 6;
+    const int64_t T = blockIdx.x;
     const int64_t G = k / GROUP_K;
-    const int64_t tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
-    int64_t T, g0, g1;
-    if (split) {
-        if (unit >= tiles * G) return;
-        T = unit / G;
-        g0 = unit - T * G;
-        g1 = g0 + 1;
-    } else {
-        if (unit >= tiles) return;
-        T = unit;
-        g0 = 0;
-        g1 = G;
-    }
+    const int64_t g0 = wv * G / W, g1 = (wv + 1) * G / W;
     const int64_t row = T * TILE_ROWS + lane;
     const bool row_ok = row < n;
     const int64_t row_c = row_ok ? row : n - 1;
 
-    const int8_t *xrow[M];
+    const ACT *xrow[M];
     const uint16_t *srow[M];
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        xrow[m] = xq + m * k;
+        xrow[m] = xq + m * ld_x;
         srow[m] = xs + m * (k / QK);
     }
     const uint8_t *wbase;
@@ -174,49 +228,50 @@ __global__ __launch_bounds__(256) void gemv_kernel(const int8_t *__restrict__ xq
         gstride = ROW_GROUP_BYTES;
     }
     float acc[M];
-    row_chain<M, LAYOUT>(wbase, gstride, g0, g1, xrow, srow, acc);
-    if (!row_ok) return;
-    if (split) {
+    if (W == 1) {
+        row_groups<M, LAYOUT, false>(wbase, gstride, 0, G, xrow, srow, acc, nullptr, lane);
+        if (row_ok) {
 #pragma unroll
-        for (int m = 0; m < M; m++) part[(g0 * M + m) * n + row] = acc[m];
-    } else {
-#pragma unroll
-        for (int m = 0; m < M; m++) y[m * ld_y + row] = acc[m];
+            for (int m = 0; m < M; m++) y[m * ld_y + row] = acc[m];
+        }
+        return;
+    }
+    row_groups<M, LAYOUT, true>(wbase, gstride, g0, g1, xrow, srow, acc, lds_u, lane);
+    __syncthreads();
+    for (int t = threadIdx.x; t < M * TILE_ROWS; t += blockDim.x) {
+        const int m = t >> 6, r = t & 63;
+        float a = lds_u[m * TILE_ROWS + r];
+        for (int64_t g = 1; g < G; g++) a += lds_u[(g * M + m) * TILE_ROWS + r];
+        const int64_t out_row = T * TILE_ROWS + r;
+        if (out_row < n) y[m * ld_y + out_row] = a;
     }
 }
 
-// Second pass of a split GEMV: y = ((u_0 + u_1) + u_2) + ... per output.
-__global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ part, int64_t m, int64_t n, int64_t G,
-                                                    float *__restrict__ y, int64_t ld_y) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= m * n) return;
-    const int64_t mi = idx / n, ni = idx - mi * n;
-    float acc = part[mi * n + ni];
-    for (int64_t g = 1; g < G; g++) acc += part[(g * m + mi) * n + ni];
-    y[mi * ld_y + ni] = acc;
+constexpr int GEMV_MAX_WAVES = 8;
+constexpr int64_t GEMV_LDS_LIMIT = 64 * 1024;
+
+// Waves per tile: enough workgroups x waves to cover the machine (about 2048
+// waves), at most one wave per group, and the group sums must fit in LDS.
+// Only speed depends on this choice; the bits do not.
+int gemv_waves(int64_t m, int64_t n, int64_t k) {
+    const int64_t tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
+    const int64_t G = k / GROUP_K;
+    if (tiles >= 1024 || G == 1) return 1;
+    int64_t W = (2048 + tiles - 1) / tiles;
+    if (W > GEMV_MAX_WAVES) W = GEMV_MAX_WAVES;
+    if (W > G) W = G;
+    if (G * m * TILE_ROWS * (int64_t)sizeof(float) > GEMV_LDS_LIMIT) W = 1;
+    return (int)W;
 }
 
-GemvPlan gemv_plan(int64_t n, int64_t k) {
-    GemvPlan p;
-    p.tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
-    p.groups = k / GROUP_K;
-    p.split = p.tiles < 1024 && p.groups > 1;
-    return p;
-}
+size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k) { return 0; }
 
-size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-    const GemvPlan p = gemv_plan(n, k);
-    if (!p.split) return 0;
-    return (size_t)(p.groups * m * n) * sizeof(float);
-}
-
-template <int LAYOUT>
-static void launch_gemv_m(int64_t m, dim3 grid, hipStream_t s, const int8_t *xq, const uint16_t *xs,
-                          const uint8_t *w, int64_t n, int64_t k, float *y, int64_t ld_y, float *part, int split) {
-#define Q8_GEMV_CASE(MM)                                                                                      \
-    case MM:                                                                                                  \
-        hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT>), grid, dim3(256), 0, s, xq, xs, w, n, k, y, ld_y, part, \
-                           split);                                                                            \
+template <int LAYOUT, typename ACT>
+static void launch_gemv_m(int64_t m, dim3 grid, dim3 block, size_t lds, hipStream_t s, const ACT *x, int64_t ld_x,
+                          const uint16_t *xs, const uint8_t *w, int64_t n, int64_t k, float *y, int64_t ld_y) {
+#define Q8_GEMV_CASE(MM)                                                                                    \
+    case MM:                                                                                                \
+        hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT, ACT>), grid, block, lds, s, x, ld_x, xs, w, n, k, y, ld_y); \
         break;
     switch (m) {
         Q8_GEMV_CASE(1) Q8_GEMV_CASE(2) Q8_GEMV_CASE(3) Q8_GEMV_CASE(4)
@@ -226,24 +281,31 @@ static void launch_gemv_m(int64_t m, dim3 grid, hipStream_t s, const int8_t *xq,
 #undef Q8_GEMV_CASE
 }
 
+template <typename ACT>
+static hipError_t launch_gemv_any(const ACT *x, int64_t ld_x, const uint16_t *xs, int64_t m, const void *w,
+                                  int layout, int64_t n, int64_t k, float *y, int64_t ld_y, hipStream_t s) {
+    const int64_t tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
+    const int W = gemv_waves(m, n, k);
+    const size_t lds = W > 1 ? (size_t)((k / GROUP_K) * m * TILE_ROWS) * sizeof(float) : 0;
+    const dim3 grid((unsigned)tiles), block((unsigned)(64 * W));
+    if (layout == 1)
+        launch_gemv_m<1, ACT>(m, grid, block, lds, s, x, ld_x, xs, (const uint8_t *)w, n, k, y, ld_y);
+    else
+        launch_gemv_m<0, ACT>(m, grid, block, lds, s, x, ld_x, xs, (const uint8_t *)w, n, k, y, ld_y);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y,
                        int64_t ld_y, void *workspace, hipStream_t s) {
-    const GemvPlan p = gemv_plan(n, k);
+    (void)workspace;
     const int8_t *xq = (const int8_t *)x_q;
     const uint16_t *xs = (const uint16_t *)((const uint8_t *)x_q + m * k);
-    const int64_t units = p.split ? p.tiles * p.groups : p.tiles;
-    const dim3 grid((unsigned)((units + 3) / 4));
-    float *part = (float *)workspace;
-    if (layout == 1)
-        launch_gemv_m<1>(m, grid, s, xq, xs, (const uint8_t *)w, n, k, y, ld_y, part, p.split ? 1 : 0);
-    else
-        launch_gemv_m<0>(m, grid, s, xq, xs, (const uint8_t *)w, n, k, y, ld_y, part, p.split ? 1 : 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !p.split) return e;
-    const int64_t outs = m * n;
-    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, part, m, n, p.groups,
-                       y, ld_y);
-    return hipGetLastError();
+    return launch_gemv_any<int8_t>(xq, k, xs, m, w, layout, n, k, y, ld_y, s);
+}
+
+hipError_t launch_gemv_f32(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
+                           float *y, int64_t ld_y, hipStream_t s) {
+    return launch_gemv_any<float>(x, ld_x, nullptr, m, w, layout, n, k, y, ld_y, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -342,7 +404,7 @@ __device__ __forceinline__ void expert_pass(const int8_t *xq, const uint16_t *xs
         srow[i] = xs + xr * (k / QK);
     }
     float acc[M];
-    row_chain<M, 1>(wbase, RECORD_BYTES, 0, G, xrow, srow, acc);
+    row_groups<M, 1, false>(wbase, RECORD_BYTES, 0, G, xrow, srow, acc, nullptr, 0);
 #pragma unroll
     for (int i = 0; i < M; i++) y[(int64_t)p[i] * n + row] = acc[i];
 }

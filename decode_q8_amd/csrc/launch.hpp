@@ -13,19 +13,16 @@ hipError_t launch_quantize(const float *x, int64_t ld_x, int64_t rows, int64_t k
 
 hipError_t launch_repack(const void *w_rows, int64_t n, int64_t k, void *w_packed, hipStream_t s);
 
-// GEMV execution plan for an (n, k) weight: whole rows per wave, or one
-// summation group per wave with a second pass that chains the group sums.
-// Both produce the same bits; the choice only changes speed.
-struct GemvPlan {
-    int64_t tiles;   // ceil(n / 64)
-    int64_t groups;  // k / 256
-    bool split;      // one group per wave + chaining pass
-};
-GemvPlan gemv_plan(int64_t n, int64_t k);
+// Waves per 64-row tile of a GEMV (only speed depends on it).
+int gemv_waves(int64_t m, int64_t n, int64_t k);
 size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 hipError_t launch_gemv(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y,
                        int64_t ld_y, void *workspace, hipStream_t s);
+
+// GEMV from fp32 activations, quantized inside the kernel (m <= 8).
+hipError_t launch_gemv_f32(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
+                           float *y, int64_t ld_y, hipStream_t s);
 
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s);

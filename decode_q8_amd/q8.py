@@ -32,6 +32,7 @@ SIGNATURES = {
     "q8_repack_weights": ([_P, _I64, _I64, _P, _P], _I),
     "q8_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q8_matmul": ([_P, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
+    "q8_quantize_matmul": ([_P, _I64, _I64, _P, _I, _I64, _I64, _P, _I64, _P], _I),
     "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
     "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
 }
@@ -124,6 +125,11 @@ def q8_matmul(x_q, m: int, w, layout: int, n: int, k: int, y, ld_y: int, workspa
                                   workspace_bytes, _stream(stream)), "q8_matmul")
 
 
+def q8_quantize_matmul(x, ld_x: int, m: int, w, layout: int, n: int, k: int, y, ld_y: int, stream=None) -> int:
+    return _check(lib().q8_quantize_matmul(_ptr(x), ld_x, m, _ptr(w), layout, n, k, _ptr(y), ld_y, _stream(stream)),
+                  "q8_quantize_matmul")
+
+
 def q8_grouped_matmul(x_q, x_rows: int, x_per_pair: int, topk_ids, tokens: int, topk: int, w_experts,
                       n_experts: int, expert_stride_bytes: int, n: int, k: int, y, workspace, workspace_bytes: int,
                       stream=None) -> int:
@@ -149,6 +155,16 @@ def repack(w_rows, n: int, k: int, stream=None):
     out = torch.empty_like(w_rows)
     q8_repack_weights(w_rows, n, k, out, stream)
     return out
+
+
+def quantize_matmul(x, w, layout: int, n: int, stream=None):
+    """fp32 [m][k] CUDA tensor (m <= 8) -> new fp32 [m][n] tensor."""
+    import torch
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    m, k = x.shape
+    y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    q8_quantize_matmul(x, x.stride(0), m, w, layout, n, k, y, n, stream)
+    return y
 
 
 def matmul(x_q, m: int, w, layout: int, n: int, k: int, workspace=None, stream=None):

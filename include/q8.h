@@ -121,7 +121,7 @@ int q8_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int 
 int q8_repack_weights(const void *w_rows, int64_t n, int64_t k, void *w_packed, hipStream_t stream);
 
 /* Workspace bytes q8_matmul needs for this shape (0 when none).  Depends on
- * (m, n, k) only. */
+ * (m, n, k) only; every shape currently needs none (pass NULL, 0). */
 size_t q8_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* y[i][j] = sum over blocks of x_q row i against weight row j (the Q8_0
@@ -139,6 +139,21 @@ size_t q8_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_matmul(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y,
               int64_t ld_y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decode GEMV straight from fp32 activations: each of the m <= 8 rows of x is
+ * quantized inside the GEMV kernel with exactly the arithmetic of
+ * q8_quantize_rows (bit-identical codes and scales), then multiplied as
+ * q8_matmul does; the output is bit-identical to q8_quantize_rows(...,
+ * Q8_LAYOUT_ACT, ...) followed by q8_matmul.  One launch instead of two
+ * ("ferro" README, "How the iGPU path is fast", item 3: producers emit the
+ * next GEMM's int8 input directly).  Each 64-row tile quantizes the
+ * activation groups it reads, so the codes are never written to memory.
+ *  x       device fp32, m x k, row stride ld_x (ld_x >= k, ld_x % 4 == 0),
+ *          16-byte aligned.
+ *  w, layout, n, k, y, ld_y: as for q8_matmul (1 <= m <= 8).
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_quantize_matmul(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
+                       float *y, int64_t ld_y, hipStream_t stream);
 
 /* Workspace bytes q8_grouped_matmul needs. */
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k);

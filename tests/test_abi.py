@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -50,9 +50,9 @@ def test_sizes():
     assert q8.q8_quantized_bytes(128256, 2048) == 128256 * 64 * 34
     assert q8.q8_quantized_bytes(3, 33) == 0
     assert q8.q8_quantized_bytes(-1, 32) == 0
-    # workspace: narrow matrices split by group, wide ones and the GEMM need none
-    assert q8.q8_matmul_workspace_bytes(1, 2048, 8192) == 32 * 1 * 2048 * 4
-    assert q8.q8_matmul_workspace_bytes(8, 2048, 2048) == 8 * 8 * 2048 * 4
+    # the GEMV and the GEMM need no workspace
+    assert q8.q8_matmul_workspace_bytes(1, 2048, 8192) == 0
+    assert q8.q8_matmul_workspace_bytes(8, 2048, 2048) == 0
     assert q8.q8_matmul_workspace_bytes(1, 128256, 2048) == 0
     assert q8.q8_matmul_workspace_bytes(188, 2048, 2048) == 0
     assert q8.q8_grouped_workspace_bytes(16, 8, 256, 2048, 7168) >= 4 * (16 + 2 * 256 + 1 + 128)
@@ -101,9 +101,26 @@ def test_matmul_validation():
     assert call(n=2000) == q8.Q8_ERR_SHAPE                          # packed needs n % 64
     assert call(m=16, layout=0) == q8.Q8_ERR_SHAPE                  # GEMM reads packed weights only
     assert call(w=B + 8) == q8.Q8_ERR_ALIGN
-    assert call(ws=None) == q8.Q8_ERR_WORKSPACE                     # 2048 x 2048 splits by group
-    assert call(wsb=100) == q8.Q8_ERR_WORKSPACE
-    assert call(ws=D + 4) == q8.Q8_ERR_ALIGN
+    assert call(y=C + 4) == q8.Q8_ERR_ALIGN
+
+
+def test_quantize_matmul_validation():
+    f = "q8_quantize_matmul"
+    ok = dict(x=A, ld=2048, m=1, w=B, layout=1, n=2048, k=2048, y=C, ldy=2048)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return _raw(f, a["x"], a["ld"], a["m"], a["w"], a["layout"], a["n"], a["k"], a["y"], a["ldy"], None)
+
+    assert call(x=None) == q8.Q8_ERR_ARG
+    assert call(ld=2000) == q8.Q8_ERR_ARG
+    assert call(ldy=100) == q8.Q8_ERR_ARG
+    assert call(layout=2) == q8.Q8_ERR_ARG
+    assert call(m=9) == q8.Q8_ERR_SHAPE                             # fused path is the decode GEMV only
+    assert call(k=2080, ld=2080) == q8.Q8_ERR_SHAPE
+    assert call(n=100) == q8.Q8_ERR_SHAPE
+    assert call(ld=2050) == q8.Q8_ERR_ALIGN
+    assert call(x=A + 4) == q8.Q8_ERR_ALIGN
 
 
 def test_grouped_validation():

@@ -94,6 +94,21 @@ def test_repeatable():
     assert bits_equal(a, b)
 
 
+@pytest.mark.parametrize("n,k", [(64, 256), (512, 2048), (640, 7168), (2048, 8192), (65536, 256)])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_fused_quantization_bit_identical(m, n, k):
+    """q8_quantize_matmul (quantization inside the GEMV) equals
+    q8_quantize_rows + q8_matmul bitwise, in both layouts, with a row stride."""
+    x, w = _case(m, n, k, seed=3 * n + m)
+    wr, wp = weights_packed(w)
+    xs = up(np.concatenate([x, np.zeros((m, 4), np.float32)], axis=1))
+    ref = _gemv(quantize(x, q8.Q8_LAYOUT_ACT), m, wp, 1, n, k)
+    for layout, wt in ((q8.Q8_LAYOUT_PACKED, wp), (q8.Q8_LAYOUT_ROWS, wr)):
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        q8.q8_quantize_matmul(xs, k + 4, m, wt, layout, n, k, y, n)
+        assert bits_equal(down(y), ref), f"layout {layout}"
+
+
 def test_ld_y_and_workspace_reuse():
     """Output row stride larger than n; a dirty, oversized workspace."""
     m, n, k = 3, 512, 2048
