@@ -131,6 +131,43 @@ def graph_time(run, stream, steps, warmup):
     return ms, g
 
 
+def per_launch_ms(run, count, stream, g_filler, reps):
+    """Average duration of each of the `count` timed launches of run(stream,
+    timers), measured with HIP events on `stream`.  Before each eager pass the
+    stream is kept busy with replays of the captured step, so that the host
+    has queued every event and launch of the pass before the GPU reaches them:
+    the events then bracket the kernels alone, not host launch latency."""
+    import torch
+    total = np.zeros(count)
+    for _ in range(reps):
+        timers = [Timer(stream) for _ in range(count)]
+        with torch.cuda.stream(stream):
+            for _ in range(8):
+                g_filler.replay()
+            run(stream, timers)
+        torch.cuda.synchronize()
+        total += np.array([t.ms() for t in timers])
+    return total / reps
+
+
+def sequence_ms(run, stream, g_filler, reps):
+    """Duration of one eager run(stream) measured by one event pair on
+    `stream`, queued behind replays of the captured step (see per_launch_ms)."""
+    import torch
+    total = 0.0
+    for _ in range(reps):
+        t = Timer(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(8):
+                g_filler.replay()
+            t.start()
+            run(stream)
+            t.stop()
+        torch.cuda.synchronize()
+        total += t.ms()
+    return total / reps
+
+
 def oracle_rows(w: np.ndarray, threads: int) -> np.ndarray:
     """Oracle quantization of a weight matrix into ROWS layout, split over row
     chunks on a thread pool (the C call releases the GIL)."""
@@ -195,6 +232,8 @@ class DecodeStep:
             self.inputs.append((xt, qb))
             self.host_x.append(x)
         self.y = [torch.empty((m, mt.n), dtype=torch.float32, device=dev) for mt in mats]
+        need = max(q8.q8_matmul_workspace_bytes(m, mt.n, mt.k) for mt in mats)
+        self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
         self.weight_bytes = sum(mt.n * (mt.k // 32) * 34 for mt in mats)
         torch.cuda.synchronize()
 
@@ -209,10 +248,10 @@ class DecodeStep:
                 gemv_timers[i].start()
             if self.fused:
                 q8.q8_quantize_matmul(xt, mt.k, self.m, self.w_packed[i], q8.Q8_LAYOUT_PACKED, mt.n, mt.k,
-                                      self.y[i], mt.n, s)
+                                      self.y[i], mt.n, self.ws, self.ws.numel(), s)
             else:
                 q8.q8_matmul(qb, self.m, self.w_packed[i], q8.Q8_LAYOUT_PACKED, mt.n, mt.k, self.y[i], mt.n,
-                             None, 0, s)
+                             self.ws, self.ws.numel(), s)
             if gemv_timers is not None:
                 gemv_timers[i].stop()
 
@@ -243,21 +282,20 @@ def bench_gemv_workload(args, mats, workload, m, label):
         step.run(stream)
     torch.cuda.synchronize()
     eager = [y.clone() for y in step.y]
-    ms_per_step, _ = graph_time(step.run, stream, args.steps, args.warmup)
+    ms_per_step, graph = graph_time(step.run, stream, args.steps, args.warmup)
     for i, y in enumerate(step.y):
         if not torch.equal(y.view(torch.int32), eager[i].view(torch.int32)):
             raise RuntimeError(f"graph replay output {i} differs from the eager step")
 
-    # the dominant kernel (the GEMV), each launch bracketed by events on its stream
-    timers = [Timer(stream) for _ in step.mats]
-    gemv_ms = np.zeros(len(step.mats))
-    reps = max(1, min(args.steps, 10))
-    for _ in range(reps):
-        with torch.cuda.stream(stream):
-            step.run(stream, timers)
-        torch.cuda.synchronize()
-        gemv_ms += np.array([tm.ms() for tm in timers])
-    gemv_ms /= reps
+    # per-matrix breakdown: each launch bracketed by its own events (an event
+    # pair also costs the launch latency the graph hides, so these overstate)
+    gemv_ms = per_launch_ms(step.run, len(step.mats), stream, g_filler=graph, reps=max(1, min(args.steps, 10)))
+    # the dominant kernel's average launch duration: in the fused step every
+    # launch is that kernel, so one event pair around the whole queued-ahead
+    # sequence, divided by the number of launches
+    seq_ms = None
+    if step.fused:
+        seq_ms = sequence_ms(step.run, stream, graph, reps=max(1, min(args.steps, 10))) / len(step.mats)
     gemv_bytes = np.array([step.gemv_bytes(i) for i in range(len(step.mats))], dtype=np.float64)
 
     value = step.weight_bytes / (ms_per_step * 1e-3) / 1e9
@@ -290,8 +328,12 @@ def bench_gemv_workload(args, mats, workload, m, label):
         "prep_seconds": round(prep_s, 1),
     }
     metric = ("Q8_0 matmul weight GB/s (%HBM peak) at M=1" if m == 1 else f"Q8_0 matmul weight GB/s at M={m}")
+    avg_ms = seq_ms if seq_ms is not None else float(gemv_ms.mean())
+    roof = hbm_roofline(kname, float(gemv_bytes.mean()), avg_ms)
+    roof["timing"] = ("one event pair around all launches of the step, queued ahead; per launch = total / launches"
+                      if seq_ms is not None else "one event pair per launch, queued ahead")
     return base_record(args, metric, value, "GB/s", ms_per_step, "int8xint8->int32, fp32 scale/sum", config,
-                       hbm_roofline(kname, float(gemv_bytes.mean()), float(gemv_ms.mean())), cpu)
+                       roof, cpu)
 
 
 def bench_decode(args):
@@ -342,16 +384,8 @@ def bench_prefill(args):
             if timers is not None:
                 timers[i].stop()
 
-    ms_per_step, _ = graph_time(run, stream, args.steps, args.warmup)
-    timers = [Timer(stream) for _ in cases]
-    ms = np.zeros(len(cases))
-    reps = max(1, min(args.steps, 10))
-    for _ in range(reps):
-        with torch.cuda.stream(stream):
-            run(stream, timers)
-        torch.cuda.synchronize()
-        ms += np.array([t.ms() for t in timers])
-    ms /= reps
+    ms_per_step, graph = graph_time(run, stream, args.steps, args.warmup)
+    ms = per_launch_ms(run, len(cases), stream, graph, reps=max(1, min(args.steps, 10)))
     ops = np.array([2.0 * c["m"] * c["n"] * c["k"] for c in cases])
     value = ops.sum() / (ms_per_step * 1e-3) / 1e12
     per_case = {f"M{c['m']}_N{c['n']}_K{c['k']}": round(ops[i] / (ms[i] * 1e-3) / 1e12, 1)
@@ -436,16 +470,8 @@ def bench_moe(args):
             if timers is not None:
                 timers[i].stop()
 
-    ms_per_step, _ = graph_time(run, stream, args.steps, args.warmup)
-    timers = [Timer(stream) for _ in mats]
-    ms = np.zeros(len(mats))
-    reps = max(1, min(args.steps, 10))
-    for _ in range(reps):
-        with torch.cuda.stream(stream):
-            run(stream, timers)
-        torch.cuda.synchronize()
-        ms += np.array([t.ms() for t in timers])
-    ms /= reps
+    ms_per_step, graph = graph_time(run, stream, args.steps, args.warmup)
+    ms = per_launch_ms(run, len(mats), stream, graph, reps=max(1, min(args.steps, 10)))
     U = len(used)
     wbytes = np.array([U * c["stride"] for c in mats], dtype=np.float64)
     abytes = np.array([wbytes[i] + c["rows"] * (c["k"] // 32) * 34 + 4 * T * K8 * c["n"] for i, c in enumerate(mats)])

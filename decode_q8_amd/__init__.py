@@ -33,4 +33,5 @@ from .q8 import (  # noqa: F401
     quantize,
     quantize_matmul,
     repack,
+    workspace,
 )

@@ -109,15 +109,20 @@ int q8_matmul(const void *x_q, int64_t m, const void *w, int layout, int64_t n, 
 }
 
 int q8_quantize_matmul(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
-                       float *y, int64_t ld_y, hipStream_t stream) {
+                       float *y, int64_t ld_y, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!x || !w || !y || m <= 0 || n <= 0 || k <= 0 || ld_x < k || ld_y < n) return Q8_ERR_ARG;
     if (layout != Q8_LAYOUT_ROWS && layout != Q8_LAYOUT_PACKED) return Q8_ERR_ARG;
     if (m > Q8_GEMV_MAX_ROWS || k % (Q8_BLOCK * Q8_TILE_BLOCKS)) return Q8_ERR_SHAPE;
     if (layout == Q8_LAYOUT_PACKED && n % Q8_TILE_ROWS) return Q8_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || ld_x % 4) return Q8_ERR_ALIGN;
+    const size_t need = q8_matmul_workspace_bytes(m, n, k);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return Q8_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return Q8_ERR_ALIGN;
+    }
     const int dev = check_device();
     if (dev != Q8_OK) return dev;
-    return launched(q8k::launch_gemv_f32(x, ld_x, m, w, layout, n, k, y, ld_y, stream));
+    return launched(q8k::launch_gemv_f32(x, ld_x, m, w, layout, n, k, y, ld_y, workspace, stream));
 }
 
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k) {

@@ -4,7 +4,8 @@
 // README, "How the iGPU path is fast", item 1): s = exact int32 sum of 32
 // int8 products (v_dot4c_i32_i8, 8 per block), t = fp32(s * (Dw * Dx)), and
 // the terms are summed in one fixed order that depends on k only: a tree over
-// the 8 blocks of each 256-value group, then the group sums left to right.
+// the 8 blocks of each 256-value group, the group sums left to right within
+// each 2048-value segment, then the segment sums left to right.
 //
 // Work split (gfx950 first, not the pages' N100/AVX-512 designs):
 //  - lane = output row: a wave owns a 64-row tile, so no cross-lane
@@ -15,10 +16,10 @@
 //    (64 rows x 16 values); a row's 8 scales arrive in one 16-byte load;
 //  - activations are wave-uniform: the compiler reads them with scalar loads
 //    into SGPRs, which feed v_dot4c directly (no LDS traffic);
-//  - one workgroup per tile; narrow matrices (fewer than 1024 tiles) give
-//    the tile to up to 8 waves that split its groups and chain the group sums
-//    in LDS in the same left-to-right order a single wave uses, so the bits
-//    do not depend on the split.
+//  - a workgroup of up to 8 waves shares a tile's groups and chains them in
+//    LDS; narrow matrices with long rows spread a tile over one workgroup per
+//    segment and hand the segment sums over through the workspace.  The
+//    order of additions is the same for every split, so the bits are too.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -155,9 +156,10 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float *
     }
 }
 
-// Walk groups [g0, g1) of one lane's row.  TO_LDS = false: chain the group
-// sums into acc (the wave owns the whole row).  TO_LDS = true: store each
-// group sum u_g at lds[(g * M + m) * 64 + lane] for a later in-order chain.
+// Walk groups [g0, g1) of one lane's row.  TO_LDS = true: store each group
+// sum u_g at lds[((g - g0) * M + m) * 64 + lane]; the workgroup chains them
+// later.  TO_LDS = false: the wave owns groups [0, G) of its row and chains in
+// registers in the canonical two-level order (used with g0 = 0).
 // wbase/gstride: address of group 0 of this lane and the step between groups.
 template <int M, int LAYOUT, bool TO_LDS, typename ACT>
 __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride, int64_t g0, int64_t g1,
@@ -165,6 +167,7 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
                                            float (&acc)[M], float *lds, int lane) {
     if (g0 >= g1) return;
     GroupRegs cur, nxt;
+    float seg[M];
     load_group<LAYOUT>(cur, wbase + g0 * gstride);
     for (int64_t g = g0; g < g1; g++) {
         if (g + 1 < g1) load_group<LAYOUT>(nxt, wbase + (g + 1) * gstride);
@@ -183,33 +186,62 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
         }
         if (TO_LDS) {
 #pragma unroll
-            for (int m = 0; m < M; m++) lds[(g * M + m) * TILE_ROWS + lane] = u[m];
+            for (int m = 0; m < M; m++) lds[((g - g0) * M + m) * TILE_ROWS + lane] = u[m];
         } else {
+            const bool seg_first = (g % SEG_GROUPS) == 0;
+            const bool seg_last = (g % SEG_GROUPS) == SEG_GROUPS - 1 || g == g1 - 1;
 #pragma unroll
-            for (int m = 0; m < M; m++) acc[m] = (g == g0) ? u[m] : acc[m] + u[m];
+            for (int m = 0; m < M; m++) {
+                seg[m] = seg_first ? u[m] : seg[m] + u[m];
+                if (seg_last) acc[m] = (g < SEG_GROUPS) ? seg[m] : acc[m] + seg[m];
+            }
         }
         cur = nxt;
     }
 }
 
-// One workgroup per 64-row tile; its W waves take contiguous, balanced ranges
-// of the k/256 groups.  With W = 1 the single wave chains in registers; with
-// W > 1 every group sum goes to LDS and, after a barrier, the workgroup chains
-// them left to right.  Either way each output is ((u_0 + u_1) + u_2) + ...
+// The GEMV.  A tile's groups are split into segments of 8 (2048 values); a
+// workgroup covers `segs` consecutive segments of one tile, its W waves take
+// balanced contiguous ranges of those groups and leave every group sum in
+// LDS.  After a barrier each (row, m) is chained in the canonical order:
+//   S_j = ((u_8j + u_8j+1) + ...) + u_8j+7   within segment j,
+//   y   = ((S_0 + S_1) + S_2) + ...          over the segments.
+// When one workgroup covers the whole tile it writes y.  Otherwise (narrow
+// matrices with long rows, where one workgroup per tile would leave most CUs
+// idle) each workgroup hands its segment sums to the workspace and counts in
+// at its tile's counter; the workgroup that arrives last chains all segment
+// sums and writes y, then clears the counter (so counters that start at zero
+// stay zero).  Cross-workgroup visibility without cache-wide fences: segment
+// sums are written and read back with read-modify-write atomics (exchange in;
+// exchange with 0 out -- an idempotent RMW would be lowered to a plain atomic
+// load, which can hit a stale line of a non-coherent L2), performed at the
+// device-coherent point like the counter; every thread waits for its
+// exchanges before the barrier that precedes the counter increment, and the
+// last workgroup reads only after that increment returned the final count.
+// Workspace: uint32 counters [tiles] (256-byte aligned), then fp32 segment sums
+// [S][M][n].
 template <int M, int LAYOUT, typename ACT>
 __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, int64_t ld_x,
                                                    const uint16_t *__restrict__ xs, const uint8_t *__restrict__ w,
-                                                   int64_t n, int64_t k, float *__restrict__ y, int64_t ld_y) {
-    extern __shared__ float lds_u[];  // [G][M][64] when W > 1
+                                                   int64_t n, int64_t k, float *__restrict__ y, int64_t ld_y,
+                                                   int wgs_per_tile, uint32_t *__restrict__ ctr,
+                                                   float *__restrict__ part) {
+    extern __shared__ float lds_u[];  // [groups of this workgroup][M][64]
+    __shared__ int last_wg;
     const int lane = threadIdx.x & 63;
     const int wv = wave_id();
     const int W = blockDim.x >> 6;
-    const int64_t T = blockIdx.x;
+    const int64_t T = blockIdx.x / wgs_per_tile;
+    const int wi = blockIdx.x - (int)T * wgs_per_tile;
     const int64_t G = k / GROUP_K;
-    const int64_t g0 = wv * G / W, g1 = (wv + 1) * G / W;
+    const int64_t S = (G + SEG_GROUPS - 1) / SEG_GROUPS;
+    const int64_t sp = (S + wgs_per_tile - 1) / wgs_per_tile;
+    const int64_t s0 = wi * sp, s1 = (s0 + sp) < S ? (s0 + sp) : S;
+    const int64_t ga = s0 * SEG_GROUPS, gb = (s1 * SEG_GROUPS) < G ? (s1 * SEG_GROUPS) : G;
+    const int64_t ng = gb - ga;
+    const int64_t g0 = ga + wv * ng / W, g1 = ga + (wv + 1) * ng / W;
     const int64_t row = T * TILE_ROWS + lane;
-    const bool row_ok = row < n;
-    const int64_t row_c = row_ok ? row : n - 1;
+    const int64_t row_c = row < n ? row : n - 1;
 
     const ACT *xrow[M];
     const uint16_t *srow[M];
@@ -218,60 +250,111 @@ __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, i
         xrow[m] = xq + m * ld_x;
         srow[m] = xs + m * (k / QK);
     }
-    const uint8_t *wbase;
-    int64_t gstride;
-    if (LAYOUT == 1) {
-        wbase = w + T * G * RECORD_BYTES + lane * 16;
-        gstride = RECORD_BYTES;
-    } else {
-        wbase = w + row_c * (k / QK) * BLOCK_BYTES;
-        gstride = ROW_GROUP_BYTES;
-    }
-    float acc[M];
-    if (W == 1) {
-        row_groups<M, LAYOUT, false>(wbase, gstride, 0, G, xrow, srow, acc, nullptr, lane);
-        if (row_ok) {
-#pragma unroll
-            for (int m = 0; m < M; m++) y[m * ld_y + row] = acc[m];
+    const uint8_t *wbase = LAYOUT == 1 ? w + T * G * RECORD_BYTES + lane * 16 : w + row_c * (k / QK) * BLOCK_BYTES;
+    const int64_t gstride = LAYOUT == 1 ? RECORD_BYTES : ROW_GROUP_BYTES;
+    float unused[M];
+    row_groups<M, LAYOUT, true>(wbase, gstride, g0, g1, xrow, srow, unused, lds_u + (g0 - ga) * M * TILE_ROWS,
+                                lane);
+    __syncthreads();
+
+    const int t = threadIdx.x;  // the plan gives at least M waves: one thread per (m, row)
+    const bool chain_thread = t < M * TILE_ROWS;
+    const int cm = t >> 6, cr = t & 63;
+    const int64_t out_row = T * TILE_ROWS + cr;
+    const bool out_ok = chain_thread && out_row < n;
+    float acc = 0.0f;
+    if (chain_thread) {
+        for (int64_t sj = s0; sj < s1; sj++) {
+            const int64_t gs = sj * SEG_GROUPS, ge = (gs + SEG_GROUPS) < G ? (gs + SEG_GROUPS) : G;
+            float sv = lds_u[((gs - ga) * M + cm) * TILE_ROWS + cr];
+            for (int64_t g = gs + 1; g < ge; g++) sv += lds_u[((g - ga) * M + cm) * TILE_ROWS + cr];
+            if (wgs_per_tile == 1) {
+                acc = sj == 0 ? sv : acc + sv;
+            } else if (out_ok) {
+                __hip_atomic_exchange((uint32_t *)&part[(sj * M + cm) * n + out_row], __builtin_bit_cast(uint32_t, sv),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
+    }
+    if (wgs_per_tile == 1) {
+        if (out_ok) y[cm * ld_y + out_row] = acc;
         return;
     }
-    row_groups<M, LAYOUT, true>(wbase, gstride, g0, g1, xrow, srow, acc, lds_u, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's exchanges have completed
     __syncthreads();
-    for (int t = threadIdx.x; t < M * TILE_ROWS; t += blockDim.x) {
-        const int m = t >> 6, r = t & 63;
-        float a = lds_u[m * TILE_ROWS + r];
-        for (int64_t g = 1; g < G; g++) a += lds_u[(g * M + m) * TILE_ROWS + r];
-        const int64_t out_row = T * TILE_ROWS + r;
-        if (out_row < n) y[m * ld_y + out_row] = a;
+    if (t == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&ctr[T], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_wg = old == (uint32_t)(wgs_per_tile - 1);
     }
+    __syncthreads();
+    if (!last_wg) return;
+    if (out_ok) {
+        for (int64_t b0 = 0; b0 < S; b0 += 8) {
+            float v[8];  // eight exchanges in flight, then the in-order chain
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                v[j] = b0 + j < S ? __builtin_bit_cast(float, __hip_atomic_exchange(
+                                                                  (uint32_t *)&part[((b0 + j) * M + cm) * n + out_row],
+                                                                  0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                  : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                if (b0 + j < S) acc = (b0 + j == 0) ? v[j] : acc + v[j];
+        }
+        y[cm * ld_y + out_row] = acc;
+    }
+    if (t == 0) __hip_atomic_exchange(&ctr[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int GEMV_MAX_WAVES = 8;
 constexpr int64_t GEMV_LDS_LIMIT = 64 * 1024;
 
-// Waves per tile: enough workgroups x waves to cover the machine (about 2048
-// waves), at most one wave per group, and the group sums must fit in LDS.
-// Only speed depends on this choice; the bits do not.
-int gemv_waves(int64_t m, int64_t n, int64_t k) {
-    const int64_t tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
-    const int64_t G = k / GROUP_K;
-    if (tiles >= 1024 || G == 1) return 1;
-    int64_t W = (2048 + tiles - 1) / tiles;
-    if (W > GEMV_MAX_WAVES) W = GEMV_MAX_WAVES;
-    if (W > G) W = G;
-    if (G * m * TILE_ROWS * (int64_t)sizeof(float) > GEMV_LDS_LIMIT) W = 1;
-    return (int)W;
+// Execution plan of a GEMV.  Only speed depends on it; every plan produces
+// the same bits.  Up to 8 waves per workgroup (one or more groups each);
+// tiles of narrow matrices are spread over one workgroup per segment so that
+// at least ~256 workgroups run; the group sums a workgroup keeps in LDS must
+// fit in 64 KB.
+GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k) {
+    GemvPlan p;
+    p.tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
+    p.groups = k / GROUP_K;
+    const int64_t S = (p.groups + SEG_GROUPS - 1) / SEG_GROUPS;
+    int64_t wgs = 1;
+    if (p.tiles < 256) wgs = (256 + p.tiles - 1) / p.tiles;
+    if (wgs > S) wgs = S;
+    for (;;) {  // LDS bound: groups per workgroup x m x 64 rows x 4 bytes
+        const int64_t sp = (S + wgs - 1) / wgs;
+        const int64_t gpw = sp * SEG_GROUPS < p.groups ? sp * SEG_GROUPS : p.groups;
+        if (gpw * m * TILE_ROWS * (int64_t)sizeof(float) <= GEMV_LDS_LIMIT || wgs >= S) break;
+        wgs++;
+    }
+    const int64_t sp = (S + wgs - 1) / wgs;
+    wgs = (S + sp - 1) / sp;  // no workgroup without a segment
+    const int64_t gpw = sp * SEG_GROUPS < p.groups ? sp * SEG_GROUPS : p.groups;
+    p.wgs_per_tile = (int)wgs;
+    // one chain thread per (row, activation row) after the barrier: at least m waves
+    int64_t waves = gpw < GEMV_MAX_WAVES ? gpw : GEMV_MAX_WAVES;
+    if (waves < m) waves = m;
+    p.waves = (int)waves;
+    p.lds = (size_t)(gpw * m * TILE_ROWS) * sizeof(float);
+    p.workspace = 0;
+    if (wgs > 1) p.workspace = (size_t)((p.tiles * 4 + 255) / 256 * 256) + (size_t)(S * m * n) * sizeof(float);
+    return p;
 }
 
-size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k) { return 0; }
+size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k) { return gemv_plan(m, n, k).workspace; }
 
 template <int LAYOUT, typename ACT>
-static void launch_gemv_m(int64_t m, dim3 grid, dim3 block, size_t lds, hipStream_t s, const ACT *x, int64_t ld_x,
-                          const uint16_t *xs, const uint8_t *w, int64_t n, int64_t k, float *y, int64_t ld_y) {
-#define Q8_GEMV_CASE(MM)                                                                                    \
-    case MM:                                                                                                \
-        hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT, ACT>), grid, block, lds, s, x, ld_x, xs, w, n, k, y, ld_y); \
+static void launch_gemv_m(int64_t m, const GemvPlan &p, hipStream_t s, const ACT *x, int64_t ld_x,
+                          const uint16_t *xs, const uint8_t *w, int64_t n, int64_t k, float *y, int64_t ld_y,
+                          void *ws) {
+    uint32_t *ctr = (uint32_t *)ws;
+    float *part = ws ? (float *)((uint8_t *)ws + (p.tiles * 4 + 255) / 256 * 256) : nullptr;
+    const dim3 grid((unsigned)(p.tiles * p.wgs_per_tile)), block((unsigned)(64 * p.waves));
+#define Q8_GEMV_CASE(MM)                                                                                         \
+    case MM:                                                                                                     \
+        hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT, ACT>), grid, block, p.lds, s, x, ld_x, xs, w, n, k, y, ld_y, \
+                           p.wgs_per_tile, ctr, part);                                                           \
         break;
     switch (m) {
         Q8_GEMV_CASE(1) Q8_GEMV_CASE(2) Q8_GEMV_CASE(3) Q8_GEMV_CASE(4)
@@ -283,29 +366,25 @@ static void launch_gemv_m(int64_t m, dim3 grid, dim3 block, size_t lds, hipStrea
 
 template <typename ACT>
 static hipError_t launch_gemv_any(const ACT *x, int64_t ld_x, const uint16_t *xs, int64_t m, const void *w,
-                                  int layout, int64_t n, int64_t k, float *y, int64_t ld_y, hipStream_t s) {
-    const int64_t tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
-    const int W = gemv_waves(m, n, k);
-    const size_t lds = W > 1 ? (size_t)((k / GROUP_K) * m * TILE_ROWS) * sizeof(float) : 0;
-    const dim3 grid((unsigned)tiles), block((unsigned)(64 * W));
+                                  int layout, int64_t n, int64_t k, float *y, int64_t ld_y, void *ws, hipStream_t s) {
+    const GemvPlan p = gemv_plan(m, n, k);
     if (layout == 1)
-        launch_gemv_m<1, ACT>(m, grid, block, lds, s, x, ld_x, xs, (const uint8_t *)w, n, k, y, ld_y);
+        launch_gemv_m<1, ACT>(m, p, s, x, ld_x, xs, (const uint8_t *)w, n, k, y, ld_y, ws);
     else
-        launch_gemv_m<0, ACT>(m, grid, block, lds, s, x, ld_x, xs, (const uint8_t *)w, n, k, y, ld_y);
+        launch_gemv_m<0, ACT>(m, p, s, x, ld_x, xs, (const uint8_t *)w, n, k, y, ld_y, ws);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y,
                        int64_t ld_y, void *workspace, hipStream_t s) {
-    (void)workspace;
     const int8_t *xq = (const int8_t *)x_q;
     const uint16_t *xs = (const uint16_t *)((const uint8_t *)x_q + m * k);
-    return launch_gemv_any<int8_t>(xq, k, xs, m, w, layout, n, k, y, ld_y, s);
+    return launch_gemv_any<int8_t>(xq, k, xs, m, w, layout, n, k, y, ld_y, workspace, s);
 }
 
 hipError_t launch_gemv_f32(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
-                           float *y, int64_t ld_y, hipStream_t s) {
-    return launch_gemv_any<float>(x, ld_x, nullptr, m, w, layout, n, k, y, ld_y, s);
+                           float *y, int64_t ld_y, void *workspace, hipStream_t s) {
+    return launch_gemv_any<float>(x, ld_x, nullptr, m, w, layout, n, k, y, ld_y, workspace, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -13,8 +13,16 @@ hipError_t launch_quantize(const float *x, int64_t ld_x, int64_t rows, int64_t k
 
 hipError_t launch_repack(const void *w_rows, int64_t n, int64_t k, void *w_packed, hipStream_t s);
 
-// Waves per 64-row tile of a GEMV (only speed depends on it).
-int gemv_waves(int64_t m, int64_t n, int64_t k);
+// Execution plan of a GEMV (only speed depends on it, never the bits).
+struct GemvPlan {
+    int64_t tiles;     // 64-row tiles
+    int64_t groups;    // 256-value groups along k
+    int wgs_per_tile;  // workgroups sharing one tile (one or more segments each)
+    int waves;         // waves per workgroup
+    size_t lds;        // dynamic LDS bytes per workgroup
+    size_t workspace;  // bytes: tile counters + segment sums when wgs_per_tile > 1
+};
+GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k);
 size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 hipError_t launch_gemv(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y,
@@ -22,7 +30,7 @@ hipError_t launch_gemv(const void *x_q, int64_t m, const void *w, int layout, in
 
 // GEMV from fp32 activations, quantized inside the kernel (m <= 8).
 hipError_t launch_gemv_f32(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
-                           float *y, int64_t ld_y, hipStream_t s);
+                           float *y, int64_t ld_y, void *workspace, hipStream_t s);
 
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s);

@@ -32,7 +32,7 @@ SIGNATURES = {
     "q8_repack_weights": ([_P, _I64, _I64, _P, _P], _I),
     "q8_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q8_matmul": ([_P, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
-    "q8_quantize_matmul": ([_P, _I64, _I64, _P, _I, _I64, _I64, _P, _I64, _P], _I),
+    "q8_quantize_matmul": ([_P, _I64, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
     "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
     "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
 }
@@ -125,9 +125,10 @@ def q8_matmul(x_q, m: int, w, layout: int, n: int, k: int, y, ld_y: int, workspa
                                   workspace_bytes, _stream(stream)), "q8_matmul")
 
 
-def q8_quantize_matmul(x, ld_x: int, m: int, w, layout: int, n: int, k: int, y, ld_y: int, stream=None) -> int:
-    return _check(lib().q8_quantize_matmul(_ptr(x), ld_x, m, _ptr(w), layout, n, k, _ptr(y), ld_y, _stream(stream)),
-                  "q8_quantize_matmul")
+def q8_quantize_matmul(x, ld_x: int, m: int, w, layout: int, n: int, k: int, y, ld_y: int, workspace=None,
+                       workspace_bytes: int = 0, stream=None) -> int:
+    return _check(lib().q8_quantize_matmul(_ptr(x), ld_x, m, _ptr(w), layout, n, k, _ptr(y), ld_y, _ptr(workspace),
+                                           workspace_bytes, _stream(stream)), "q8_quantize_matmul")
 
 
 def q8_grouped_matmul(x_q, x_rows: int, x_per_pair: int, topk_ids, tokens: int, topk: int, w_experts,
@@ -157,22 +158,31 @@ def repack(w_rows, n: int, k: int, stream=None):
     return out
 
 
-def quantize_matmul(x, w, layout: int, n: int, stream=None):
+def workspace(m: int, n: int, k: int, device="cuda"):
+    """A zero-filled workspace for q8_matmul / q8_quantize_matmul (None when
+    the shape needs none)."""
+    import torch
+    need = q8_matmul_workspace_bytes(m, n, k)
+    return torch.zeros(need, dtype=torch.uint8, device=device) if need else None
+
+
+def quantize_matmul(x, w, layout: int, n: int, ws=None, stream=None):
     """fp32 [m][k] CUDA tensor (m <= 8) -> new fp32 [m][n] tensor."""
     import torch
     assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
     m, k = x.shape
     y = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    q8_quantize_matmul(x, x.stride(0), m, w, layout, n, k, y, n, stream)
+    if ws is None:
+        ws = workspace(m, n, k, x.device)
+    q8_quantize_matmul(x, x.stride(0), m, w, layout, n, k, y, n, ws, 0 if ws is None else ws.numel(), stream)
     return y
 
 
-def matmul(x_q, m: int, w, layout: int, n: int, k: int, workspace=None, stream=None):
-    """-> new fp32 [m][n] tensor; allocates a workspace if none is given."""
+def matmul(x_q, m: int, w, layout: int, n: int, k: int, ws=None, stream=None):
+    """-> new fp32 [m][n] tensor; allocates a zeroed workspace if none is given."""
     import torch
     y = torch.empty((m, n), dtype=torch.float32, device=w.device)
-    need = q8_matmul_workspace_bytes(m, n, k)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
-    q8_matmul(x_q, m, w, layout, n, k, y, n, workspace, need if workspace is not None else 0, stream)
+    if ws is None:
+        ws = workspace(m, n, k, w.device)
+    q8_matmul(x_q, m, w, layout, n, k, y, n, ws, 0 if ws is None else ws.numel(), stream)
     return y

@@ -12,9 +12,10 @@
  *  - Block dot: s = exact int32 sum of the 32 products, term
  *    t = fp32(s * (Dw * Dx)) (Dw * Dx is exact in fp32, so one rounding).
  *  - Output: the terms of a row summed in fp32 in one fixed order that
- *    depends on k only: groups of 8 consecutive blocks are summed as the tree
- *    ((t0+t1)+(t2+t3))+((t4+t5)+(t6+t7)), then the group sums are added left
- *    to right starting from the first group.  Every entry point that produces
+ *    depends on k only: groups of 8 consecutive blocks (256 values) are summed
+ *    as the tree ((t0+t1)+(t2+t3))+((t4+t5)+(t6+t7)); the group sums of each
+ *    segment of 8 consecutive groups (2048 values) are added left to right;
+ *    the segment sums are added left to right.  Every entry point that produces
  *    GEMV outputs (m <= 8, and every routed pair) uses exactly this order, so
  *    a row's output is bit-identical alone, in any batch of up to 8 rows, in
  *    any row order, in either weight layout, for any n, and in the routed
@@ -120,8 +121,15 @@ int q8_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int 
  *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_repack_weights(const void *w_rows, int64_t n, int64_t k, void *w_packed, hipStream_t stream);
 
-/* Workspace bytes q8_matmul needs for this shape (0 when none).  Depends on
- * (m, n, k) only; every shape currently needs none (pass NULL, 0). */
+/* Workspace bytes q8_matmul / q8_quantize_matmul need for this shape (0 when
+ * none).  Depends on (m, n, k) only.  Narrow matrices (fewer than 1024 row
+ * tiles of 64) spread each tile's k over independent waves; they need a
+ * workspace holding one uint32 counter per tile (first 256-byte-aligned part)
+ * and the per-group partial sums.  The counters must be zero before the first
+ * call that uses a workspace (allocate it zero-filled); every completed call
+ * leaves them zero again, so one workspace serves any sequence of calls on one
+ * stream, including replays of a captured graph.  Calls that run concurrently
+ * need separate workspaces. */
 size_t q8_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* y[i][j] = sum over blocks of x_q row i against weight row j (the Q8_0
@@ -131,8 +139,8 @@ size_t q8_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *          Q8_LAYOUT_ROWS (any n; only for m <= 8).
  *  y       device fp32, m x n with row stride ld_y >= n (elements).
  *  workspace, workspace_bytes: device scratch of at least
- *          q8_matmul_workspace_bytes(m, n, k) (may be NULL when that is 0);
- *          contents on entry do not matter; must not overlap y.
+ *          q8_matmul_workspace_bytes(m, n, k) (may be NULL when that is 0),
+ *          counters zero as described above; must not overlap y.
  *  Routing is by m alone: m <= 8 runs the GEMV, m > 8 the MFMA GEMM.
  *  k % 256 == 0.
  *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
@@ -150,10 +158,11 @@ int q8_matmul(const void *x_q, int64_t m, const void *w, int layout, int64_t n, 
  * activation groups it reads, so the codes are never written to memory.
  *  x       device fp32, m x k, row stride ld_x (ld_x >= k, ld_x % 4 == 0),
  *          16-byte aligned.
- *  w, layout, n, k, y, ld_y: as for q8_matmul (1 <= m <= 8).
- *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+ *  w, layout, n, k, y, ld_y, workspace: as for q8_matmul (1 <= m <= 8).
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
+ *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_quantize_matmul(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
-                       float *y, int64_t ld_y, hipStream_t stream);
+                       float *y, int64_t ld_y, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes q8_grouped_matmul needs. */
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k);

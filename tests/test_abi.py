@@ -50,10 +50,13 @@ def test_sizes():
     assert q8.q8_quantized_bytes(128256, 2048) == 128256 * 64 * 34
     assert q8.q8_quantized_bytes(3, 33) == 0
     assert q8.q8_quantized_bytes(-1, 32) == 0
-    # the GEMV and the GEMM need no workspace
-    assert q8.q8_matmul_workspace_bytes(1, 2048, 8192) == 0
-    assert q8.q8_matmul_workspace_bytes(8, 2048, 2048) == 0
-    assert q8.q8_matmul_workspace_bytes(1, 128256, 2048) == 0
+    # narrow GEMVs with long rows spread a tile over one workgroup per
+    # 2048-value segment: tile counters (256-byte aligned) + segment sums
+    assert q8.q8_matmul_workspace_bytes(1, 2048, 8192) == 256 + 4 * 1 * 2048 * 4
+    assert q8.q8_matmul_workspace_bytes(8, 2048, 7168) == 256 + 4 * 8 * 2048 * 4
+    assert q8.q8_matmul_workspace_bytes(8, 2048, 2048) == 0          # one segment: no hand-off
+    assert q8.q8_matmul_workspace_bytes(1, 64000, 256) == 0          # a single group: no split
+    assert q8.q8_matmul_workspace_bytes(1, 128256, 2048) == 0        # wide: whole rows per wave
     assert q8.q8_matmul_workspace_bytes(188, 2048, 2048) == 0
     assert q8.q8_grouped_workspace_bytes(16, 8, 256, 2048, 7168) >= 4 * (16 + 2 * 256 + 1 + 128)
 
@@ -102,15 +105,19 @@ def test_matmul_validation():
     assert call(m=16, layout=0) == q8.Q8_ERR_SHAPE                  # GEMM reads packed weights only
     assert call(w=B + 8) == q8.Q8_ERR_ALIGN
     assert call(y=C + 4) == q8.Q8_ERR_ALIGN
+    assert call(k=8192, ws=None) == q8.Q8_ERR_WORKSPACE             # 2048 x 8192 splits by segment
+    assert call(k=8192, wsb=100) == q8.Q8_ERR_WORKSPACE
+    assert call(k=8192, ws=D + 4) == q8.Q8_ERR_ALIGN
 
 
 def test_quantize_matmul_validation():
     f = "q8_quantize_matmul"
-    ok = dict(x=A, ld=2048, m=1, w=B, layout=1, n=2048, k=2048, y=C, ldy=2048)
+    ok = dict(x=A, ld=2048, m=1, w=B, layout=1, n=2048, k=2048, y=C, ldy=2048, ws=D, wsb=1 << 30)
 
     def call(**kw):
         a = {**ok, **kw}
-        return _raw(f, a["x"], a["ld"], a["m"], a["w"], a["layout"], a["n"], a["k"], a["y"], a["ldy"], None)
+        return _raw(f, a["x"], a["ld"], a["m"], a["w"], a["layout"], a["n"], a["k"], a["y"], a["ldy"], a["ws"],
+                    a["wsb"], None)
 
     assert call(x=None) == q8.Q8_ERR_ARG
     assert call(ld=2000) == q8.Q8_ERR_ARG
@@ -121,6 +128,7 @@ def test_quantize_matmul_validation():
     assert call(n=100) == q8.Q8_ERR_SHAPE
     assert call(ld=2050) == q8.Q8_ERR_ALIGN
     assert call(x=A + 4) == q8.Q8_ERR_ALIGN
+    assert call(k=8192, ld=8192, ws=None) == q8.Q8_ERR_WORKSPACE
 
 
 def test_grouped_validation():

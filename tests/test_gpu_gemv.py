@@ -47,9 +47,8 @@ def test_parity_packed_and_rows(m, n, k):
     assert bits_equal(yp, yr), "packed and row-contiguous layouts differ"
 
 
-@pytest.mark.parametrize("n", [1, 50, 100, 1000])
-def test_rows_layout_ragged_n(n):
-    k = 512
+@pytest.mark.parametrize("n,k", [(1, 512), (50, 512), (100, 512), (1000, 512), (100, 4096), (1, 7168)])
+def test_rows_layout_ragged_n(n, k):
     x, w = _case(3, n, k, seed=n)
     xq = quantize(x, q8.Q8_LAYOUT_ACT)
     wr = quantize(w, q8.Q8_LAYOUT_ROWS)
@@ -85,6 +84,25 @@ def test_fused_matrix_rows_equal_parts():
     assert bits_equal(yf[:, 512:], _gemv(xq, 2, p2, 1, 65536, k))
 
 
+def test_long_rows_wide_matrix_m8():
+    """m = 8 with k = 8448 (33 groups, 5 segments) on a wide matrix: the group
+    sums of a whole tile exceed 64 KB of LDS, so tiles are spread over two
+    workgroups even though n / 64 >= 256."""
+    m, n, k = 8, 16384, 8448
+    assert q8.q8_matmul_workspace_bytes(m, n, k) > 0
+    x, w = _case(m, n, k, seed=21)
+    wr, wp = weights_packed(w)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    y = _gemv(xq, m, wp, 1, n, k)
+    rng = np.random.default_rng(21)
+    mi, ni = rng.integers(0, m, 2048), rng.integers(0, n, 2048)
+    y_ref, S = oracle.matmul_points(down(xq), m, down(wr), n, k, mi, ni)
+    check_tol(y[mi, ni], y_ref, S, "m=8 k=8448")
+    for i in (0, 5):
+        yi = _gemv(quantize(x[i:i + 1], q8.Q8_LAYOUT_ACT), 1, wp, 1, n, k)
+        assert bits_equal(y[i:i + 1], yi)
+
+
 def test_repeatable():
     x, w = _case(4, 2048, 8192, seed=13)
     xq = quantize(x, q8.Q8_LAYOUT_ACT)
@@ -105,22 +123,30 @@ def test_fused_quantization_bit_identical(m, n, k):
     ref = _gemv(quantize(x, q8.Q8_LAYOUT_ACT), m, wp, 1, n, k)
     for layout, wt in ((q8.Q8_LAYOUT_PACKED, wp), (q8.Q8_LAYOUT_ROWS, wr)):
         y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-        q8.q8_quantize_matmul(xs, k + 4, m, wt, layout, n, k, y, n)
+        ws = q8.workspace(m, n, k)
+        q8.q8_quantize_matmul(xs, k + 4, m, wt, layout, n, k, y, n, ws, 0 if ws is None else ws.numel())
         assert bits_equal(down(y), ref), f"layout {layout}"
 
 
 def test_ld_y_and_workspace_reuse():
-    """Output row stride larger than n; a dirty, oversized workspace."""
-    m, n, k = 3, 512, 2048
-    x, w = _case(m, n, k, seed=14)
-    xq = quantize(x, q8.Q8_LAYOUT_ACT)
-    _, wp = weights_packed(w)
-    y = torch.full((m, n + 64), 7.0, dtype=torch.float32, device="cuda")
-    ws = torch.full((q8.q8_matmul_workspace_bytes(m, n, k) + 4096,), 255, dtype=torch.uint8, device="cuda")
-    q8.q8_matmul(xq, m, wp, 1, n, k, y, n + 64, ws, ws.numel())
-    got = down(y)
-    assert np.all(got[:, n:] == 7.0)
-    assert bits_equal(got[:, :n], _gemv(xq, m, wp, 1, n, k))
+    """Output row stride larger than n; one zeroed workspace reused by calls of
+    different shapes and m leaves its tile counters at zero and gives the same
+    bits as fresh workspaces."""
+    k = 8192
+    need = max(q8.q8_matmul_workspace_bytes(m, n, k) for m in (1, 3, 8) for n in (512, 2048))
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for m, n in ((3, 512), (1, 2048), (8, 512), (3, 2048)):
+        x, w = _case(m, n, k, seed=14 + m + n)
+        xq = quantize(x, q8.Q8_LAYOUT_ACT)
+        _, wp = weights_packed(w)
+        y = torch.full((m, n + 64), 7.0, dtype=torch.float32, device="cuda")
+        q8.q8_matmul(xq, m, wp, 1, n, k, y, n + 64, ws, ws.numel())
+        got = down(y)
+        assert np.all(got[:, n:] == 7.0)
+        assert bits_equal(got[:, :n], _gemv(xq, m, wp, 1, n, k))
+        tiles = (n + 63) // 64
+        assert not down(ws[: tiles * 4]).any(), "tile counters not left at zero"
 
 
 def test_single_gemv_full_size():
