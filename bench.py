@@ -150,6 +150,25 @@ def per_launch_ms(run, count, stream, g_filler, reps):
     return total / reps
 
 
+def profiled_traffic(profile: str, source: str):
+    """HBM bytes per launch recorded in profiles/<profile> by the rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, if that summary was taken from the current
+    kernel source (its sha256 matches); otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def sequence_ms(run, stream, g_filler, reps):
     """Duration of one eager run(stream) measured by one event pair on
     `stream`, queued behind replays of the captured step (see per_launch_ms)."""
@@ -332,6 +351,8 @@ def bench_gemv_workload(args, mats, workload, m, label):
     roof = hbm_roofline(kname, float(gemv_bytes.mean()), avg_ms)
     roof["timing"] = ("one event pair around all launches of the step, queued ahead; per launch = total / launches"
                       if seq_ms is not None else "one event pair per launch, queued ahead")
+    if step.fused and m == 1 and len(mats) == 65:
+        roof["traffic"] = profiled_traffic("gemv_decode_step_llama1b.txt", "decode_q8_amd/csrc/gemv.hip")
     return base_record(args, metric, value, "GB/s", ms_per_step, "int8xint8->int32, fp32 scale/sum", config,
                        roof, cpu)
 
