@@ -20,8 +20,8 @@ def _gemm(xq, m, wp, n, k):
     return down(q8.matmul(xq, m, wp, q8.Q8_LAYOUT_PACKED, n, k))
 
 
-@pytest.mark.parametrize("m,n,k", [(9, 64, 256), (32, 128, 256), (40, 192, 512), (130, 256, 2048),
-                                   (188, 320, 1024), (257, 128, 7168)])
+@pytest.mark.parametrize("m,n,k", [(9, 64, 256), (32, 128, 256), (40, 192, 512), (24, 64, 768), (130, 256, 2048),
+                                   (136, 128, 1280), (188, 320, 1024), (257, 128, 7168)])
 def test_parity(m, n, k):
     x = wl.activation(wl.PREFILL, 50 + m, m, k, outliers=True)
     w = wl.weight(wl.PREFILL, 50 + n, n, k)
