@@ -5,6 +5,8 @@ Every source is compiled for gfx950 only, with:
                         every fma they use, so results never depend on the
                         compiler's contraction choices;
   -packed-fp32-ops off  no v_pk_{add,mul,fma}_f32 (scalar fp32 VALU only);
+  mfma-vgpr-form        MFMA results land in ordinary VGPRs, which the epilogue
+                        reads directly (no accumulator-register copies);
   default HIP division  fp32 '/' is correctly rounded (the quantizer relies on
                         it); no -ffast-math, no denormal flushing.
 """
@@ -28,7 +30,8 @@ HOST_SOURCES = ["api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def hipcc() -> str:

@@ -15,9 +15,10 @@
 // any row order.  Two VALU operations per output and block remain; with
 // packed fp32 unavailable they, not the MFMA, bound this kernel.
 //
-// Tiling: a 512-thread workgroup owns a 128 x 128 output tile (two packed
-// 64-row weight tiles); each of its 8 waves a 32 x 64 strip (1 x 2 MFMA
-// tiles).  The k loop runs in stages of 4 blocks (128 values).  Stages move
+// Tiling: each wave owns a 32 x 64 output strip (1 x 2 MFMA tiles); a
+// workgroup of WM x WN waves owns a (32 WM) x (64 WN) tile: 128 x 128 (8
+// waves) for large problems, 64 x 64 (2 waves) when 128 x 128 tiles would
+// leave CUs idle.  The k loop runs in stages of 4 blocks (128 values).  Stages move
 // from HBM straight into LDS with global_load_lds_dwordx4 / _dword (no
 // register staging), NS = 4 stages deep, so three stages are in flight while
 // one is computed.  Every wave issues exactly LOADS_PER_STAGE such loads per
@@ -26,32 +27,46 @@
 // is the same for both operands (lane half h holds values 16h..16h+15 of the
 // block), which is all an exact integer dot needs.
 //
-// LDS stage layout (35 KB, NS = 4 stages = 140 KB of gfx950's 160 KB):
-//   A   16 KB  activation rows: row r's 16-byte chunk c at r*128 + (c ^ (r & 7))*16
-//              (the XOR swizzle keeps the MFMA operand reads bank-conflict free)
-//   B   16 KB  the two weight tiles' 4 block records, as packed (8 KB each)
-//   SX   1 KB  activation scales [row][4 blocks]
-//   SW   1 KB  weight scales [tile][row][4 blocks]
-//   Z    1 KB  zeros, read by the lanes that carry no scale in the rank-1 MFMA
+// LDS stage layout (128 x 128: 35 KB, NS = 4 stages = 140 KB of gfx950's
+// 160 KB; 64 x 64: 18 KB, 72 KB for four stages):
+//   A   activation rows: row r's 16-byte chunk c at r*128 + (c ^ (r & 7))*16
+//       (the XOR swizzle keeps the MFMA operand reads bank-conflict free)
+//   B   the weight tiles' 4 block records, as packed (8 KB per tile)
+//   SX  activation scales [row][4 blocks]
+//   SW  weight scales [tile][row][4 blocks]
+//   Z   1 KB of zeros, read by the lanes that carry no scale in the rank-1 MFMA
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace q8k {
 
-constexpr int GT_M = 128;
-constexpr int GT_N = 128;
-constexpr int SB = 4;                        // blocks per stage
-constexpr int NS = 4;                        // stages resident in LDS
-constexpr int A_BYTES = GT_M * SB * QK;      // 16384
-constexpr int B_TILE = SB * 2048;            // 8192: one weight tile's 4 block records
-constexpr int B_BYTES = 2 * B_TILE;          // 16384
-constexpr int S_BYTES = GT_M * SB * 2;       // 1024
-constexpr int SX_OFF = A_BYTES + B_BYTES;
-constexpr int SW_OFF = SX_OFF + S_BYTES;
-constexpr int Z_OFF = SW_OFF + S_BYTES;
-constexpr int STAGE_BYTES = Z_OFF + S_BYTES;  // 35840
-constexpr int THREADS = 512;
-constexpr int LOADS_PER_STAGE = 5;  // per wave: 2 activation, 2 weight, 1 scale
+constexpr int SB = 4;   // blocks per stage
+constexpr int NS = 4;   // stages resident in LDS
+constexpr int Z_BYTES = 1024;
+
+// Workgroup shape: WM x WN waves, each a 32 x 64 output strip (1 x 2 MFMA
+// tiles), so the workgroup tile is (32 WM) x (64 WN).
+template <int WM, int WN>
+struct Tile {
+    static constexpr int WAVES = WM * WN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int ROWS = 32 * WM;                  // output rows per workgroup
+    static constexpr int COLS = 64 * WN;                  // output columns (packed tiles x 64)
+    static constexpr int A_BYTES = ROWS * SB * QK;         // activation rows, 128 bytes each
+    static constexpr int B_BYTES = WN * SB * 2048;         // WN weight tiles' 4 block records
+    static constexpr int SX_BYTES = ROWS * SB * 2;
+    static constexpr int SW_BYTES = COLS * SB * 2;
+    static constexpr int SX_OFF = A_BYTES + B_BYTES;
+    static constexpr int SW_OFF = SX_OFF + SX_BYTES;
+    static constexpr int Z_OFF = SW_OFF + SW_BYTES;
+    static constexpr int STAGE_BYTES = Z_OFF + Z_BYTES;
+    // direct-to-LDS loads per stage: 1 KB activation / weight loads, 256-byte scale loads
+    static constexpr int NA = A_BYTES / 1024, NB = B_BYTES / 1024, NSX = SX_BYTES / 256, NSW = SW_BYTES / 256;
+    static constexpr int LOADS = NA + NB + NSX + NSW;
+    static constexpr int PER_WAVE = (LOADS + WAVES - 1) / WAVES;  // a wave short of work repeats its last load
+    static_assert(SX_BYTES <= Z_BYTES && SW_BYTES <= Z_BYTES, "zero region must cover every scale offset");
+    static_assert(PER_WAVE * (NS - 2) <= 63, "vmcnt threshold out of range");
+};
 
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -66,63 +81,63 @@ __device__ __forceinline__ v4h rank1_operand(const uint8_t *p) {
     return __builtin_bit_cast(v4h, v);
 }
 
-// Issue this wave's LOADS_PER_STAGE direct-to-LDS loads of stage s (blocks
-// 4s..4s+3).  Each load writes 64 lanes x size bytes contiguously from the
-// wave-uniform LDS address; the lane decides which global bytes it fetches.
+// Issue this wave's PER_WAVE direct-to-LDS loads of stage s (blocks 4s..4s+3).
+// Each load writes 64 lanes x size bytes contiguously from the wave-uniform
+// LDS address; the lane decides which global bytes it fetches.  Load i of the
+// stage goes to wave i % WAVES.
+template <int WM, int WN>
 __device__ __forceinline__ void issue_stage(uint8_t *buf, const int8_t *xq, const uint16_t *xs, int64_t M,
-                                            int64_t m_tile, const uint8_t *w0, const uint8_t *w1, int64_t K,
+                                            int64_t m_tile, const uint8_t *w_tiles, int64_t tile_stride, int64_t K,
                                             int64_t nb, int64_t s, int wave, int lane) {
+    using T = Tile<WM, WN>;
     const int64_t blk0 = s * SB;
-    const int64_t grp = s >> 1;
     const int bb0 = (int)(s & 1) * SB;
-    const uint8_t *rec0 = w0 + grp * RECORD_BYTES;
-    const uint8_t *rec1 = w1 + grp * RECORD_BYTES;
-    // activations: 16 loads of 8 rows x 128 bytes, waves w and w + 8
+    const uint8_t *recs = w_tiles + (s >> 1) * RECORD_BYTES;  // group s/2 of the workgroup's first tile
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-        const int i = wave + 8 * u;
-        const int r = 8 * i + (lane >> 3);
-        const int c = (lane & 7) ^ (lane >> 3);  // (r & 7) == lane >> 3
-        int64_t row = m_tile + r;
-        row = row < M ? row : M - 1;
-        __builtin_amdgcn_global_load_lds(xq + row * K + blk0 * QK + c * 16, (lds_ptr)(buf + i * 1024), 16, 0, 0);
+    for (int u = 0; u < T::PER_WAVE; u++) {
+        int i = wave + T::WAVES * u;
+        i = i < T::LOADS ? i : T::LOADS - 1;
+        if (i < T::NA) {  // activations: 8 rows x 128 bytes, row r's chunk c at position c ^ (r & 7)
+            const int r = 8 * i + (lane >> 3);
+            const int c = (lane & 7) ^ (lane >> 3);
+            int64_t row = m_tile + r;
+            row = row < M ? row : M - 1;
+            __builtin_amdgcn_global_load_lds(xq + row * K + blk0 * QK + c * 16, (lds_ptr)(buf + i * 1024), 16, 0, 0);
+        } else if (i < T::NA + T::NB) {  // weights: a tile's 4 block records are 8 KB contiguous
+            const int q = i - T::NA;
+            const uint8_t *rec = recs + (q >> 3) * tile_stride;
+            __builtin_amdgcn_global_load_lds(rec + bb0 * 2048 + (q & 7) * 1024 + lane * 16,
+                                             (lds_ptr)(buf + T::A_BYTES + q * 1024), 16, 0, 0);
+        } else if (i < T::NA + T::NB + T::NSX) {  // activation scales [row][4], 4 bytes per lane
+            const int d = (i - T::NA - T::NB) * 64 + lane;
+            int64_t row = m_tile + (d >> 1);
+            row = row < M ? row : M - 1;
+            __builtin_amdgcn_global_load_lds(xs + row * nb + blk0 + 2 * (d & 1),
+                                             (lds_ptr)(buf + T::SX_OFF + (i - T::NA - T::NB) * 256), 4, 0, 0);
+        } else {  // weight scales [tile][row][4], 4 bytes per lane
+            const int e = i - T::NA - T::NB - T::NSX;
+            const int d = e * 64 + lane;
+            const uint8_t *rec = recs + (d >> 7) * tile_stride;
+            __builtin_amdgcn_global_load_lds(rec + RECORD_Q_BYTES + ((d >> 1) & 63) * 16 + bb0 * 2 + (d & 1) * 4,
+                                             (lds_ptr)(buf + T::SW_OFF + e * 256), 4, 0, 0);
+        }
     }
-    // weights: each tile's 4 block records are 8 KB contiguous; 8 loads per tile
-#pragma unroll
-    for (int u = 0; u < 2; u++) {
-        const int q = wave + 8 * u;
-        const uint8_t *rec = q < 8 ? rec0 : rec1;
-        __builtin_amdgcn_global_load_lds(rec + bb0 * 2048 + (q & 7) * 1024 + lane * 16,
-                                         (lds_ptr)(buf + A_BYTES + q * 1024), 16, 0, 0);
-    }
-    // scales, 4 bytes (two blocks) per lane: waves 0..3 activation rows, 4..7 weight rows
-    const int d = (wave & 3) * 64 + lane;
-    const int pair = d & 1;
-    const void *src;
-    if (wave < 4) {
-        int64_t row = m_tile + (d >> 1);
-        row = row < M ? row : M - 1;
-        src = xs + row * nb + blk0 + 2 * pair;
-    } else {
-        const uint8_t *rec = d < 128 ? rec0 : rec1;
-        src = rec + RECORD_Q_BYTES + ((d >> 1) & 63) * 16 + bb0 * 2 + pair * 4;
-    }
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + SX_OFF + wave * 256), 4, 0, 0);
 }
 
 // Wait until this wave's loads of the stage about to be computed have landed
 // (pending = how many later stages it has issued since), then barrier, so
 // every wave's loads have landed and every wave is done with the stage
 // before it.
+template <int L>
 __device__ __forceinline__ void stage_barrier(int pending) {
+    static_assert(NS == 4, "thresholds below assume at most two later stages in flight");
     if (pending >= 2)
-        asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * L) : "memory");
     else if (pending == 1)
-        asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(L) : "memory");
     else
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-static_assert(NS == 4 && LOADS_PER_STAGE == 5, "stage_barrier's vmcnt thresholds assume 4 stages of 5 loads");
 
 struct Lane {
     int a_off[SB];  // activation chunk offsets of this lane's row, per block
@@ -130,50 +145,85 @@ struct Lane {
     int sx_off, sw_off;
 };
 
+struct Args {
+    const int8_t *xq;
+    const uint16_t *xs;
+    int64_t M, m_tile;
+    const uint8_t *w_tiles;  // the workgroup's first packed tile
+    int64_t tile_stride;     // bytes between consecutive packed tiles (0: a single tile, reloaded)
+    int64_t K, nb, S;
+};
+
+// Read block bb's operands from the stage buffer and issue its MFMAs: the
+// exact int32 block dots (one i8 MFMA per 32 x 32 tile) and the rank-1 scale
+// products Dx * Dw in the same register layout.
+template <typename T>
+__device__ __forceinline__ void mfma_block(v16i (&sv)[2], v16f (&sp)[2], const uint8_t *buf, const Lane &ln, int bb) {
+    const v4i av = *reinterpret_cast<const v4i *>(buf + ln.a_off[bb]);
+    const v4h as = rank1_operand(buf + ln.sx_off + bb * 2);
+    v4i b[2];
+    v4h bs[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        b[j] = *reinterpret_cast<const v4i *>(buf + T::A_BYTES + ln.b_off + bb * 2048 + j * 512);
+        bs[j] = rank1_operand(buf + ln.sw_off + j * 256 + bb * 2);
+    }
+    const v16i zi = {0};
+    const v16f zf = {0};
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        sv[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b[j], zi, 0, 0, 0);
+        sp[j] = __builtin_amdgcn_mfma_f32_32x32x8f16(as, bs[j], zf, 0, 0, 0);
+    }
+}
+
 // One 256-value group = stages 2g and 2g + 1, resident in buffers 2P and 2P + 1.
-template <int P>
-__device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const Lane &ln, const int8_t *xq,
-                                      const uint16_t *xs, int64_t M, int64_t m_tile, const uint8_t *w0,
-                                      const uint8_t *w1, int64_t K, int64_t nb, int64_t g, int64_t S, int wave,
-                                      int lane) {
+template <int WM, int WN, int P>
+__device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const Lane &ln, const Args &a, int64_t g,
+                                      int wave, int lane) {
+    using T = Tile<WM, WN>;
     float ga[2][16];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
         const int64_t s = 2 * g + h;
-        const int64_t last = s + NS - 2 < S - 1 ? s + NS - 2 : S - 1;  // latest stage issued so far
-        stage_barrier((int)(last - s));
-        if (s + NS - 1 < S)
-            issue_stage(lds + ((2 * P + h + NS - 1) % NS) * STAGE_BYTES, xq, xs, M, m_tile, w0, w1, K, nb,
-                        s + NS - 1, wave, lane);
-        const uint8_t *buf = lds + (2 * P + h) * STAGE_BYTES;
+        const int64_t last = s + NS - 2 < a.S - 1 ? s + NS - 2 : a.S - 1;  // latest stage issued so far
+        stage_barrier<T::PER_WAVE>((int)(last - s));
+        if (s + NS - 1 < a.S)
+            issue_stage<WM, WN>(lds + ((2 * P + h + NS - 1) % NS) * T::STAGE_BYTES, a.xq, a.xs, a.M, a.m_tile,
+                                a.w_tiles, a.tile_stride, a.K, a.nb, s + NS - 1, wave, lane);
+        const uint8_t *buf = lds + (2 * P + h) * T::STAGE_BYTES;
+        // Software pipeline over the stage's blocks: the MFMAs of block bb + 1
+        // are issued before the VALU epilogue of block bb, so the matrix core
+        // works while the VALU converts and accumulates the previous result.
+        v16i sv[2][2];
+        v16f sp[2][2];
+        mfma_block<T>(sv[0], sp[0], buf, ln, 0);
 #pragma unroll
         for (int bb = 0; bb < SB; bb++) {
-            const v4i a = *reinterpret_cast<const v4i *>(buf + ln.a_off[bb]);
-            const v4h as = rank1_operand(buf + ln.sx_off + bb * 2);
-            v4i b[2];
-            v4h bs[2];
+            if (bb + 1 < SB) mfma_block<T>(sv[(bb + 1) & 1], sp[(bb + 1) & 1], buf, ln, bb + 1);
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                b[j] = *reinterpret_cast<const v4i *>(buf + A_BYTES + ln.b_off + bb * 2048 + j * 512);
-                bs[j] = rank1_operand(buf + ln.sw_off + j * 256 + bb * 2);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const v16i zi = {0};
-                const v16f zf = {0};
-                const v16i sv = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j], zi, 0, 0, 0);
-                const v16f sp = __builtin_amdgcn_mfma_f32_32x32x8f16(as, bs[j], zf, 0, 0, 0);
+            for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int r = 0; r < 16; r++)
-                    ga[j][r] = (h == 0 && bb == 0) ? (float)sv[r] * sp[r]
-                                                   : __builtin_fmaf((float)sv[r], sp[r], ga[j][r]);
-            }
+                    ga[j][r] = (h == 0 && bb == 0)
+                                   ? (float)sv[bb & 1][j][r] * sp[bb & 1][j][r]
+                                   : __builtin_fmaf((float)sv[bb & 1][j][r], sp[bb & 1][j][r], ga[j][r]);
             // pin the block's results here, so the epilogue is not sunk past the
             // next stage's barrier with every MFMA result of the stage live
 #pragma unroll
             for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) asm volatile("" : "+v"(ga[j][r]));
+            // interleave: operand reads, then each MFMA followed by a slice of the
+            // epilogue, so the VALU runs while the matrix core is busy
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
@@ -182,39 +232,56 @@ __device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const L
         for (int r = 0; r < 16; r++) acc[j][r] += ga[j][r];
 }
 
-__global__ __launch_bounds__(512) void gemm_kernel(const int8_t *__restrict__ xq, const uint16_t *__restrict__ xs,
-                                                      int64_t M, const uint8_t *__restrict__ w, int64_t N, int64_t K,
-                                                      float *__restrict__ y, int64_t ld_y) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE_BYTES];  // 140 KB of gfx950's 160 KB
+template <int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__restrict__ xq,
+                                                             const uint16_t *__restrict__ xs, int64_t M,
+                                                             const uint8_t *__restrict__ w, int64_t N, int64_t K,
+                                                             float *__restrict__ y, int64_t ld_y) {
+    using T = Tile<WM, WN>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * T::STAGE_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = wave_id();
-    const int wm = wave & 3, wn = wave >> 2;  // 32-row strip wm of packed tile wn
+    const int wm = wave % WM, wn = wave / WM;  // 32-row strip wm of packed tile wn
     const int half = lane >> 5, l32 = lane & 31;
-    const int64_t m_tile = (int64_t)blockIdx.y * GT_M;
-    const int64_t T0 = (int64_t)blockIdx.x * 2;  // packed weight tiles T0 and T0 + 1
     const int64_t tiles = N / TILE_ROWS;
-    const bool has1 = T0 + 1 < tiles;
+    const int64_t T0 = (int64_t)blockIdx.x * WN;  // the workgroup's first packed weight tile
     const int64_t G = K / GROUP_K;
-    const int64_t S = 2 * G;  // stages
-    const int64_t nb = K / QK;
-    const uint8_t *w0 = w + (T0 * G) * RECORD_BYTES;
-    const uint8_t *w1 = has1 ? w + ((T0 + 1) * G) * RECORD_BYTES : w0;  // tile 2 absent: reload tile 1
+    Args a;
+    a.xq = xq;
+    a.xs = xs;
+    a.M = M;
+    a.m_tile = (int64_t)blockIdx.y * T::ROWS;
+    a.w_tiles = w + (T0 * G) * RECORD_BYTES;
+    // tiles past the last one (N not a multiple of the workgroup's columns) reload the last tile
+    a.tile_stride = T0 + WN <= tiles ? G * RECORD_BYTES : 0;
+    a.K = K;
+    a.nb = K / QK;
+    a.S = 2 * G;
+    const bool ragged = T0 + WN > tiles;
 
-    if (tid < NS * S_BYTES / 16) {  // every buffer's zero region, written once
-        const int b = tid / (S_BYTES / 16), c = tid % (S_BYTES / 16);
-        *reinterpret_cast<uint4 *>(lds + b * STAGE_BYTES + Z_OFF + c * 16) = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < NS * Z_BYTES / 16) {  // every buffer's zero region, written once
+        const int b = tid / (Z_BYTES / 16), c = tid % (Z_BYTES / 16);
+        *reinterpret_cast<uint4 *>(lds + b * T::STAGE_BYTES + T::Z_OFF + c * 16) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (NS * Z_BYTES / 16 > T::THREADS) {
+        for (int t = tid + T::THREADS; t < NS * Z_BYTES / 16; t += T::THREADS) {
+            const int b = t / (Z_BYTES / 16), c = t % (Z_BYTES / 16);
+            *reinterpret_cast<uint4 *>(lds + b * T::STAGE_BYTES + T::Z_OFF + c * 16) = make_uint4(0u, 0u, 0u, 0u);
+        }
     }
     __syncthreads();
     for (int s = 0; s < NS - 1; s++)
-        if (s < S) issue_stage(lds + s * STAGE_BYTES, xq, xs, M, m_tile, w0, w1, K, nb, s, wave, lane);
+        if (s < a.S)
+            issue_stage<WM, WN>(lds + s * T::STAGE_BYTES, xq, xs, M, a.m_tile, a.w_tiles, a.tile_stride, K, a.nb, s,
+                                wave, lane);
 
     Lane ln;
     const int row = wm * 32 + l32;
 #pragma unroll
     for (int bb = 0; bb < SB; bb++) ln.a_off[bb] = row * 128 + (((2 * bb + half) ^ (row & 7)) * 16);
-    ln.b_off = wn * B_TILE + half * 1024 + l32 * 16;
-    ln.sx_off = (half == 0 ? SX_OFF : Z_OFF) + row * 8;
-    ln.sw_off = (half == 0 ? SW_OFF : Z_OFF) + (wn * 64 + l32) * 8;
+    ln.b_off = wn * SB * 2048 + half * 1024 + l32 * 16;
+    ln.sx_off = (half == 0 ? T::SX_OFF : T::Z_OFF) + row * 8;
+    ln.sw_off = (half == 0 ? T::SW_OFF : T::Z_OFF) + (wn * 64 + l32) * 8;
 
     float acc[2][16];
 #pragma unroll
@@ -222,28 +289,46 @@ __global__ __launch_bounds__(512) void gemm_kernel(const int8_t *__restrict__ xq
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[j][r] = -0.0f;  // -0 + x == x for every x
     for (int64_t g = 0; g < G; g += 2) {
-        group<0>(acc, lds, ln, xq, xs, M, m_tile, w0, w1, K, nb, g, S, wave, lane);
-        if (g + 1 < G) group<1>(acc, lds, ln, xq, xs, M, m_tile, w0, w1, K, nb, g + 1, S, wave, lane);
+        group<WM, WN, 0>(acc, lds, ln, a, g, wave, lane);
+        if (g + 1 < G) group<WM, WN, 1>(acc, lds, ln, a, g + 1, wave, lane);
     }
-    if (wn == 1 && !has1) return;
+    if (ragged && T0 + wn >= tiles) return;
     const int64_t n_wave = (T0 + wn) * TILE_ROWS;
     // lane holds column l32 of each 32 x 32 tile and rows 8q + 4*half + p
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-        const int64_t orow = m_tile + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int64_t orow = a.m_tile + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (orow >= M) continue;
 #pragma unroll
         for (int j = 0; j < 2; j++) y[orow * ld_y + n_wave + j * 32 + l32] = acc[j][r];
     }
 }
 
+template <int WM, int WN>
+static hipError_t launch_tiles(const int8_t *xq, const uint16_t *xs, int64_t m, const uint8_t *w, int64_t n,
+                               int64_t k, float *y, int64_t ld_y, hipStream_t s) {
+    using T = Tile<WM, WN>;
+    const dim3 grid((unsigned)((n + T::COLS - 1) / T::COLS), (unsigned)((m + T::ROWS - 1) / T::ROWS));
+    hipLaunchKernelGGL((gemm_kernel<WM, WN>), grid, dim3(T::THREADS), 0, s, xq, xs, m, w, n, k, y, ld_y);
+    return hipGetLastError();
+}
+
+// Workgroup shape by problem size: 128 x 128 tiles while they give every CU a
+// workgroup, else 64 x 64 tiles (two waves; two workgroups fit a CU's LDS).
+// Each output's arithmetic is the same in both shapes, so rows stay
+// bit-identical across m.
+int gemm_variant(int64_t m, int64_t n) {
+    const int64_t big = ((m + 127) / 128) * ((n + 127) / 128);
+    return big >= 256 ? 0 : 1;
+}
+
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s) {
     const int8_t *xq = (const int8_t *)x_q;
     const uint16_t *xs = (const uint16_t *)((const uint8_t *)x_q + m * k);
-    const dim3 grid((unsigned)((n + GT_N - 1) / GT_N), (unsigned)((m + GT_M - 1) / GT_M));
-    hipLaunchKernelGGL(gemm_kernel, grid, dim3(THREADS), 0, s, xq, xs, m, (const uint8_t *)w, n, k, y, ld_y);
-    return hipGetLastError();
+    const uint8_t *wb = (const uint8_t *)w;
+    if (gemm_variant(m, n) == 0) return launch_tiles<4, 2>(xq, xs, m, wb, n, k, y, ld_y, s);
+    return launch_tiles<2, 1>(xq, xs, m, wb, n, k, y, ld_y, s);
 }
 
 }  // namespace q8k

@@ -45,6 +45,17 @@ def test_row_invariance_across_m_and_order():
     assert bits_equal(yp, y188[perm])
 
 
+def test_row_invariance_across_tile_shapes():
+    """m = 1024 on n = 4096 runs 128 x 128 workgroups, m = 100 the 64 x 64
+    ones: the rows they share are still bit-identical."""
+    n, k = 4096, 512
+    x = wl.activation(wl.PREFILL, 61, 1024, k, outliers=True)
+    _, wp = weights_packed(wl.weight(wl.PREFILL, 61, n, k))
+    y_big = _gemm(quantize(x, q8.Q8_LAYOUT_ACT), 1024, wp, n, k)
+    y_small = _gemm(quantize(x[900:1000], q8.Q8_LAYOUT_ACT), 100, wp, n, k)
+    assert bits_equal(y_small, y_big[900:1000])
+
+
 @pytest.mark.parametrize("m", wl.PREFILL_M)
 @pytest.mark.parametrize("n,k", wl.PREFILL_NK)
 def test_prefill_full_size_sampled(m, n, k):
