@@ -5,9 +5,9 @@
 // quantized per 32-block).  One v_mfma_i32_32x32x32_i8 covers exactly one
 // block for a 32 x 32 output tile, so its int32 results are the exact block
 // dots s.  The per-block scale product Dx[m] * Dw[n] of the same tile comes
-// from a rank-1 v_mfma_f32_32x32x8_f16 (one non-zero k: fp16 x fp16 is exact
-// in fp32), so it lands in the same register layout as s and the VALU only
-// converts s and fuses it in:
+// from a rank-1 f16 MFMA (one non-zero k: fp16 x fp16 is exact in fp32), so
+// it lands in the same register layout as s and the VALU only converts s and
+// fuses it in:
 //   group accumulator  a = fma(float(s), Dx * Dw, a)  over the 8 blocks of a
 //                          256-value group (the first block multiplies),
 //   output             y = ((a_0 + a_1) + a_2) + ...   over the groups.
@@ -27,14 +27,13 @@
 // is the same for both operands (lane half h holds values 16h..16h+15 of the
 // block), which is all an exact integer dot needs.
 //
-// LDS stage layout (128 x 128: 35 KB, NS = 4 stages = 140 KB of gfx950's
-// 160 KB; 64 x 64: 18 KB, 72 KB for four stages):
+// LDS stage layout (128 x 128: 34 KB, NS = 4 stages = 136 KB of gfx950's
+// 160 KB; 64 x 64: 17 KB, 68 KB for four stages):
 //   A   activation rows: row r's 16-byte chunk c at r*128 + (c ^ (r & 7))*16
 //       (the XOR swizzle keeps the MFMA operand reads bank-conflict free)
 //   B   the weight tiles' 4 block records, as packed (8 KB per tile)
 //   SX  activation scales [row][4 blocks]
 //   SW  weight scales [tile][row][4 blocks]
-//   Z   1 KB of zeros, read by the lanes that carry no scale in the rank-1 MFMA
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -42,7 +41,6 @@ namespace q8k {
 
 constexpr int SB = 4;   // blocks per stage
 constexpr int NS = 4;   // stages resident in LDS
-constexpr int Z_BYTES = 1024;
 
 // Workgroup shape: WM x WN waves, each a 32 x 64 output strip (1 x 2 MFMA
 // tiles), so the workgroup tile is (32 WM) x (64 WN).
@@ -58,24 +56,25 @@ struct Tile {
     static constexpr int SW_BYTES = COLS * SB * 2;
     static constexpr int SX_OFF = A_BYTES + B_BYTES;
     static constexpr int SW_OFF = SX_OFF + SX_BYTES;
-    static constexpr int Z_OFF = SW_OFF + SW_BYTES;
-    static constexpr int STAGE_BYTES = Z_OFF + Z_BYTES;
+    static constexpr int STAGE_BYTES = SW_OFF + SW_BYTES;
     // direct-to-LDS loads per stage: 1 KB activation / weight loads, 256-byte scale loads
     static constexpr int NA = A_BYTES / 1024, NB = B_BYTES / 1024, NSX = SX_BYTES / 256, NSW = SW_BYTES / 256;
     static constexpr int LOADS = NA + NB + NSX + NSW;
     static constexpr int PER_WAVE = (LOADS + WAVES - 1) / WAVES;  // a wave short of work repeats its last load
-    static_assert(SX_BYTES <= Z_BYTES && SW_BYTES <= Z_BYTES, "zero region must cover every scale offset");
     static_assert(PER_WAVE * (NS - 2) <= 63, "vmcnt threshold out of range");
 };
 
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
-// Operand of the rank-1 scale MFMA: lanes 0..31 carry their fp16 scale in
-// k = 0, every other element is zero.  Lanes 32..63 read their "scale" from
-// the zero region, so the operand is built without a select.
+// Operand of the rank-1 scale MFMA: the lane's fp16 scale in k = 0, zeros in
+// k = 1..3.  One v_mfma_f32_32x32x4_2b_f16 then yields the scale products
+// Dx * Dw of both 32 x 32 tiles of a wave (block 0 of the instruction: lanes
+// 0..31, tile 0; block 1: lanes 32..63, tile 1), each in the register layout of
+// the i8 MFMA's output.
 __device__ __forceinline__ v4h rank1_operand(const uint8_t *p) {
     const v2u v = {(uint32_t)*reinterpret_cast<const uint16_t *>(p), 0u};
     return __builtin_bit_cast(v4h, v);
@@ -161,20 +160,17 @@ template <typename T>
 __device__ __forceinline__ void mfma_block(v16i (&sv)[2], v16f (&sp)[2], const uint8_t *buf, const Lane &ln, int bb) {
     const v4i av = *reinterpret_cast<const v4i *>(buf + ln.a_off[bb]);
     const v4h as = rank1_operand(buf + ln.sx_off + bb * 2);
+    const v4h bs = rank1_operand(buf + ln.sw_off + bb * 2);
     v4i b[2];
-    v4h bs[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        b[j] = *reinterpret_cast<const v4i *>(buf + T::A_BYTES + ln.b_off + bb * 2048 + j * 512);
-        bs[j] = rank1_operand(buf + ln.sw_off + j * 256 + bb * 2);
-    }
+    for (int j = 0; j < 2; j++) b[j] = *reinterpret_cast<const v4i *>(buf + T::A_BYTES + ln.b_off + bb * 2048 + j * 512);
     const v16i zi = {0};
-    const v16f zf = {0};
+    const v32f zf = {0};
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        sv[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b[j], zi, 0, 0, 0);
-        sp[j] = __builtin_amdgcn_mfma_f32_32x32x8f16(as, bs[j], zf, 0, 0, 0);
-    }
+    for (int j = 0; j < 2; j++) sv[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b[j], zi, 0, 0, 0);
+    const v32f pp = __builtin_amdgcn_mfma_f32_32x32x4f16(as, bs, zf, 0, 0, 0);
+    sp[0] = __builtin_shufflevector(pp, pp, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    sp[1] = __builtin_shufflevector(pp, pp, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31);
 }
 
 // One 256-value group = stages 2g and 2g + 1, resident in buffers 2P and 2P + 1.
@@ -216,12 +212,12 @@ __device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const L
                 for (int r = 0; r < 16; r++) asm volatile("" : "+v"(ga[j][r]));
             // interleave: operand reads, then each MFMA followed by a slice of the
             // epilogue, so the VALU runs while the matrix core is busy
-            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < 3; i++) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);  // VALU
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -259,17 +255,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     a.S = 2 * G;
     const bool ragged = T0 + WN > tiles;
 
-    if (tid < NS * Z_BYTES / 16) {  // every buffer's zero region, written once
-        const int b = tid / (Z_BYTES / 16), c = tid % (Z_BYTES / 16);
-        *reinterpret_cast<uint4 *>(lds + b * T::STAGE_BYTES + T::Z_OFF + c * 16) = make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (NS * Z_BYTES / 16 > T::THREADS) {
-        for (int t = tid + T::THREADS; t < NS * Z_BYTES / 16; t += T::THREADS) {
-            const int b = t / (Z_BYTES / 16), c = t % (Z_BYTES / 16);
-            *reinterpret_cast<uint4 *>(lds + b * T::STAGE_BYTES + T::Z_OFF + c * 16) = make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-    __syncthreads();
     for (int s = 0; s < NS - 1; s++)
         if (s < a.S)
             issue_stage<WM, WN>(lds + s * T::STAGE_BYTES, xq, xs, M, a.m_tile, a.w_tiles, a.tile_stride, K, a.nb, s,
@@ -280,8 +265,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
 #pragma unroll
     for (int bb = 0; bb < SB; bb++) ln.a_off[bb] = row * 128 + (((2 * bb + half) ^ (row & 7)) * 16);
     ln.b_off = wn * SB * 2048 + half * 1024 + l32 * 16;
-    ln.sx_off = (half == 0 ? T::SX_OFF : T::Z_OFF) + row * 8;
-    ln.sw_off = (half == 0 ? T::SW_OFF : T::Z_OFF) + (wn * 64 + l32) * 8;
+    ln.sx_off = T::SX_OFF + row * 8;
+    ln.sw_off = T::SW_OFF + (wn * 64 + half * 32 + l32) * 8;
 
     float acc[2][16];
 #pragma unroll
