@@ -436,7 +436,8 @@ def bench_prefill(args):
         "hip_graph": True,
     }
     roof = {"kernel": "q8k::gemm_kernel", "bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
-            "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+            "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+            "traffic": profiled_traffic("gemm_prefill.txt", "decode_q8_amd/csrc/gemm.hip"),
             "avg_launch_us": round(float(ms.mean()) * 1e3, 3), "algorithmic_ops_per_launch": int(ops.mean())}
     return base_record(args, "Q8_0 prefill GEMM int8 TOPS (%MFMA peak)", value, "TOPS", ms_per_step,
                        "int8xint8->int32 (MFMA), fp32 scale/sum", config, roof, cpu)
@@ -525,6 +526,7 @@ def bench_moe(args):
         "hip_graph": True,
     }
     roof = hbm_roofline("q8k::grouped_gemv_kernel", float(abytes.mean()), float(ms.mean()))
+    roof["traffic"] = profiled_traffic("grouped_gemv_moe.txt", "decode_q8_amd/csrc/gemv.hip")
     roof["note"] = "launch time includes the expert-grouping kernel that precedes the GEMV in each call"
     return base_record(args, "Q8_0 routed-expert GEMV weight GB/s (%HBM peak)", value, "GB/s", ms_per_step,
                        "int8xint8->int32, fp32 scale/sum", config, roof, cpu)
