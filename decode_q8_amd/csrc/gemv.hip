@@ -156,21 +156,23 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float *
     }
 }
 
-// Walk groups [g0, g1) of one lane's row.  TO_LDS = true: store each group
-// sum u_g at lds[((g - g0) * M + m) * 64 + lane]; the workgroup chains them
-// later.  TO_LDS = false: the wave owns groups [0, G) of its row and chains in
-// registers in the canonical two-level order (used with g0 = 0).
-// wbase/gstride: address of group 0 of this lane and the step between groups.
+// Walk groups g0, g0 + step, ... (< g1) of one lane's row.  TO_LDS = true:
+// store each group sum u_g at lds[((g - g0) * M + m) * 64 + lane] (the caller
+// points lds at group g0's slot; slots of M x 64 floats hold consecutive
+// groups); the workgroup chains them later.  TO_LDS = false (step 1, g0 = 0): the wave owns
+// groups [0, G) of its row and chains in registers in the canonical two-level
+// order.  wbase/gstride: address of group 0 of this lane and the step between
+// groups in memory.
 template <int M, int LAYOUT, bool TO_LDS, typename ACT>
-__device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride, int64_t g0, int64_t g1,
+__device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride, int g0, int g1, int step,
                                            const ACT *const (&xrow)[M], const uint16_t *const (&srow)[M],
                                            float (&acc)[M], float *lds, int lane) {
     if (g0 >= g1) return;
     GroupRegs cur, nxt;
     float seg[M];
     load_group<LAYOUT>(cur, wbase + g0 * gstride);
-    for (int64_t g = g0; g < g1; g++) {
-        if (g + 1 < g1) load_group<LAYOUT>(nxt, wbase + (g + 1) * gstride);
+    for (int g = g0; g < g1; g += step) {
+        if (g + step < g1) load_group<LAYOUT>(nxt, wbase + (g + step) * gstride);
         if (LAYOUT == 0) rows_to_packed(cur);
         const ACT *xg[M];
 #pragma unroll
@@ -201,9 +203,9 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
 }
 
 // The GEMV.  A tile's groups are split into segments of 8 (2048 values); a
-// workgroup covers `segs` consecutive segments of one tile, its W waves take
-// balanced contiguous ranges of those groups and leave every group sum in
-// LDS.  After a barrier each (row, m) is chained in the canonical order:
+// workgroup covers segs_per_wg consecutive segments of one tile, its W waves
+// take those groups round-robin (wave w: groups w, w + W, ...) and leave every
+// group sum in LDS.  After a barrier each (row, m) is chained in the canonical order:
 //   S_j = ((u_8j + u_8j+1) + ...) + u_8j+7   within segment j,
 //   y   = ((S_0 + S_1) + S_2) + ...          over the segments.
 // When one workgroup covers the whole tile it writes y.  Otherwise (narrow
@@ -224,22 +226,23 @@ template <int M, int LAYOUT, typename ACT>
 __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, int64_t ld_x,
                                                    const uint16_t *__restrict__ xs, const uint8_t *__restrict__ w,
                                                    int64_t n, int64_t k, float *__restrict__ y, int64_t ld_y,
-                                                   int wgs_per_tile, uint32_t *__restrict__ ctr,
+                                                   int segs_per_wg, uint32_t *__restrict__ ctr,
                                                    float *__restrict__ part) {
     extern __shared__ float lds_u[];  // [groups of this workgroup][M][64]
     __shared__ int last_wg;
+    // Grid: x = workgroup within the tile, y = tile.  Everything below is
+    // 32-bit and division-free, so the first weight load issues after a few
+    // scalar instructions (64-bit divisions here cost hundreds).
     const int lane = threadIdx.x & 63;
     const int wv = wave_id();
     const int W = blockDim.x >> 6;
-    const int64_t T = blockIdx.x / wgs_per_tile;
-    const int wi = blockIdx.x - (int)T * wgs_per_tile;
-    const int64_t G = k / GROUP_K;
-    const int64_t S = (G + SEG_GROUPS - 1) / SEG_GROUPS;
-    const int64_t sp = (S + wgs_per_tile - 1) / wgs_per_tile;
-    const int64_t s0 = wi * sp, s1 = (s0 + sp) < S ? (s0 + sp) : S;
-    const int64_t ga = s0 * SEG_GROUPS, gb = (s1 * SEG_GROUPS) < G ? (s1 * SEG_GROUPS) : G;
-    const int64_t ng = gb - ga;
-    const int64_t g0 = ga + wv * ng / W, g1 = ga + (wv + 1) * ng / W;
+    const int wgs_per_tile = gridDim.x;
+    const int wi = blockIdx.x;
+    const int64_t T = blockIdx.y;
+    const int G = (int)(k >> 8);                        // k is a multiple of 256
+    const int S = (G + SEG_GROUPS - 1) / SEG_GROUPS;    // constant divisor: a shift
+    const int s0 = wi * segs_per_wg, s1 = min(s0 + segs_per_wg, S);
+    const int ga = s0 * SEG_GROUPS, gb = min(s1 * SEG_GROUPS, G);
     const int64_t row = T * TILE_ROWS + lane;
     const int64_t row_c = row < n ? row : n - 1;
 
@@ -253,7 +256,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, i
     const uint8_t *wbase = LAYOUT == 1 ? w + T * G * RECORD_BYTES + lane * 16 : w + row_c * (k / QK) * BLOCK_BYTES;
     const int64_t gstride = LAYOUT == 1 ? RECORD_BYTES : ROW_GROUP_BYTES;
     float unused[M];
-    row_groups<M, LAYOUT, true>(wbase, gstride, g0, g1, xrow, srow, unused, lds_u + (g0 - ga) * M * TILE_ROWS,
+    // wave wv takes the workgroup's groups ga + wv, ga + wv + W, ...; each sum lands in its group's LDS slot
+    row_groups<M, LAYOUT, true>(wbase, gstride, ga + wv, gb, W, xrow, srow, unused, lds_u + wv * M * TILE_ROWS,
                                 lane);
     __syncthreads();
 
@@ -332,6 +336,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k) {
     wgs = (S + sp - 1) / sp;  // no workgroup without a segment
     const int64_t gpw = sp * SEG_GROUPS < p.groups ? sp * SEG_GROUPS : p.groups;
     p.wgs_per_tile = (int)wgs;
+    p.segs_per_wg = (int)sp;
     // one chain thread per (row, activation row) after the barrier: at least m waves
     int64_t waves = gpw < GEMV_MAX_WAVES ? gpw : GEMV_MAX_WAVES;
     if (waves < m) waves = m;
@@ -350,11 +355,11 @@ static void launch_gemv_m(int64_t m, const GemvPlan &p, hipStream_t s, const ACT
                           void *ws) {
     uint32_t *ctr = (uint32_t *)ws;
     float *part = ws ? (float *)((uint8_t *)ws + (p.tiles * 4 + 255) / 256 * 256) : nullptr;
-    const dim3 grid((unsigned)(p.tiles * p.wgs_per_tile)), block((unsigned)(64 * p.waves));
+    const dim3 grid((unsigned)p.wgs_per_tile, (unsigned)p.tiles), block((unsigned)(64 * p.waves));
 #define Q8_GEMV_CASE(MM)                                                                                         \
     case MM:                                                                                                     \
         hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT, ACT>), grid, block, p.lds, s, x, ld_x, xs, w, n, k, y, ld_y, \
-                           p.wgs_per_tile, ctr, part);                                                           \
+                           p.segs_per_wg, ctr, part);                                                            \
         break;
     switch (m) {
         Q8_GEMV_CASE(1) Q8_GEMV_CASE(2) Q8_GEMV_CASE(3) Q8_GEMV_CASE(4)
@@ -483,7 +488,7 @@ __device__ __forceinline__ void expert_pass(const int8_t *xq, const uint16_t *xs
         srow[i] = xs + xr * (k / QK);
     }
     float acc[M];
-    row_groups<M, 1, false>(wbase, RECORD_BYTES, 0, G, xrow, srow, acc, nullptr, 0);
+    row_groups<M, 1, false>(wbase, RECORD_BYTES, 0, (int)G, 1, xrow, srow, acc, nullptr, 0);
 #pragma unroll
     for (int i = 0; i < M; i++) y[(int64_t)p[i] * n + row] = acc[i];
 }

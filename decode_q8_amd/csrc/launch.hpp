@@ -18,6 +18,7 @@ struct GemvPlan {
     int64_t tiles;     // 64-row tiles
     int64_t groups;    // 256-value groups along k
     int wgs_per_tile;  // workgroups sharing one tile (one or more segments each)
+    int segs_per_wg;   // 2048-value segments per workgroup
     int waves;         // waves per workgroup
     size_t lds;        // dynamic LDS bytes per workgroup
     size_t workspace;  // bytes: tile counters + segment sums when wgs_per_tile > 1
