@@ -163,16 +163,20 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float *
 // groups [0, G) of its row and chains in registers in the canonical two-level
 // order.  wbase/gstride: address of group 0 of this lane and the step between
 // groups in memory.
-template <int M, int LAYOUT, bool TO_LDS, typename ACT>
+template <int M, int LAYOUT, bool TO_LDS, typename ACT, bool ONE = false>
 __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride, int g0, int g1, int step,
                                            const ACT *const (&xrow)[M], const uint16_t *const (&srow)[M],
                                            float (&acc)[M], float *lds, int lane) {
     if (g0 >= g1) return;
-    GroupRegs cur, nxt;
+    // ONE: the caller guarantees at most one group (g0 + step >= g1), so no
+    // second register buffer is allocated (17 VGPRs x 4 fewer per lane, more
+    // waves per SIMD to keep loads in flight).
+    GroupRegs cur;
+    GroupRegs nxt;
     float seg[M];
     load_group<LAYOUT>(cur, wbase + g0 * gstride);
     for (int g = g0; g < g1; g += step) {
-        if (g + step < g1) load_group<LAYOUT>(nxt, wbase + (g + step) * gstride);
+        if (!ONE && g + step < g1) load_group<LAYOUT>(nxt, wbase + (g + step) * gstride);
         if (LAYOUT == 0) rows_to_packed(cur);
         const ACT *xg[M];
 #pragma unroll
@@ -198,6 +202,7 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
                 if (seg_last) acc[m] = (g < SEG_GROUPS) ? seg[m] : acc[m] + seg[m];
             }
         }
+        if (ONE) break;
         cur = nxt;
     }
 }
@@ -222,7 +227,7 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
 // last workgroup reads only after that increment returned the final count.
 // Workspace: uint32 counters [tiles] (256-byte aligned), then fp32 segment sums
 // [S][M][n].
-template <int M, int LAYOUT, typename ACT>
+template <int M, int LAYOUT, typename ACT, bool ONE>
 __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, int64_t ld_x,
                                                    const uint16_t *__restrict__ xs, const uint8_t *__restrict__ w,
                                                    int64_t n, int64_t k, float *__restrict__ y, int64_t ld_y,
@@ -257,8 +262,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, i
     const int64_t gstride = LAYOUT == 1 ? RECORD_BYTES : ROW_GROUP_BYTES;
     float unused[M];
     // wave wv takes the workgroup's groups ga + wv, ga + wv + W, ...; each sum lands in its group's LDS slot
-    row_groups<M, LAYOUT, true>(wbase, gstride, ga + wv, gb, W, xrow, srow, unused, lds_u + wv * M * TILE_ROWS,
-                                lane);
+    row_groups<M, LAYOUT, true, ACT, ONE>(wbase, gstride, ga + wv, gb, W, xrow, srow, unused,
+                                          lds_u + wv * M * TILE_ROWS, lane);
     __syncthreads();
 
     const int t = threadIdx.x;  // the plan gives at least M waves: one thread per (m, row)
@@ -356,10 +361,17 @@ static void launch_gemv_m(int64_t m, const GemvPlan &p, hipStream_t s, const ACT
     uint32_t *ctr = (uint32_t *)ws;
     float *part = ws ? (float *)((uint8_t *)ws + (p.tiles * 4 + 255) / 256 * 256) : nullptr;
     const dim3 grid((unsigned)p.wgs_per_tile, (unsigned)p.tiles), block((unsigned)(64 * p.waves));
-#define Q8_GEMV_CASE(MM)                                                                                         \
-    case MM:                                                                                                     \
-        hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT, ACT>), grid, block, p.lds, s, x, ld_x, xs, w, n, k, y, ld_y, \
-                           p.segs_per_wg, ctr, part);                                                            \
+    // one group per wave whenever the workgroup's groups do not exceed its waves
+    const int64_t gpw = (int64_t)p.segs_per_wg * SEG_GROUPS < p.groups ? (int64_t)p.segs_per_wg * SEG_GROUPS : p.groups;
+    const bool one = gpw <= p.waves;
+#define Q8_GEMV_CASE(MM)                                                                                          \
+    case MM:                                                                                                      \
+        if (one)                                                                                                  \
+            hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT, ACT, true>), grid, block, p.lds, s, x, ld_x, xs, w, n, k, \
+                               y, ld_y, p.segs_per_wg, ctr, part);                                                \
+        else                                                                                                      \
+            hipLaunchKernelGGL((gemv_kernel<MM, LAYOUT, ACT, false>), grid, block, p.lds, s, x, ld_x, xs, w, n,   \
+                               k, y, ld_y, p.segs_per_wg, ctr, part);                                             \
         break;
     switch (m) {
         Q8_GEMV_CASE(1) Q8_GEMV_CASE(2) Q8_GEMV_CASE(3) Q8_GEMV_CASE(4)
