@@ -494,8 +494,8 @@ __device__ __forceinline__ void expert_pass(const int8_t *xq, const uint16_t *xs
     int32_t p[M];
 #pragma unroll
     for (int i = 0; i < M; i++) {
-        p[i] = plist[i];
-        const int64_t xr = x_per_pair ? (int64_t)p[i] : (int64_t)p[i] / topk;
+        p[i] = plist[i];  // < 65536 pairs: 32-bit division
+        const int64_t xr = x_per_pair ? (int64_t)p[i] : (int64_t)((uint32_t)p[i] / (uint32_t)topk);
         xrow[i] = xq + xr * k;
         srow[i] = xs + xr * (k / QK);
     }
@@ -510,18 +510,19 @@ __global__ __launch_bounds__(256) void grouped_gemv_kernel(const int8_t *__restr
                                                            int topk, const uint8_t *__restrict__ w,
                                                            int64_t expert_stride, int64_t n, int64_t n_experts,
                                                            float *__restrict__ y, const int32_t *__restrict__ ws) {
+    // Grid: x = 4 consecutive tiles (one per wave), y = active-expert slot.
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + wave_id();
     const int64_t tiles = n / TILE_ROWS;
-    const int64_t slot = unit / tiles, T = unit - slot * tiles;
+    const int64_t T = (int64_t)blockIdx.x * 4 + wave_id();
+    const int64_t slot = blockIdx.y;
     const int n_active = ws[1];
-    if (slot >= n_active) return;
+    if (slot >= n_active || T >= tiles) return;
     const int32_t *active = ws + 16;
     const int32_t *offs = active + n_experts;
     const int32_t *list = offs + n_experts + 1;
     const int64_t e = active[slot];
     const int beg = offs[slot], cnt = offs[slot + 1] - beg;
-    const int64_t G = k / GROUP_K;
+    const int64_t G = k >> 8;  // k is a multiple of 256
     const uint8_t *wbase = w + e * expert_stride + T * G * RECORD_BYTES + lane * 16;
     const int64_t row = T * TILE_ROWS + lane;
     for (int start = 0; start < cnt; start += 8) {
@@ -553,11 +554,12 @@ hipError_t launch_grouped(const void *x_q, int64_t x_rows, int x_per_pair, const
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t max_slots = n_experts < pairs ? n_experts : pairs;
-    const int64_t units = max_slots * (n / TILE_ROWS);
+    const int64_t tiles = n / TILE_ROWS;
     const int8_t *xq = (const int8_t *)x_q;
     const uint16_t *xs = (const uint16_t *)((const uint8_t *)x_q + x_rows * k);
-    hipLaunchKernelGGL(grouped_gemv_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, xq, xs, k, x_per_pair,
-                       topk, (const uint8_t *)w, expert_stride, n, n_experts, y, (const int32_t *)ws);
+    hipLaunchKernelGGL(grouped_gemv_kernel, dim3((unsigned)((tiles + 3) / 4), (unsigned)max_slots), dim3(256), 0, s,
+                       xq, xs, k, x_per_pair, topk, (const uint8_t *)w, expert_stride, n, n_experts, y,
+                       (const int32_t *)ws);
     return hipGetLastError();
 }
 
