@@ -108,22 +108,23 @@ __device__ __forceinline__ void group_sums(const GroupRegs &g, const int8_t *con
     }
 }
 
-// Group sums with the activation quantization fused in: xf[m] points at the
-// group's 256 fp32 values of row m.  Lane l quantizes values 4l..4l+3 (block
+// Group sums with the activation quantization fused in: xv[m] holds lane l's
+// values 4l..4l+3 of the group's 256 fp32 values of row m (loaded by the
+// caller ahead of the weights, so the quantization does not wait for them).
+// Lane l quantizes values 4l..4l+3 (block
 // l / 8) with exactly the arithmetic of the standalone quantizer (amax over
 // the block by an exact max butterfly, d = amax / 127, q = round-half-away of
 // x / d, stored scale fp16(d)), so the codes and scales are bit-identical to
 // q8_quantize_rows.  The packed codes and scales are then broadcast from their
 // lane to the whole wave (v_readlane) as v_dot4c's scalar operand.
 template <int M>
-__device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float *const (&xf)[M], int lane,
-                                               float (&u)[M]) {
+__device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 (&xv)[M], float (&u)[M]) {
     float dw[8];
 #pragma unroll
     for (int bb = 0; bb < 8; bb++) dw[bb] = half_bits_to_float(half_of(g.c[16], bb));
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const float4 v = *reinterpret_cast<const float4 *>(xf[m] + 4 * lane);
+        const float4 v = xv[m];
         float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
         amax = fmaxf(amax, __shfl_xor(amax, 1));
         amax = fmaxf(amax, __shfl_xor(amax, 2));
@@ -174,21 +175,37 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
     GroupRegs cur;
     GroupRegs nxt;
     float seg[M];
+    // fp32 activations: each group's x values are loaded before its weights
+    // (loads complete in order, so the quantization can start early)
+    constexpr bool F32 = sizeof(ACT) == 4;
+    float4 xv[M], xn[M];
+    if constexpr (F32) {
+#pragma unroll
+        for (int m = 0; m < M; m++) xv[m] = *reinterpret_cast<const float4 *>(xrow[m] + g0 * GROUP_K + 4 * lane);
+    }
     load_group<LAYOUT>(cur, wbase + g0 * gstride);
     for (int g = g0; g < g1; g += step) {
-        if (!ONE && g + step < g1) load_group<LAYOUT>(nxt, wbase + (g + step) * gstride);
-        if (LAYOUT == 0) rows_to_packed(cur);
-        const ACT *xg[M];
+        if (!ONE && g + step < g1) {
+            if constexpr (F32) {
 #pragma unroll
-        for (int m = 0; m < M; m++) xg[m] = xrow[m] + g * GROUP_K;
+                for (int m = 0; m < M; m++)
+                    xn[m] = *reinterpret_cast<const float4 *>(xrow[m] + (g + step) * GROUP_K + 4 * lane);
+            }
+            load_group<LAYOUT>(nxt, wbase + (g + step) * gstride);
+        }
+        if (LAYOUT == 0) rows_to_packed(cur);
         float u[M];
-        if constexpr (sizeof(ACT) == 1) {
+        if constexpr (!F32) {
+            const ACT *xg[M];
             const uint16_t *sg[M];
 #pragma unroll
-            for (int m = 0; m < M; m++) sg[m] = srow[m] + g * GROUP_BLOCKS;
+            for (int m = 0; m < M; m++) {
+                xg[m] = xrow[m] + g * GROUP_K;
+                sg[m] = srow[m] + g * GROUP_BLOCKS;
+            }
             group_sums<M>(cur, xg, sg, u);
         } else {
-            group_sums_f32<M>(cur, xg, lane, u);
+            group_sums_f32<M>(cur, xv, u);
         }
         if (TO_LDS) {
 #pragma unroll
@@ -204,6 +221,10 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
         }
         if (ONE) break;
         cur = nxt;
+        if constexpr (F32) {
+#pragma unroll
+            for (int m = 0; m < M; m++) xv[m] = xn[m];
+        }
     }
 }
 
