@@ -3,10 +3,12 @@
 Default workload (``--workload decode``): one decode step of a
 Llama-3.2-1B-shaped model at batch 1 -- 16 layers of fused QKV [3072x2048],
 O [2048x2048], fused gate||up [16384x2048], down [2048x8192], then the LM head
-[128256x2048].  Every distinct input is an fp32 N(0,1) row; each matrix runs
-one q8_quantize_matmul launch (activation quantization fused into the GEMV,
-bit-identical to q8_quantize_rows + q8_matmul).  ``--unfused`` runs the two
-calls separately instead.  Weights are N(0, 0.02) fp32, quantized
+[128256x2048].  Every distinct input is an fp32 N(0,1) row.  The whole step
+is one q8_quantize_matmul_sequence launch (the 65 GEMVs in dependency order,
+activation quantization fused into each, every output bit-identical to its own
+q8_quantize_matmul launch, which the bench checks).  ``--per-matrix`` runs one
+q8_quantize_matmul launch per matrix instead, ``--unfused`` separate
+q8_quantize_rows and q8_matmul launches.  Weights are N(0, 0.02) fp32, quantized
 (q8_quantize_rows) and repacked (q8_repack_weights) on the device before
 timing.  The 1.31 GB weight set is larger than every on-chip cache, so each
 step streams it from HBM.  A step is captured once into a HIP graph and
@@ -50,6 +52,8 @@ def parse():
                     choices=["decode", "single", "batched", "prefill", "moe", "copy"])
     ap.add_argument("--m", type=int, default=1, help="rows per GEMV for --workload batched")
     ap.add_argument("--unfused", action="store_true", help="decode: separate quantize and GEMV launches")
+    ap.add_argument("--per-matrix", action="store_true",
+                    help="decode: one fused quantize+GEMV launch per matrix instead of one launch per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     return ap.parse_args()
@@ -153,7 +157,8 @@ def per_launch_ms(run, count, stream, g_filler, reps):
 def profiled_traffic(profile: str, source: str):
     """HBM bytes per launch recorded in profiles/<profile> by the rocprofv3
     FETCH_SIZE / WRITE_SIZE runs, if that summary was taken from the current
-    kernel source (its sha256 matches); otherwise None."""
+    kernel source (the sha256 of the source file, or of the listed files
+    concatenated, matches); otherwise None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
@@ -163,7 +168,11 @@ def profiled_traffic(profile: str, source: str):
         if ":" in line:
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    sources = [source] if isinstance(source, str) else list(source)
+    h = hashlib.sha256()
+    for src in sources:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    sha = h.hexdigest()
     if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -221,13 +230,19 @@ def timed_repeat(fn, min_seconds=2.0, max_reps=50):
 # --------------------------------------------------------------------------
 
 class DecodeStep:
-    def __init__(self, mats, workload, m, threads, keep_host_rows, fused):
+    """The matrices of a decode step and three ways to run them: "sequence"
+    (one q8_quantize_matmul_sequence launch for the whole step), "fused" (one
+    q8_quantize_matmul launch per matrix) and "unfused" (q8_quantize_rows then
+    q8_matmul per matrix)."""
+
+    def __init__(self, mats, workload, m, threads, keep_host_rows, mode):
         import torch
 
         import workloads as wl
         from decode_q8_amd import q8
 
-        self.q8, self.m, self.mats, self.fused = q8, m, mats, fused
+        self.q8, self.m, self.mats, self.mode = q8, m, mats, mode
+        self.fused = mode != "unfused"
         dev = torch.device("cuda", 0)
         self.w_packed, self.host_rows = [], []
         chunk = 8
@@ -253,10 +268,22 @@ class DecodeStep:
         self.y = [torch.empty((m, mt.n), dtype=torch.float32, device=dev) for mt in mats]
         need = max(q8.q8_matmul_workspace_bytes(m, mt.n, mt.k) for mt in mats)
         self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        self.steps = [(self.inputs[i][0], mt.k, self.w_packed[i], mt.n, mt.k, self.y[i], mt.n)
+                      for i, mt in enumerate(mats)]
+        if mode == "sequence":
+            need = q8.q8_sequence_workspace_bytes(self.steps, m)
+            self.seq_ws = torch.zeros(need, dtype=torch.uint8, device=dev)
         self.weight_bytes = sum(mt.n * (mt.k // 32) * 34 for mt in mats)
         torch.cuda.synchronize()
 
     def run(self, stream, gemv_timers=None):
+        if self.mode == "sequence":
+            self.q8.q8_quantize_matmul_sequence(self.steps, self.m, self.seq_ws, self.seq_ws.numel(),
+                                                stream.cuda_stream)
+        else:
+            self.run_per_matrix(stream, gemv_timers)
+
+    def run_per_matrix(self, stream, gemv_timers=None):
         q8 = self.q8
         s = stream.cuda_stream
         for i, mt in enumerate(self.mats):
@@ -289,11 +316,11 @@ class DecodeStep:
             oracle.matmul(xa, self.m, self.host_rows[i], mt.n, mt.k, threads=threads)
 
 
-def bench_gemv_workload(args, mats, workload, m, label):
+def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
     import torch
     t0 = time.time()
-    step = DecodeStep(mats, workload, m, args.threads, keep_host_rows=not args.no_cpu_baseline,
-                      fused=not args.unfused)
+    mode = "unfused" if args.unfused else ("fused" if args.per_matrix or not allow_sequence else "sequence")
+    step = DecodeStep(mats, workload, m, args.threads, keep_host_rows=not args.no_cpu_baseline, mode=mode)
     prep_s = time.time() - t0
     stream = torch.cuda.Stream()
 
@@ -305,17 +332,26 @@ def bench_gemv_workload(args, mats, workload, m, label):
     for i, y in enumerate(step.y):
         if not torch.equal(y.view(torch.int32), eager[i].view(torch.int32)):
             raise RuntimeError(f"graph replay output {i} differs from the eager step")
+    if mode == "sequence":
+        # the one-launch step must equal the per-matrix launches bit for bit
+        step.run_per_matrix(stream)
+        torch.cuda.synchronize()
+        for i, y in enumerate(step.y):
+            if not torch.equal(y.view(torch.int32), eager[i].view(torch.int32)):
+                raise RuntimeError(f"sequence output {i} differs from its own launch")
 
-    # per-matrix breakdown: each launch bracketed by its own events (an event
-    # pair also costs the launch latency the graph hides, so these overstate)
-    gemv_ms = per_launch_ms(step.run, len(step.mats), stream, g_filler=graph, reps=max(1, min(args.steps, 10)))
-    # the dominant kernel's average launch duration: in the fused step every
-    # launch is that kernel, so one event pair around the whole queued-ahead
-    # sequence, divided by the number of launches
-    seq_ms = None
-    if step.fused:
-        seq_ms = sequence_ms(step.run, stream, graph, reps=max(1, min(args.steps, 10))) / len(step.mats)
+    # per-matrix breakdown (one launch per matrix, each bracketed by its own
+    # events queued behind replays of the captured step)
+    gemv_ms = per_launch_ms(step.run_per_matrix, len(step.mats), stream, g_filler=graph,
+                            reps=max(1, min(args.steps, 10)))
     gemv_bytes = np.array([step.gemv_bytes(i) for i in range(len(step.mats))], dtype=np.float64)
+    # the dominant kernel's average launch duration: one event pair around the
+    # queued-ahead launches of one step, divided by the number of launches
+    seq_ms = None
+    if mode == "sequence":
+        seq_ms = sequence_ms(step.run, stream, graph, reps=max(1, min(args.steps, 10)))
+    elif mode == "fused":
+        seq_ms = sequence_ms(step.run, stream, graph, reps=max(1, min(args.steps, 10))) / len(step.mats)
 
     value = step.weight_bytes / (ms_per_step * 1e-3) / 1e9
     per = {}
@@ -332,27 +368,38 @@ def bench_gemv_workload(args, mats, workload, m, label):
                "sample": f"the whole {label} ({len(mats)} matrices, quantize + matmul), {reps_c} runs, "
                          f"{sec:.3f} s each"}
 
-    kname = "q8k::gemv_kernel<%d, packed, %s>" % (m, "fp32 in" if step.fused else "int8 in")
+    launches = {"sequence": f"1 (q8_quantize_matmul_sequence over {len(mats)} fused quantize+GEMV steps)",
+                "fused": f"{len(mats)} fused quantize+GEMV",
+                "unfused": f"{len(mats)} quantize + {len(mats)} GEMV"}[mode]
     config = {
         "workload": label,
         "m": m,
         "weight_bytes": step.weight_bytes,
-        "launches_per_step": (f"{len(mats)} fused quantize+GEMV" if step.fused
-                              else f"{len(mats)} quantize + {len(mats)} GEMV"),
+        "launches_per_step": launches,
         "hip_graph": True,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "gemv_GBs_by_matrix": per_matrix,
-        "gemv_us_by_matrix": {mt.name: round(float(gemv_ms[i]) * 1e3, 2) for i, mt in enumerate(step.mats)
-                              if mt.layer == 0 or mt.name == "lm_head"},
+        "per_matrix_launch_GBs": per_matrix,
+        "per_matrix_launch_us": {mt.name: round(float(gemv_ms[i]) * 1e3, 2) for i, mt in enumerate(step.mats)
+                                 if mt.layer == 0 or mt.name == "lm_head"},
         "prep_seconds": round(prep_s, 1),
     }
     metric = ("Q8_0 matmul weight GB/s (%HBM peak) at M=1" if m == 1 else f"Q8_0 matmul weight GB/s at M={m}")
-    avg_ms = seq_ms if seq_ms is not None else float(gemv_ms.mean())
-    roof = hbm_roofline(kname, float(gemv_bytes.mean()), avg_ms)
-    roof["timing"] = ("one event pair around all launches of the step, queued ahead; per launch = total / launches"
-                      if seq_ms is not None else "one event pair per launch, queued ahead")
-    if step.fused and m == 1 and len(mats) == 65:
-        roof["traffic"] = profiled_traffic("gemv_decode_step_llama1b.txt", "decode_q8_amd/csrc/gemv.hip")
+    if mode == "sequence":
+        kname = "q8k::gemv_sequence_kernel<%d>" % m
+        roof = hbm_roofline(kname, float(gemv_bytes.sum()), seq_ms)
+        roof["timing"] = "one event pair around the step's single launch, queued ahead"
+        if m == 1 and len(mats) == 65:
+            roof["traffic"] = profiled_traffic("gemv_sequence_decode_step_llama1b.txt",
+                                               ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
+    else:
+        kname = "q8k::gemv_kernel<%d, packed, %s>" % (m, "fp32 in" if step.fused else "int8 in")
+        avg_ms = seq_ms if seq_ms is not None else float(gemv_ms.mean())
+        roof = hbm_roofline(kname, float(gemv_bytes.mean()), avg_ms)
+        roof["timing"] = ("one event pair around all launches of the step, queued ahead; per launch = total / "
+                          "launches" if seq_ms is not None else "one event pair per launch, queued ahead")
+        if step.fused and m == 1 and len(mats) == 65:
+            roof["traffic"] = profiled_traffic("gemv_decode_step_llama1b.txt",
+                                               ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
     return base_record(args, metric, value, "GB/s", ms_per_step, "int8xint8->int32, fp32 scale/sum", config,
                        roof, cpu)
 
@@ -368,7 +415,8 @@ def bench_decode(args):
 def bench_single(args):
     import workloads as wl
     mats = [wl.Matrix("w", 2048, 2048, 0, 0, 0)]
-    return bench_gemv_workload(args, mats, wl.SINGLE, 1, "single Q8_0 GEMV, W 2048x2048, one activation row")
+    return bench_gemv_workload(args, mats, wl.SINGLE, 1, "single Q8_0 GEMV, W 2048x2048, one activation row",
+                               allow_sequence=False)
 
 
 # --------------------------------------------------------------------------

@@ -13,6 +13,8 @@
 #include "../../include/q8.h"
 #include "launch.hpp"
 
+static_assert(Q8_SEQUENCE_MAX_STEPS == q8k::SEQ_MAX_STEPS, "sequence length limit");
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -123,6 +125,44 @@ int q8_quantize_matmul(const float *x, int64_t ld_x, int64_t m, const void *w, i
     const int dev = check_device();
     if (dev != Q8_OK) return dev;
     return launched(q8k::launch_gemv_f32(x, ld_x, m, w, layout, n, k, y, ld_y, workspace, stream));
+}
+
+namespace {
+
+// Validates a sequence and converts it to the launcher's form; returns a status.
+int sequence_steps(const q8_gemv_step *steps, int count, int64_t m, q8k::SeqHostStep *out) {
+    if (!steps || count <= 0 || m <= 0) return Q8_ERR_ARG;
+    if (count > Q8_SEQUENCE_MAX_STEPS || m > Q8_GEMV_MAX_ROWS) return Q8_ERR_SHAPE;
+    for (int i = 0; i < count; i++) {
+        const q8_gemv_step &s = steps[i];
+        if (!s.x || !s.w || !s.y || s.n <= 0 || s.k <= 0 || s.ld_x < s.k || s.ld_y < s.n) return Q8_ERR_ARG;
+        if (s.n % Q8_TILE_ROWS || s.k % (Q8_BLOCK * Q8_TILE_BLOCKS)) return Q8_ERR_SHAPE;
+        if (s.n > INT32_MAX || s.k > INT32_MAX || s.ld_x > INT32_MAX || s.ld_y > INT32_MAX) return Q8_ERR_SHAPE;
+        if (!aligned16(s.x) || !aligned16(s.w) || !aligned16(s.y) || s.ld_x % 4) return Q8_ERR_ALIGN;
+        out[i] = q8k::SeqHostStep{s.x, s.w, s.y, s.ld_x, s.ld_y, s.n, s.k};
+    }
+    return Q8_OK;
+}
+
+}  // namespace
+
+size_t q8_sequence_workspace_bytes(const q8_gemv_step *steps, int count, int64_t m) {
+    q8k::SeqHostStep hs[Q8_SEQUENCE_MAX_STEPS];
+    if (sequence_steps(steps, count, m, hs) != Q8_OK) return 0;
+    return q8k::gemv_sequence_workspace_bytes(hs, count, m);
+}
+
+int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    q8k::SeqHostStep hs[Q8_SEQUENCE_MAX_STEPS];
+    const int st = sequence_steps(steps, count, m, hs);
+    if (st != Q8_OK) return st;
+    const size_t need = q8k::gemv_sequence_workspace_bytes(hs, count, m);
+    if (!workspace || workspace_bytes < need) return Q8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return Q8_ERR_ALIGN;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_gemv_sequence(hs, count, m, workspace, stream));
 }
 
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k) {

@@ -1,0 +1,325 @@
+// Device code of the GEMV shared by the per-matrix kernel (gemv.hip) and the
+// persistent sequence kernel (gemv_seq.hip): one lane's group of weights, the
+// group sums (int8 or fp32 activations), the walk over a row's groups and one
+// workgroup's share of a 64-row tile with its fixed-order chain.
+#pragma once
+
+#include "device.hpp"
+
+namespace q8k {
+
+// One lane's bytes of one group of one row: chunks [2*bb + h] hold the 16
+// values of block bb, half h; chunk 16 holds the 8 fp16 scales.
+struct GroupRegs {
+    uint4 c[17];
+};
+
+template <int LAYOUT>
+__device__ __forceinline__ void load_group(GroupRegs &g, const uint8_t *p) {
+    if (LAYOUT == 1) {  // packed: p = record + lane * 16
+#pragma unroll
+        for (int i = 0; i < 16; i++) g.c[i] = *reinterpret_cast<const uint4 *>(p + i * 1024);
+        g.c[16] = *reinterpret_cast<const uint4 *>(p + RECORD_Q_BYTES);
+    } else {  // rows: p = this row's 272 bytes of the group (8 blocks of 34 bytes)
+#pragma unroll
+        for (int i = 0; i < 17; i++) g.c[i] = *reinterpret_cast<const uint4 *>(p + i * 16);
+    }
+}
+
+// Row-contiguous bytes [d0 q0..q31][d1 q0..q31]... -> the packed register form.
+// Even blocks start on a dword boundary (scale in the low half); odd blocks
+// start 2 bytes into a dword (scale in the high half, values dword aligned).
+__device__ __forceinline__ void rows_to_packed(GroupRegs &g) {
+    uint32_t w[68];
+#pragma unroll
+    for (int i = 0; i < 17; i++) {
+        w[4 * i] = g.c[i].x; w[4 * i + 1] = g.c[i].y; w[4 * i + 2] = g.c[i].z; w[4 * i + 3] = g.c[i].w;
+    }
+    uint32_t q[64], sc[8];
+#pragma unroll
+    for (int bb = 0; bb < 8; bb++) {
+        const int wi = 17 * (bb >> 1) + ((bb & 1) ? 8 : 0);
+        if ((bb & 1) == 0) {
+            sc[bb] = w[wi] & 0xffffu;
+#pragma unroll
+            for (int c = 0; c < 8; c++) q[8 * bb + c] = __builtin_amdgcn_alignbyte(w[wi + c + 1], w[wi + c], 2);
+        } else {
+            sc[bb] = w[wi] >> 16;
+#pragma unroll
+            for (int c = 0; c < 8; c++) q[8 * bb + c] = w[wi + 1 + c];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++) g.c[i] = make_uint4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+    g.c[16] = make_uint4(sc[0] | (sc[1] << 16), sc[2] | (sc[3] << 16), sc[4] | (sc[5] << 16), sc[6] | (sc[7] << 16));
+}
+
+__device__ __forceinline__ uint32_t half_of(const uint4 &v, int bb) {
+    return (word_of(v, bb >> 1) >> (16 * (bb & 1))) & 0xffffu;
+}
+
+typedef __attribute__((address_space(4))) int const_i32;
+
+// Group sums u[m] for M activation rows.  xg[m] / sg[m] point at the group's
+// 256 int8 values / 8 fp16 scales of row m (wave-uniform).
+template <int M>
+__device__ __forceinline__ void group_sums(const GroupRegs &g, const int8_t *const (&xg)[M],
+                                           const uint16_t *const (&sg)[M], float (&u)[M]) {
+    float dw[8];
+#pragma unroll
+    for (int bb = 0; bb < 8; bb++) dw[bb] = half_bits_to_float(half_of(g.c[16], bb));
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        // Activations are read-only and wave-uniform: constant-address-space
+        // loads become scalar loads into SGPRs, which v_dot4c reads directly.
+        const const_i32 *xi = (const const_i32 *)(xg[m]);
+        const const_i32 *xsp = (const const_i32 *)(sg[m]);
+        const uint4 xsv = make_uint4((uint32_t)xsp[0], (uint32_t)xsp[1], (uint32_t)xsp[2], (uint32_t)xsp[3]);
+        float t[8];
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) {
+            int s = 0;
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    s = __builtin_amdgcn_sdot4((int)word_of(g.c[2 * bb + h], c), xi[8 * bb + 4 * h + c], s, false);
+            const float dx = half_bits_to_float(half_of(xsv, bb));
+            t[bb] = (float)s * (dw[bb] * dx);  // Dw * Dx exact: one rounding
+        }
+        u[m] = tree8(t);
+    }
+}
+
+// Group sums with the activation quantization fused in: xv[m] holds lane l's
+// values 4l..4l+3 of the group's 256 fp32 values of row m (loaded by the
+// caller ahead of the weights, so the quantization does not wait for them).
+// Lane l quantizes values 4l..4l+3 (block
+// l / 8) with exactly the arithmetic of the standalone quantizer (amax over
+// the block by an exact max butterfly, d = amax / 127, q = round-half-away of
+// x / d, stored scale fp16(d)), so the codes and scales are bit-identical to
+// q8_quantize_rows.  The packed codes and scales are then broadcast from their
+// lane to the whole wave (v_readlane) as v_dot4c's scalar operand.
+template <int M>
+__device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 (&xv)[M], float (&u)[M]) {
+    float dw[8];
+#pragma unroll
+    for (int bb = 0; bb < 8; bb++) dw[bb] = half_bits_to_float(half_of(g.c[16], bb));
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const float4 v = xv[m];
+        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const float d = amax / 127.0f;
+        int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+        if (d != 0.0f) {
+            q0 = (int)roundf(v.x / d);
+            q1 = (int)roundf(v.y / d);
+            q2 = (int)roundf(v.z / d);
+            q3 = (int)roundf(v.w / d);
+        }
+        const int qd = (int)(((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
+                             ((uint32_t)q3 << 24));
+        const float dxl = half_bits_to_float(float_to_half_bits(d));
+        float t[8];
+#pragma unroll
+        for (int bb = 0; bb < 8; bb++) {
+            int s = 0;
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    s = __builtin_amdgcn_sdot4((int)word_of(g.c[2 * bb + h], c),
+                                               __builtin_amdgcn_readlane(qd, 8 * bb + 4 * h + c), s, false);
+            const float dx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dxl), 8 * bb));
+            t[bb] = (float)s * (dw[bb] * dx);
+        }
+        u[m] = tree8(t);
+    }
+}
+
+// Walk groups g0, g0 + step, ... (< g1) of one lane's row.  TO_LDS = true:
+// store each group sum u_g at lds[((g - g0) * M + m) * 64 + lane] (the caller
+// points lds at group g0's slot; slots of M x 64 floats hold consecutive
+// groups); the workgroup chains them later.  TO_LDS = false (step 1, g0 = 0):
+// the wave owns groups [0, G) of its row and chains in registers in the
+// canonical two-level order.  wbase/gstride: address of group 0 of this lane
+// and the step between groups in memory.
+// wait_inputs() runs after the first group's weight loads are issued and
+// before any activation is read; every wave calls it, also a wave without a
+// group, so it may contain a workgroup barrier.
+template <int M, int LAYOUT, bool TO_LDS, typename ACT, bool ONE, typename Wait>
+__device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride, int g0, int g1, int step,
+                                           const ACT *const (&xrow)[M], const uint16_t *const (&srow)[M],
+                                           float (&acc)[M], float *lds, int lane, Wait &&wait_inputs) {
+    // ONE: the caller guarantees at most one group (g0 + step >= g1), so no
+    // second register buffer is allocated (17 VGPRs x 4 fewer per lane, more
+    // waves per SIMD to keep loads in flight).
+    GroupRegs cur;
+    GroupRegs nxt;
+    float seg[M];
+    constexpr bool F32 = sizeof(ACT) == 4;
+    float4 xv[M], xn[M];
+    const bool any = g0 < g1;
+    if (any) load_group<LAYOUT>(cur, wbase + g0 * gstride);
+    wait_inputs();
+    if (!any) return;
+    if constexpr (F32) {
+#pragma unroll
+        for (int m = 0; m < M; m++) xv[m] = *reinterpret_cast<const float4 *>(xrow[m] + g0 * GROUP_K + 4 * lane);
+    }
+    for (int g = g0; g < g1; g += step) {
+        if (!ONE && g + step < g1) {
+            if constexpr (F32) {
+#pragma unroll
+                for (int m = 0; m < M; m++)
+                    xn[m] = *reinterpret_cast<const float4 *>(xrow[m] + (g + step) * GROUP_K + 4 * lane);
+            }
+            load_group<LAYOUT>(nxt, wbase + (g + step) * gstride);
+        }
+        if (LAYOUT == 0) rows_to_packed(cur);
+        float u[M];
+        if constexpr (!F32) {
+            const ACT *xg[M];
+            const uint16_t *sg[M];
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                xg[m] = xrow[m] + g * GROUP_K;
+                sg[m] = srow[m] + g * GROUP_BLOCKS;
+            }
+            group_sums<M>(cur, xg, sg, u);
+        } else {
+            group_sums_f32<M>(cur, xv, u);
+        }
+        if (TO_LDS) {
+#pragma unroll
+            for (int m = 0; m < M; m++) lds[((g - g0) * M + m) * TILE_ROWS + lane] = u[m];
+        } else {
+            const bool seg_first = (g % SEG_GROUPS) == 0;
+            const bool seg_last = (g % SEG_GROUPS) == SEG_GROUPS - 1 || g == g1 - 1;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                seg[m] = seg_first ? u[m] : seg[m] + u[m];
+                if (seg_last) acc[m] = (g < SEG_GROUPS) ? seg[m] : acc[m] + seg[m];
+            }
+        }
+        if (ONE) break;
+        cur = nxt;
+        if constexpr (F32) {
+#pragma unroll
+            for (int m = 0; m < M; m++) xv[m] = xn[m];
+        }
+    }
+}
+
+struct NoWait {
+    __device__ void operator()() const {}
+};
+
+// One workgroup's share of one 64-row tile: segments [wi * segs_per_wg, ...)
+// of tile T.  A tile's groups are split into segments of 8 (2048 values); the
+// workgroup's W waves take its groups round-robin (wave w: groups w, w + W,
+// ...) and leave every group sum in LDS.  After a barrier each (row, m) is
+// chained in the canonical order:
+//   S_j = ((u_8j + u_8j+1) + ...) + u_8j+7   within segment j,
+//   y   = ((S_0 + S_1) + S_2) + ...          over the segments.
+// When one workgroup covers the whole tile (wgs_per_tile == 1) it writes y.
+// Otherwise (narrow matrices with long rows, where one workgroup per tile
+// would leave most CUs idle) each workgroup hands its segment sums to the
+// workspace and counts in at its tile's counter; the workgroup that arrives
+// last chains all segment sums and writes y, then clears the counter (so
+// counters that start at zero stay zero).  Cross-workgroup visibility without
+// cache-wide fences: segment sums are written and read back with
+// read-modify-write atomics (exchange in; exchange with 0 out -- an idempotent
+// RMW would be lowered to a plain atomic load, which can hit a stale line of a
+// non-coherent L2), performed at the device-coherent point like the counter;
+// every thread waits for its exchanges before the barrier that precedes the
+// counter increment, and the last workgroup reads only after that increment
+// returned the final count.  Every thread of the workgroup calls this
+// (it contains barriers); lds_u holds [groups of the workgroup][M][64] floats.
+// Workspace: uint32 counters [tiles] (256-byte aligned), then fp32 segment sums
+// [S][M][n].
+template <int M, int LAYOUT, typename ACT, bool ONE, typename Wait>
+__device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld_x, const uint16_t *__restrict__ xs,
+                                          const uint8_t *__restrict__ w, int64_t n, int64_t k, float *__restrict__ y,
+                                          int64_t ld_y, int64_t T, int wi, int wgs_per_tile, int segs_per_wg,
+                                          uint32_t *__restrict__ ctr, float *__restrict__ part, float *lds_u,
+                                          int *last_wg, Wait &&wait_inputs) {
+    const int lane = threadIdx.x & 63;
+    const int wv = wave_id();
+    const int W = blockDim.x >> 6;
+    const int G = (int)(k >> 8);                        // k is a multiple of 256
+    const int S = (G + SEG_GROUPS - 1) / SEG_GROUPS;    // constant divisor: a shift
+    const int s0 = wi * segs_per_wg, s1 = min(s0 + segs_per_wg, S);
+    const int ga = s0 * SEG_GROUPS, gb = min(s1 * SEG_GROUPS, G);
+    const int64_t row = T * TILE_ROWS + lane;
+    const int64_t row_c = row < n ? row : n - 1;
+
+    const ACT *xrow[M];
+    const uint16_t *srow[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        xrow[m] = xq + m * ld_x;
+        srow[m] = xs + m * (k / QK);
+    }
+    const uint8_t *wbase = LAYOUT == 1 ? w + T * G * RECORD_BYTES + lane * 16 : w + row_c * (k / QK) * BLOCK_BYTES;
+    const int64_t gstride = LAYOUT == 1 ? RECORD_BYTES : ROW_GROUP_BYTES;
+    float unused[M];
+    // wave wv takes the workgroup's groups ga + wv, ga + wv + W, ...; each sum lands in its group's LDS slot
+    row_groups<M, LAYOUT, true, ACT, ONE>(wbase, gstride, ga + wv, gb, W, xrow, srow, unused,
+                                          lds_u + wv * M * TILE_ROWS, lane, wait_inputs);
+    __syncthreads();
+
+    const int t = threadIdx.x;  // the plan gives at least M waves: one thread per (m, row)
+    const bool chain_thread = t < M * TILE_ROWS;
+    const int cm = t >> 6, cr = t & 63;
+    const int64_t out_row = T * TILE_ROWS + cr;
+    const bool out_ok = chain_thread && out_row < n;
+    float acc = 0.0f;
+    if (chain_thread) {
+        for (int64_t sj = s0; sj < s1; sj++) {
+            const int64_t gs = sj * SEG_GROUPS, ge = (gs + SEG_GROUPS) < G ? (gs + SEG_GROUPS) : G;
+            float sv = lds_u[((gs - ga) * M + cm) * TILE_ROWS + cr];
+            for (int64_t g = gs + 1; g < ge; g++) sv += lds_u[((g - ga) * M + cm) * TILE_ROWS + cr];
+            if (wgs_per_tile == 1) {
+                acc = sj == 0 ? sv : acc + sv;
+            } else if (out_ok) {
+                __hip_atomic_exchange((uint32_t *)&part[(sj * M + cm) * n + out_row], __builtin_bit_cast(uint32_t, sv),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (wgs_per_tile == 1) {
+        if (out_ok) y[cm * ld_y + out_row] = acc;
+        return;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's exchanges have completed
+    __syncthreads();
+    if (t == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&ctr[T], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last_wg = old == (uint32_t)(wgs_per_tile - 1);
+    }
+    __syncthreads();
+    if (!*last_wg) return;
+    if (out_ok) {
+        for (int64_t b0 = 0; b0 < S; b0 += 8) {
+            float v[8];  // eight exchanges in flight, then the in-order chain
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                v[j] = b0 + j < S ? __builtin_bit_cast(float, __hip_atomic_exchange(
+                                                                  (uint32_t *)&part[((b0 + j) * M + cm) * n + out_row],
+                                                                  0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                  : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                if (b0 + j < S) acc = (b0 + j == 0) ? v[j] : acc + v[j];
+        }
+        y[cm * ld_y + out_row] = acc;
+    }
+    if (t == 0) __hip_atomic_exchange(&ctr[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
+}  // namespace q8k

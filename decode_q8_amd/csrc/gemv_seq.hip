@@ -1,0 +1,214 @@
+// A sequence of fused-quantization GEMVs in one persistent launch (a decode
+// step's matrices, each consuming the activation of the step before it).
+//
+// Every GEMV is computed exactly as the per-matrix kernel computes it (the
+// same tile_unit, so the outputs are bit-identical); what changes is how the
+// work is scheduled.  A fixed grid of workgroups that all fit on the GPU at
+// once walks the steps in order.  Step p's work units (a 64-row tile, or one
+// workgroup's share of a split tile) go to the workgroups round-robin,
+// starting where step p - 1's units ended, so consecutive small steps land on
+// different workgroups.  A workgroup issues the weight loads of its next unit
+// as soon as it is free, then waits until every unit of step p - 1 has been
+// counted done before it reads step p's activations: the weights of the next
+// matrix stream in while the previous one finishes, which a launch per matrix
+// cannot do (the weights do not depend on the activations; the activations
+// do depend on the step before, which the wait models).
+//
+// Step completion is a per-step counter in the workspace, incremented with a
+// device-scope atomic (performed at the device-coherent point) once a unit is
+// done.  The unit that brings it to the step's unit count raises the step's
+// flag in FLAG_LINES separate lines with system-scope stores, and a waiting
+// workgroup polls "its" line (workgroup index mod FLAG_LINES, so roughly one
+// line per XCD) with system-scope loads: both bypass the per-XCD L2s, which
+// are not coherent with each other, and spreading the pollers over lines
+// keeps hundreds of them from queueing on one address (measured: polling the
+// counter itself with read-modify-writes made the step 2x slower).  The poll
+// is bounded: a wait that does not end within the limit (only possible if the
+// grid did not fit on the GPU) records Q8_ERR_LAUNCH in the workspace status
+// word and proceeds -- outputs do not depend on the waits, since every input
+// is ready before the launch.  The unit that completes the last step returns
+// every counter and flag to zero; by then no workgroup is waiting any more,
+// since each wait precedes a unit that the last step transitively depends on.
+#include "device.hpp"
+#include "gemv_core.hpp"
+#include "launch.hpp"
+
+namespace q8k {
+
+constexpr int SEQ_THREADS = 512;
+constexpr uint32_t SEQ_SPIN_LIMIT = 1u << 18;  // polls of roughly 1 us each
+constexpr int FLAG_LINES = 8;
+constexpr int FLAG_LINE_BYTES = 4096;  // one int32 flag per step in each line
+static_assert(SEQ_MAX_STEPS * 4 <= FLAG_LINE_BYTES, "a flag line holds every step's flag");
+
+struct SeqStep {
+    const float *x;
+    const uint8_t *w;
+    float *y;
+    int32_t ld_x, ld_y, n, k;
+    uint32_t ws_off;  // this step's tile counters and segment sums at ws + 256 * ws_off (0: none)
+    uint16_t wgs;     // workgroups per tile
+    uint16_t segs;    // segments per workgroup
+};
+static_assert(sizeof(SeqStep) == 48, "kernel-argument layout");
+
+// Workspace: [0, 4) status word; step p's done counter at 256 * (p + 1);
+// FLAG_LINES flag lines from flag_off (4 KB aligned); then the split steps'
+// tile counters and segment sums.
+struct SeqArgs {
+    uint8_t *ws;
+    int32_t count, nwg;
+    int32_t flag_off;
+    SeqStep step[SEQ_MAX_STEPS];
+};
+
+__device__ __forceinline__ uint32_t *done_counter(uint8_t *ws, int p) {
+    return reinterpret_cast<uint32_t *>(ws + 256 * (p + 1));
+}
+
+__device__ __forceinline__ uint32_t *step_flag(const SeqArgs &a, int line, int p) {
+    return reinterpret_cast<uint32_t *>(a.ws + a.flag_off + FLAG_LINE_BYTES * line + 4 * p);
+}
+
+// Thread-level wait until *flag != 0 (bounded; see the file comment).
+__device__ __forceinline__ void wait_flag(uint32_t *flag, int32_t *status) {
+    for (uint32_t i = 0; i < SEQ_SPIN_LIMIT; i++) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u) return;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __hip_atomic_exchange(status, 6 /* Q8_ERR_LAUNCH */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int M, bool ONE>
+__global__ __launch_bounds__(SEQ_THREADS) void gemv_sequence_kernel(const SeqArgs a) {
+    extern __shared__ float lds_u[];  // [groups of a unit][M][64]
+    __shared__ int last_wg;
+    const int wg = blockIdx.x, nwg = a.nwg;
+    int32_t *status = reinterpret_cast<int32_t *>(a.ws);
+    int start = 0;       // workgroup of step p's first unit: (units of all earlier steps) mod nwg
+    for (int p = 0; p < a.count; p++) {
+        const SeqStep &st = a.step[p];
+        const int tiles = st.n >> 6;
+        const int units = tiles * st.wgs;
+        uint32_t *ctr = st.ws_off ? reinterpret_cast<uint32_t *>(a.ws + 256 * (size_t)st.ws_off) : nullptr;
+        float *part = ctr ? reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ctr) + (tiles * 4 + 255) / 256 * 256)
+                          : nullptr;
+        // this workgroup's units of step p: u = first, first + nwg, ... (32-bit arithmetic throughout)
+        const int first = wg >= start ? wg - start : wg - start + nwg;
+        bool ready = p == 0;
+        for (int u = first; u < units; u += nwg) {
+            const int T = u / st.wgs, wi = u - T * st.wgs;
+            __syncthreads();  // the previous unit's LDS reads are complete
+            auto wait_inputs = [&]() {
+                if (!ready) {
+                    if (threadIdx.x == 0) wait_flag(step_flag(a, wg % FLAG_LINES, p - 1), status);
+                    __syncthreads();
+                }
+            };
+            tile_unit<M, 1, float, ONE>(st.x, st.ld_x, nullptr, st.w, st.n, st.k, st.y, st.ld_y, T, wi, st.wgs,
+                                        st.segs, ctr, part, lds_u, &last_wg, wait_inputs);
+            ready = true;
+            __syncthreads();  // every wave of the unit is done
+            if (threadIdx.x < 64) {  // wave 0: count the unit in; the last one raises the step's flags
+                uint32_t old = 0;
+                if (threadIdx.x == 0)
+                    old = __hip_atomic_fetch_add(done_counter(a.ws, p), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool last = __builtin_amdgcn_readfirstlane(old) == (uint32_t)units - 1;
+                if (last && threadIdx.x < FLAG_LINES)
+                    __hip_atomic_store(step_flag(a, threadIdx.x, p), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                if (last && p == a.count - 1) {  // the whole sequence is done: clear counters and flags
+                    for (int q = threadIdx.x; q < a.count; q += 64)
+                        __hip_atomic_exchange(done_counter(a.ws, q), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int i = threadIdx.x; i < FLAG_LINES * a.count; i += 64)
+                        __hip_atomic_store(step_flag(a, i / a.count, i % a.count), 0u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+                }
+            }
+        }
+        start = (start + units % nwg) % nwg;
+    }
+}
+
+// Host side ---------------------------------------------------------------
+
+struct SeqLayout {
+    bool one;
+    size_t lds, workspace;
+    SeqArgs args;
+};
+
+static bool seq_layout(const SeqHostStep *steps, int count, int64_t m, SeqLayout &L) {
+    L.one = true;
+    L.lds = 0;
+    // status line + one line per done counter, then the flag lines (4 KB aligned)
+    const size_t flag_off = (256 * (size_t)(count + 1) + FLAG_LINE_BYTES - 1) / FLAG_LINE_BYTES * FLAG_LINE_BYTES;
+    size_t off = flag_off + (size_t)FLAG_LINES * FLAG_LINE_BYTES;
+    L.args.count = count;
+    L.args.flag_off = (int32_t)flag_off;
+    for (int i = 0; i < count; i++) {
+        const SeqHostStep &h = steps[i];
+        const GemvPlan p = gemv_plan(m, h.n, h.k);
+        const int64_t gpw = (int64_t)p.segs_per_wg * SEG_GROUPS < p.groups ? (int64_t)p.segs_per_wg * SEG_GROUPS
+                                                                           : p.groups;
+        if (gpw > SEQ_THREADS / 64) L.one = false;
+        if (p.lds > L.lds) L.lds = p.lds;
+        SeqStep &s = L.args.step[i];
+        s.x = h.x;
+        s.w = (const uint8_t *)h.w;
+        s.y = h.y;
+        s.ld_x = (int32_t)h.ld_x;
+        s.ld_y = (int32_t)h.ld_y;
+        s.n = (int32_t)h.n;
+        s.k = (int32_t)h.k;
+        s.wgs = (uint16_t)p.wgs_per_tile;
+        s.segs = (uint16_t)p.segs_per_wg;
+        s.ws_off = 0;
+        if (p.workspace) {
+            s.ws_off = (uint32_t)(off / 256);
+            off += (p.workspace + 255) / 256 * 256;
+        }
+    }
+    L.workspace = off;
+    return true;
+}
+
+size_t gemv_sequence_workspace_bytes(const SeqHostStep *steps, int count, int64_t m) {
+    SeqLayout L;
+    seq_layout(steps, count, m, L);
+    return L.workspace;
+}
+
+template <int M, bool ONE>
+static hipError_t launch_seq(SeqLayout &L, void *ws, hipStream_t s) {
+    // The grid is as many workgroups as the GPU holds at once: the waits need
+    // every workgroup resident.
+    int dev = 0, per_cu = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_sequence_kernel<M, ONE>, SEQ_THREADS, L.lds);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+    L.args.ws = (uint8_t *)ws;
+    L.args.nwg = per_cu * cus;
+    hipLaunchKernelGGL((gemv_sequence_kernel<M, ONE>), dim3((unsigned)L.args.nwg), dim3(SEQ_THREADS), L.lds, s,
+                       L.args);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, void *ws, hipStream_t s) {
+    SeqLayout L;
+    seq_layout(steps, count, m, L);
+#define Q8_SEQ_CASE(MM) \
+    case MM:            \
+        return L.one ? launch_seq<MM, true>(L, ws, s) : launch_seq<MM, false>(L, ws, s);
+    switch (m) {
+        Q8_SEQ_CASE(1) Q8_SEQ_CASE(2) Q8_SEQ_CASE(3) Q8_SEQ_CASE(4)
+        Q8_SEQ_CASE(5) Q8_SEQ_CASE(6) Q8_SEQ_CASE(7) Q8_SEQ_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef Q8_SEQ_CASE
+}
+
+}  // namespace q8k

@@ -33,6 +33,19 @@ hipError_t launch_gemv(const void *x_q, int64_t m, const void *w, int layout, in
 hipError_t launch_gemv_f32(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
                            float *y, int64_t ld_y, void *workspace, hipStream_t s);
 
+// A sequence of fused-quantization GEMVs in one persistent launch (packed
+// weights, m <= 8 rows each, step p + 1 reading its activations only after
+// step p is complete).
+constexpr int SEQ_MAX_STEPS = 72;
+struct SeqHostStep {
+    const float *x;
+    const void *w;
+    float *y;
+    int64_t ld_x, ld_y, n, k;
+};
+size_t gemv_sequence_workspace_bytes(const SeqHostStep *steps, int count, int64_t m);
+hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, void *workspace, hipStream_t s);
+
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s);
 

@@ -21,6 +21,13 @@ Q8_BLOCK = 32
 Q8_BLOCK_BYTES = 34
 Q8_TILE_ROWS = 64
 Q8_GEMV_MAX_ROWS = 8
+Q8_SEQUENCE_MAX_STEPS = 72
+
+
+class q8_gemv_step(ctypes.Structure):
+    """One GEMV of a sequence (the C struct q8_gemv_step)."""
+    _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("y", ctypes.c_void_p), ("ld_x", ctypes.c_int64),
+                ("ld_y", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 # The C entry points declared in include/q8.h, with their ctypes signatures.
 _P, _I64, _I, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32
@@ -33,6 +40,8 @@ SIGNATURES = {
     "q8_matmul_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "q8_matmul": ([_P, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
     "q8_quantize_matmul": ([_P, _I64, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
+    "q8_sequence_workspace_bytes": ([_P, _I, _I64], _SZ),
+    "q8_quantize_matmul_sequence": ([_P, _I, _I64, _P, _SZ, _P], _I),
     "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
     "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
 }
@@ -104,6 +113,27 @@ def q8_quantized_bytes(rows: int, k: int) -> int:
 
 def q8_matmul_workspace_bytes(m: int, n: int, k: int) -> int:
     return lib().q8_matmul_workspace_bytes(m, n, k)
+
+
+def _steps(steps):
+    """A sequence of (x, ld_x, w, n, k, y, ld_y) tuples (tensors or pointers) ->
+    (ctypes array of q8_gemv_step, count)."""
+    arr = (q8_gemv_step * max(1, len(steps)))()
+    for i, (x, ld_x, w, n, k, y, ld_y) in enumerate(steps):
+        arr[i] = q8_gemv_step(_ptr(x), _ptr(w), _ptr(y), ld_x, ld_y, n, k)
+    return arr, len(steps)
+
+
+def q8_sequence_workspace_bytes(steps, m: int) -> int:
+    arr, count = _steps(steps)
+    return lib().q8_sequence_workspace_bytes(arr, count, m)
+
+
+def q8_quantize_matmul_sequence(steps, m: int, workspace, workspace_bytes: int, stream=None) -> int:
+    """steps: sequence of (x, ld_x, w, n, k, y, ld_y)."""
+    arr, count = _steps(steps)
+    return _check(lib().q8_quantize_matmul_sequence(arr, count, m, _ptr(workspace), workspace_bytes,
+                                                    _stream(stream)), "q8_quantize_matmul_sequence")
 
 
 def q8_grouped_workspace_bytes(tokens: int, topk: int, n_experts: int, n: int, k: int) -> int:

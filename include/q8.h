@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 1u
+#define Q8_ABI_VERSION 2u  /* 2: adds q8_gemv_step and the sequence entry points */
 #define Q8_BLOCK 32          /* values per block */
 #define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
 #define Q8_TILE_ROWS 64      /* rows per packed record */
@@ -122,10 +122,11 @@ int q8_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int 
 int q8_repack_weights(const void *w_rows, int64_t n, int64_t k, void *w_packed, hipStream_t stream);
 
 /* Workspace bytes q8_matmul / q8_quantize_matmul need for this shape (0 when
- * none).  Depends on (m, n, k) only.  Narrow matrices (fewer than 1024 row
- * tiles of 64) spread each tile's k over independent waves; they need a
- * workspace holding one uint32 counter per tile (first 256-byte-aligned part)
- * and the per-group partial sums.  The counters must be zero before the first
+ * none).  Depends on (m, n, k) only.  Narrow matrices with long rows (fewer
+ * than 256 row tiles of 64 and k > 2048) spread each tile's 2048-value
+ * segments over several workgroups; they need a workspace holding one uint32
+ * counter per tile (first 256-byte-aligned part) and the per-segment partial
+ * sums.  The counters must be zero before the first
  * call that uses a workspace (allocate it zero-filled); every completed call
  * leaves them zero again, so one workspace serves any sequence of calls on one
  * stream, including replays of a captured graph.  Calls that run concurrently
@@ -163,6 +164,46 @@ int q8_matmul(const void *x_q, int64_t m, const void *w, int layout, int64_t n, 
  *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_quantize_matmul(const float *x, int64_t ld_x, int64_t m, const void *w, int layout, int64_t n, int64_t k,
                        float *y, int64_t ld_y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One GEMV of a sequence: y = q8_quantize_matmul(x, ld_x, m, w,
+ * Q8_LAYOUT_PACKED, n, k, y, ld_y) with the sequence's m. */
+typedef struct {
+    const float *x; /* device fp32, m x k, row stride ld_x (ld_x >= k, ld_x % 4 == 0), 16-byte aligned */
+    const void *w;  /* device, n x k weights in Q8_LAYOUT_PACKED, 16-byte aligned */
+    float *y;       /* device fp32, m x n, row stride ld_y >= n, 16-byte aligned */
+    int64_t ld_x, ld_y, n, k;
+} q8_gemv_step;
+
+#define Q8_SEQUENCE_MAX_STEPS 72
+
+/* Workspace bytes q8_quantize_matmul_sequence needs for these steps (0 if the
+ * arguments are invalid).  Depends on the shapes and m only. */
+size_t q8_sequence_workspace_bytes(const q8_gemv_step *steps, int count, int64_t m);
+
+/* A chain of decode GEMVs in one persistent launch (launch amortization of a
+ * decode step: one launch instead of one per matrix; the "ferro" README,
+ * "Using LFM2.5", attributes the decode time beyond weight streaming to some
+ * 70 small-kernel launches per token).  Step i's output is bit-identical to q8_quantize_matmul on step i
+ * alone.  Steps run in order: step i + 1 reads its activations only after
+ * every output of step i is complete (the dependency of consecutive layers;
+ * its weight loads may start earlier, since weights do not depend on
+ * activations).  A step's x must be ready before the call: no step's y may
+ * overlap any step's x, and the y's must not overlap each other.
+ *  steps     host array of count descriptors (read during the call only),
+ *            1 <= count <= Q8_SEQUENCE_MAX_STEPS, each with n % 64 == 0 and
+ *            k % 256 == 0; 1 <= m <= 8 for all steps.
+ *  workspace device, >= q8_sequence_workspace_bytes(steps, count, m) bytes,
+ *            zero-filled before its first use; every completed call leaves
+ *            it zero except the int32 status word at byte 0, which a call
+ *            sets to Q8_ERR_LAUNCH if one of its internal waits timed out
+ *            (possible only when other work occupies the GPU and not all of
+ *            the call's workgroups can be resident; outputs are still
+ *            correct) -- clear it to reuse the flag.  Calls that run
+ *            concurrently need separate workspaces.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
+ *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes q8_grouped_matmul needs. */
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k);

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert q8.q8_abi_version() == 1
+    assert q8.q8_abi_version() == 2
     for s in range(7):
         assert q8.status_str(s).startswith("Q8_")
     assert q8.status_str(99) == "Q8_ERR_UNKNOWN"
@@ -153,6 +153,40 @@ def test_grouped_validation():
     assert call(ids=B + 2) == q8.Q8_ERR_ALIGN
 
 
+def _seq(steps, m, ws=D, wsb=1 << 30):
+    arr, count = q8._steps(steps)
+    return _raw("q8_quantize_matmul_sequence", arr, count, m, ws, wsb, None)
+
+
+def test_sequence_workspace_and_validation():
+    down = (A, 8192, B, 2048, 8192, C, 2048)
+    o = (A, 2048, B, 2048, 2048, C, 2048)
+    # status line + one 256-byte line per step counter (rounded up to 4 KB),
+    # eight 4 KB flag lines, then each split step's tile counters (256-byte
+    # aligned) and segment sums
+    head = 4096 + 8 * 4096
+    assert q8.q8_sequence_workspace_bytes([o], 1) == head
+    assert q8.q8_sequence_workspace_bytes([down], 1) == head + 256 + 4 * 1 * 2048 * 4
+    assert q8.q8_sequence_workspace_bytes([o, down, o], 2) == head + 256 + 4 * 2 * 2048 * 4
+    assert q8.q8_sequence_workspace_bytes([o] * 16, 1) == 8192 + 8 * 4096
+    assert q8.q8_sequence_workspace_bytes([], 1) == 0
+    assert q8.q8_sequence_workspace_bytes([o], 9) == 0
+    assert _seq([], 1) == q8.Q8_ERR_ARG
+    assert _seq([o], 0) == q8.Q8_ERR_ARG
+    assert _seq([(None, 2048, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_ARG
+    assert _seq([(A, 2000, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_ARG      # ld_x < k
+    assert _seq([(A, 2048, B, 2048, 2048, C, 100)], 1) == q8.Q8_ERR_ARG       # ld_y < n
+    assert _seq([o], 9) == q8.Q8_ERR_SHAPE                                     # decode rows only
+    assert _seq([o] * (q8.Q8_SEQUENCE_MAX_STEPS + 1), 1) == q8.Q8_ERR_SHAPE
+    assert _seq([o, (A, 2048, B, 2000, 2048, C, 2048)], 1) == q8.Q8_ERR_SHAPE  # n % 64
+    assert _seq([(A, 2080, B, 2048, 2080, C, 2048)], 1) == q8.Q8_ERR_SHAPE     # k % 256
+    assert _seq([(A + 4, 2048, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_ALIGN
+    assert _seq([(A, 2050, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_ALIGN
+    assert _seq([o], 1, ws=None) == q8.Q8_ERR_WORKSPACE
+    assert _seq([down], 1, wsb=1024) == q8.Q8_ERR_WORKSPACE
+    assert _seq([o], 1, ws=D + 8) == q8.Q8_ERR_ALIGN
+
+
 def _no_gpu():
     import torch
     return torch.cuda.device_count() == 0
@@ -162,3 +196,4 @@ def _no_gpu():
 def test_valid_request_without_device_reports_device_error():
     assert _raw("q8_quantize_rows", A, 64, 1, 64, 2, B, None) == q8.Q8_ERR_DEVICE
     assert _raw("q8_matmul", A, 1, B, 1, 131072, 2048, C, 131072, None, 0, None) == q8.Q8_ERR_DEVICE
+    assert _seq([(A, 2048, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_DEVICE
