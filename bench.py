@@ -574,7 +574,8 @@ def bench_moe(args):
         "hip_graph": True,
     }
     roof = hbm_roofline("q8k::grouped_gemv_kernel", float(abytes.mean()), float(ms.mean()))
-    roof["traffic"] = profiled_traffic("grouped_gemv_moe.txt", "decode_q8_amd/csrc/gemv.hip")
+    roof["traffic"] = profiled_traffic("grouped_gemv_moe.txt",
+                                       ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
     roof["note"] = "launch time includes the expert-grouping kernel that precedes the GEMV in each call"
     return base_record(args, "Q8_0 routed-expert GEMV weight GB/s (%HBM peak)", value, "GB/s", ms_per_step,
                        "int8xint8->int32, fp32 scale/sum", config, roof, cpu)
