@@ -298,13 +298,104 @@ static hipError_t launch_tiles(const int8_t *xq, const uint16_t *xs, int64_t m, 
     return hipGetLastError();
 }
 
-// Workgroup shape by problem size: 128 x 128 tiles while they give every CU a
-// workgroup, else 64 x 64 tiles (two waves; two workgroups fit a CU's LDS).
-// Each output's arithmetic is the same in both shapes, so rows stay
-// bit-identical across m.
+// Small problems: one workgroup of 8 waves owns a 32 x 64 output strip (32
+// rows, one packed weight tile) and splits k across its waves instead.  The k
+// loop runs in batches of up to 8 groups, one per wave: each wave loads its
+// group's operands straight into registers (26 16-byte loads per lane, all in
+// flight together), forms the group accumulator a_g exactly as the tiled
+// kernel does (same MFMAs, same convert / multiply / fma sequence), and parks
+// it in LDS; after a barrier the 512 threads fold the batch's a_g into their
+// outputs' running sums in group order, so every output sees the same
+// sequence of fp32 operations as in the tiled kernel and rows stay
+// bit-identical whichever kernel m selects.  Many small strips with all waves
+// busy replace few large tiles with one wave per SIMD.
+constexpr int STRIP_WAVES = 8;
+
+__global__ __launch_bounds__(512) void gemm_strip_kernel(const int8_t *__restrict__ xq,
+                                                         const uint16_t *__restrict__ xs, int64_t M,
+                                                         const uint8_t *__restrict__ w, int64_t N, int64_t K,
+                                                         float *__restrict__ y, int64_t ld_y) {
+    __shared__ float park[STRIP_WAVES][2 * 16 * 64];  // [wave][(j * 16 + r) * 64 + lane]: 64 KB
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = wave_id();
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t m0 = (int64_t)blockIdx.y * 32;
+    const int64_t T = blockIdx.x;
+    const int G = (int)(K >> 8), nb = (int)(K >> 5);
+    int64_t row = m0 + l32;
+    row = row < M ? row : M - 1;
+    const int8_t *xrow = xq + row * K + half * 16;
+    const uint16_t *xsrow = xs + row * nb;
+    const uint8_t *wt = w + T * (int64_t)G * RECORD_BYTES;
+    float acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = -0.0f;  // -0 + x == x for every x
+    for (int g0 = 0; g0 < G; g0 += STRIP_WAVES) {
+        const int g = g0 + wave;
+        if (g < G) {
+            const uint8_t *rec = wt + (int64_t)g * RECORD_BYTES;
+            // scales first: loads complete in order, so block 0 can start while the rest arrive
+            const uint4 sx = *reinterpret_cast<const uint4 *>(xsrow + g * GROUP_BLOCKS);  // the row's 8 scales
+            const uint4 sw = *reinterpret_cast<const uint4 *>(rec + RECORD_Q_BYTES + (half * 32 + l32) * 16);
+            __builtin_amdgcn_sched_barrier(0);
+            v4i a[GROUP_BLOCKS], b[GROUP_BLOCKS][2];
+#pragma unroll
+            for (int bb = 0; bb < GROUP_BLOCKS; bb++) {
+                a[bb] = *reinterpret_cast<const v4i *>(xrow + (g * GROUP_BLOCKS + bb) * QK);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    b[bb][j] = *reinterpret_cast<const v4i *>(rec + bb * 2048 + half * 1024 + (j * 32 + l32) * 16);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // all of the group's loads are in flight before the first MFMA
+            float ga[2][16];
+#pragma unroll
+            for (int bb = 0; bb < GROUP_BLOCKS; bb++) {
+                const v2u xa = {(word_of(sx, bb >> 1) >> (16 * (bb & 1))) & 0xffffu, 0u};
+                const v2u wa = {(word_of(sw, bb >> 1) >> (16 * (bb & 1))) & 0xffffu, 0u};
+                const v16i zi = {0};
+                const v32f zf = {0};
+                v16i sv[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++) sv[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[bb], b[bb][j], zi, 0, 0, 0);
+                const v32f pp = __builtin_amdgcn_mfma_f32_32x32x4f16(__builtin_bit_cast(v4h, xa),
+                                                                     __builtin_bit_cast(v4h, wa), zf, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+                        ga[j][r] = bb == 0 ? (float)sv[j][r] * pp[16 * j + r]
+                                           : __builtin_fmaf((float)sv[j][r], pp[16 * j + r], ga[j][r]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) park[wave][(j * 16 + r) * 64 + lane] = ga[j][r];
+        }
+        __syncthreads();
+        const int gn = G - g0 < STRIP_WAVES ? G - g0 : STRIP_WAVES;
+        for (int q = 0; q < gn; q++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[i] += park[q][tid + 512 * i];
+        __syncthreads();
+    }
+    // thread tid holds outputs o = tid + 512 i, o = (j * 16 + r) * 64 + lane of the MFMA layout:
+    // column j * 32 + (lane & 31), row 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int o = tid + 512 * i;
+        const int ol = o & 63, r = (o >> 6) & 15, j = o >> 10;
+        const int64_t orow = m0 + 8 * (r >> 2) + 4 * (ol >> 5) + (r & 3);
+        if (orow < M) y[orow * ld_y + T * TILE_ROWS + j * 32 + (ol & 31)] = acc[i];
+    }
+}
+
+// Kernel by problem size: 128 x 128 tiles while they give every CU a
+// workgroup, else 32 x 64 strips with k split across the waves.  Each
+// output's arithmetic is the same in both, so rows stay bit-identical across m.
 int gemm_variant(int64_t m, int64_t n) {
     const int64_t big = ((m + 127) / 128) * ((n + 127) / 128);
-    return big >= 256 ? 0 : 1;
+    return big >= 256 ? 0 : 2;
 }
 
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
@@ -312,8 +403,12 @@ hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int
     const int8_t *xq = (const int8_t *)x_q;
     const uint16_t *xs = (const uint16_t *)((const uint8_t *)x_q + m * k);
     const uint8_t *wb = (const uint8_t *)w;
-    if (gemm_variant(m, n) == 0) return launch_tiles<4, 2>(xq, xs, m, wb, n, k, y, ld_y, s);
-    return launch_tiles<2, 1>(xq, xs, m, wb, n, k, y, ld_y, s);
+    const int v = gemm_variant(m, n);
+    if (v == 0) return launch_tiles<4, 2>(xq, xs, m, wb, n, k, y, ld_y, s);
+    if (v == 1) return launch_tiles<2, 1>(xq, xs, m, wb, n, k, y, ld_y, s);
+    const dim3 grid((unsigned)(n / TILE_ROWS), (unsigned)((m + 31) / 32));
+    hipLaunchKernelGGL(gemm_strip_kernel, grid, dim3(512), 0, s, xq, xs, m, wb, n, k, y, ld_y);
+    return hipGetLastError();
 }
 
 }  // namespace q8k
