@@ -98,7 +98,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void gemv_sequence_kernel(const SeqArg
         bool ready = p == 0;
         for (int u = first; u < units; u += nwg) {
             const int T = u / st.wgs, wi = u - T * st.wgs;
-            __syncthreads();  // the previous unit's LDS reads are complete
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // previous unit's LDS reads done
             auto wait_inputs = [&]() {
                 if (!ready) {
                     if (threadIdx.x == 0) wait_flag(step_flag(a, wg % FLAG_LINES, p - 1), status);
@@ -108,7 +108,9 @@ __global__ __launch_bounds__(SEQ_THREADS) void gemv_sequence_kernel(const SeqArg
             tile_unit<M, 1, float, ONE>(st.x, st.ld_x, nullptr, st.w, st.n, st.k, st.y, st.ld_y, T, wi, st.wgs,
                                         st.segs, ctr, part, lds_u, &last_wg, wait_inputs);
             ready = true;
-            __syncthreads();  // every wave of the unit is done
+            // every wave of the unit is done (its LDS work complete); its output
+            // stores may still be in flight: nothing in the launch reads them
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             if (threadIdx.x < 64) {  // wave 0: count the unit in; the last one raises the step's flags
                 uint32_t old = 0;
                 if (threadIdx.x == 0)
