@@ -62,8 +62,9 @@ def lib() -> ctypes.CDLL:
         L.q8ref_matmul.argtypes = [P, I64, P, I64, I64, P, I64, P, I]
         L.q8ref_matmul_points.argtypes = [P, I64, P, I64, I64, P, P, I64, P, P]
         L.q8ref_grouped_matmul.argtypes = [P, I64, I, P, I64, I, P, I64, I64, I64, I64, P, P, I]
+        L.q8ref_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, ctypes.c_float, P, P]
         for name in ("q8ref_quantize_rows", "q8ref_pack", "q8ref_unpack", "q8ref_block_terms",
-                     "q8ref_matmul", "q8ref_matmul_points", "q8ref_grouped_matmul"):
+                     "q8ref_matmul", "q8ref_matmul_points", "q8ref_grouped_matmul", "q8ref_rmsnorm_quantize"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -118,6 +119,23 @@ def quantize_rows(x: np.ndarray, layout: int = LAYOUT_ACT) -> np.ndarray:
     out = np.empty(quantized_bytes(rows, k), dtype=np.uint8)
     _check(lib().q8ref_quantize_rows(_p(x), ld, rows, k, layout, _p(out)), "quantize_rows")
     return out
+
+
+def rmsnorm_quantize(x: np.ndarray, res_in: np.ndarray, w: np.ndarray, eps: float):
+    """Fused residual + RMSNorm + Q8_0 quantization (q8ref_rmsnorm_quantize):
+    fp32 [rows][k] x and residual, fp32 [k] weight -> (new residual fp32
+    [rows][k], ACT buffer of the normalized rows)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, k = x.shape
+    r = np.ascontiguousarray(res_in, dtype=np.float32).reshape(rows, k)
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(k)
+    res_out = np.empty((rows, k), dtype=np.float32)
+    q = np.empty(quantized_bytes(rows, k), dtype=np.uint8)
+    _check(lib().q8ref_rmsnorm_quantize(_p(x), _p(r), _p(w), rows, k, float(eps), _p(res_out), _p(q)),
+           "rmsnorm_quantize")
+    return res_out, q
 
 
 def act_planes(buf: np.ndarray, rows: int, k: int):

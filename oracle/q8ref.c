@@ -133,6 +133,51 @@ int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* fused residual + RMSNorm + quantization ("ferro" README, item 3)          */
+/* ------------------------------------------------------------------------ */
+
+int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, int64_t rows, int64_t k, float eps,
+                           float *res_out, uint8_t *q_out) {
+    if (!x || !res_in || !w || !res_out || !q_out || rows < 0 || k <= 0) return Q8REF_EARG;
+    if (k % QK) return Q8REF_ESHAPE;
+    int64_t nb = k / QK;
+    float *h = malloc(sizeof(float) * (size_t)k);
+    float *n = malloc(sizeof(float) * (size_t)k);
+    if (!h || !n) {
+        free(h);
+        free(n);
+        return Q8REF_EARG;
+    }
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t j = 0; j < k; j++) h[j] = res_in[r * k + j] + x[r * k + j];
+        /* the defined fp64 summation order: 256 strided partials, then the halving tree */
+        double p[256];
+        for (int t = 0; t < 256; t++) {
+            p[t] = 0.0;
+            for (int64_t j = t; j < k; j += 256) p[t] += (double)h[j] * (double)h[j];
+        }
+        for (int stride = 128; stride >= 1; stride /= 2)
+            for (int t = 0; t < stride; t++) p[t] += p[t + stride];
+        const double mean = p[0] / (double)k;
+        const float rs = (float)(1.0 / sqrt(mean + (double)eps));
+        for (int64_t j = 0; j < k; j++) {
+            const float hr = h[j] * rs;
+            n[j] = hr * w[j];
+        }
+        for (int64_t j = 0; j < k; j++) res_out[r * k + j] = h[j];
+        for (int64_t b = 0; b < nb; b++) {
+            int8_t q[QK];
+            uint16_t d = q8ref_quantize_block(n + b * QK, q, NULL);
+            memcpy(q_out + r * k + b * QK, q, QK);
+            put16(q_out + rows * k + (r * nb + b) * 2, d);
+        }
+    }
+    free(h);
+    free(n);
+    return Q8REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* packed layout                                                            */
 /* ------------------------------------------------------------------------ */
 

@@ -68,6 +68,25 @@ uint16_t q8ref_quantize_block(const float *x, int8_t *q, float *d_out);
 /* rows x k fp32 (row stride ld_x elements) -> layout 0 (ROWS) or 2 (ACT). */
 int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int layout, uint8_t *out);
 
+/* Fused producer: residual add + RMSNorm + Q8_0 quantization of each row
+ * ("ferro" README, "How the iGPU path is fast", item 3: residual + norm +
+ * int8 quantization in one pass, emitting the next GEMM's int8 input).  The
+ * pages name the fusion but not the norm's formula or precision; the reading
+ * taken (Llama's RMSNorm):
+ *   h_j   = fp32(res_in_j + x_j)                     (written to res_out)
+ *   ss    = sum_j (double)h_j^2 in a fixed order: partial p_t = sum over
+ *           j = t, t + 256, t + 512, ... (< k) in increasing j, for
+ *           t = 0..255; then for stride 128, 64, ..., 1: p_t += p_{t+stride}
+ *           for t < stride; ss = p_0 (every h_j^2 is exact in fp64; the
+ *           order only fixes the fp64 roundings of the sum)
+ *   r     = fp32(1.0 / sqrt(ss / k + eps)), all in correctly rounded fp64
+ *   n_j   = fp32(fp32(h_j * r) * w_j)
+ * and n is quantized per 32-value block as q8ref_quantize_block does, into
+ * the ACT layout.  res_out may equal res_in.  Returns Q8REF_OK, Q8REF_EARG or
+ * Q8REF_ESHAPE (k % 32). */
+int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, int64_t rows, int64_t k, float eps,
+                           float *res_out, uint8_t *q_out);
+
 /* ROWS <-> PACKED byte permutations. */
 int q8ref_pack(const uint8_t *w_rows, int64_t n, int64_t k, uint8_t *w_packed);
 int q8ref_unpack(const uint8_t *w_packed, int64_t n, int64_t k, uint8_t *w_rows);
