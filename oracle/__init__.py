@@ -123,17 +123,18 @@ def quantize_rows(x: np.ndarray, layout: int = LAYOUT_ACT) -> np.ndarray:
 
 def rmsnorm_quantize(x: np.ndarray, res_in: np.ndarray, w: np.ndarray, eps: float):
     """Fused residual + RMSNorm + Q8_0 quantization (q8ref_rmsnorm_quantize):
-    fp32 [rows][k] x and residual, fp32 [k] weight -> (new residual fp32
-    [rows][k], ACT buffer of the normalized rows)."""
+    fp32 [rows][k] x and residual (None: no residual add), fp32 [k] weight ->
+    (new residual fp32 [rows][k], ACT buffer of the normalized rows)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     if x.ndim == 1:
         x = x[None, :]
     rows, k = x.shape
-    r = np.ascontiguousarray(res_in, dtype=np.float32).reshape(rows, k)
+    r = None if res_in is None else np.ascontiguousarray(res_in, dtype=np.float32).reshape(rows, k)
     w = np.ascontiguousarray(w, dtype=np.float32).reshape(k)
     res_out = np.empty((rows, k), dtype=np.float32)
     q = np.empty(quantized_bytes(rows, k), dtype=np.uint8)
-    _check(lib().q8ref_rmsnorm_quantize(_p(x), _p(r), _p(w), rows, k, float(eps), _p(res_out), _p(q)),
+    _check(lib().q8ref_rmsnorm_quantize(_p(x), None if r is None else _p(r), _p(w), rows, k, float(eps),
+                                        _p(res_out), _p(q)),
            "rmsnorm_quantize")
     return res_out, q
 

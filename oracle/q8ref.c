@@ -138,7 +138,7 @@ int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, i
 
 int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, int64_t rows, int64_t k, float eps,
                            float *res_out, uint8_t *q_out) {
-    if (!x || !res_in || !w || !res_out || !q_out || rows < 0 || k <= 0) return Q8REF_EARG;
+    if (!x || !w || !q_out || rows < 0 || k <= 0) return Q8REF_EARG;
     if (k % QK) return Q8REF_ESHAPE;
     int64_t nb = k / QK;
     float *h = malloc(sizeof(float) * (size_t)k);
@@ -149,14 +149,15 @@ int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, 
         return Q8REF_EARG;
     }
     for (int64_t r = 0; r < rows; r++) {
-        for (int64_t j = 0; j < k; j++) h[j] = res_in[r * k + j] + x[r * k + j];
-        /* the defined fp64 summation order: 256 strided partials, then the halving tree */
-        double p[256];
-        for (int t = 0; t < 256; t++) {
+        for (int64_t j = 0; j < k; j++) h[j] = res_in ? res_in[r * k + j] + x[r * k + j] : x[r * k + j];
+        /* the defined fp64 summation order: 512 partials over 4-value chunks, then the halving tree */
+        double p[512];
+        for (int t = 0; t < 512; t++) {
             p[t] = 0.0;
-            for (int64_t j = t; j < k; j += 256) p[t] += (double)h[j] * (double)h[j];
+            for (int64_t j0 = 4 * (int64_t)t; j0 < k; j0 += 2048)
+                for (int c = 0; c < 4; c++) p[t] += (double)h[j0 + c] * (double)h[j0 + c];
         }
-        for (int stride = 128; stride >= 1; stride /= 2)
+        for (int stride = 256; stride >= 1; stride /= 2)
             for (int t = 0; t < stride; t++) p[t] += p[t + stride];
         const double mean = p[0] / (double)k;
         const float rs = (float)(1.0 / sqrt(mean + (double)eps));
@@ -164,7 +165,8 @@ int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, 
             const float hr = h[j] * rs;
             n[j] = hr * w[j];
         }
-        for (int64_t j = 0; j < k; j++) res_out[r * k + j] = h[j];
+        if (res_out)
+            for (int64_t j = 0; j < k; j++) res_out[r * k + j] = h[j];
         for (int64_t b = 0; b < nb; b++) {
             int8_t q[QK];
             uint16_t d = q8ref_quantize_block(n + b * QK, q, NULL);

@@ -73,16 +73,19 @@ int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, i
  * int8 quantization in one pass, emitting the next GEMM's int8 input).  The
  * pages name the fusion but not the norm's formula or precision; the reading
  * taken (Llama's RMSNorm):
- *   h_j   = fp32(res_in_j + x_j)                     (written to res_out)
- *   ss    = sum_j (double)h_j^2 in a fixed order: partial p_t = sum over
- *           j = t, t + 256, t + 512, ... (< k) in increasing j, for
- *           t = 0..255; then for stride 128, 64, ..., 1: p_t += p_{t+stride}
- *           for t < stride; ss = p_0 (every h_j^2 is exact in fp64; the
- *           order only fixes the fp64 roundings of the sum)
+ *   h_j   = fp32(res_in_j + x_j), or x_j when res_in is NULL (a norm with
+ *           no residual add, as before a model's first layer); written to
+ *           res_out unless res_out is NULL
+ *   ss    = sum_j (double)h_j^2 in a fixed order: partial p_t = sum of the
+ *           j whose 4-value chunk index floor(j / 4) is t mod 512, in
+ *           increasing j, for t = 0..511; then for stride 256, 128, ..., 1:
+ *           p_t += p_{t+stride} for t < stride; ss = p_0 (every h_j^2 is
+ *           exact in fp64; the order only fixes the fp64 roundings of the
+ *           sum)
  *   r     = fp32(1.0 / sqrt(ss / k + eps)), all in correctly rounded fp64
  *   n_j   = fp32(fp32(h_j * r) * w_j)
  * and n is quantized per 32-value block as q8ref_quantize_block does, into
- * the ACT layout.  res_out may equal res_in.  Returns Q8REF_OK, Q8REF_EARG or
+ * the ACT layout.  res_out may be the same buffer as res_in or x.  Returns Q8REF_OK, Q8REF_EARG or
  * Q8REF_ESHAPE (k % 32). */
 int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, int64_t rows, int64_t k, float eps,
                            float *res_out, uint8_t *q_out);

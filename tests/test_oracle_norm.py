@@ -136,3 +136,12 @@ def test_residual_in_place_and_bad_shape():
     with pytest.raises(ValueError):
         oracle.rmsnorm_quantize(np.zeros((1, 40), np.float32), np.zeros((1, 40), np.float32),
                                 np.ones(40, np.float32), EPS)
+
+
+def test_no_residual_equals_zero_residual():
+    """Without a residual the normalized row is that of x itself: identical to
+    passing an all-zero residual (fp32 0 + x == x exactly)."""
+    x, _, w = _case(3, 2048, 9)
+    ro0, q0 = oracle.rmsnorm_quantize(x, None, w, EPS)
+    ro1, q1 = oracle.rmsnorm_quantize(x, np.zeros_like(x), w, EPS)
+    assert np.array_equal(q0, q1) and np.array_equal(ro0, x) and np.array_equal(ro1, x)
