@@ -18,8 +18,9 @@ Other workloads (same JSON line format): ``single`` (one 2048x2048 GEMV),
 ``batched`` (the decode step with ``--m`` rows per GEMV), ``prefill`` (the
 int8-MFMA GEMM at M in {188, 752, 2048} x (N, K) in {(2048, 2048),
 (8192, 2048), (2048, 8192)}), ``moe`` (routed-expert GEMVs: 256 experts,
-16 tokens, top-8; gate, up and down), ``copy`` (a device copy of 1 GiB, used
-to calibrate rocprofv3's byte counters).
+16 tokens, top-8; gate, up and down), ``norm`` (the fused residual + RMSNorm +
+Q8_0 quantize producer at the prefill row counts, hidden 2048), ``copy`` (a
+device copy of 1 GiB, used to calibrate rocprofv3's byte counters).
 
 The JSON line carries the metric, the roofline of the dominant kernel (its
 average launch duration measured with HIP events on the stream it runs on)
@@ -49,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "single", "batched", "prefill", "moe", "copy"])
+                    choices=["decode", "single", "batched", "prefill", "moe", "norm", "copy"])
     ap.add_argument("--m", type=int, default=1, help="rows per GEMV for --workload batched")
     ap.add_argument("--unfused", action="store_true", help="decode: separate quantize and GEMV launches")
     ap.add_argument("--per-matrix", action="store_true",
@@ -582,6 +583,101 @@ def bench_moe(args):
 
 
 # --------------------------------------------------------------------------
+# fused residual + RMSNorm + quantization producer
+# --------------------------------------------------------------------------
+
+def norm_bytes(rows: int, k: int) -> int:
+    """Algorithmic HBM bytes of one q8_rmsnorm_quantize launch: x, residual in
+    and residual out (fp32), the int8 codes and fp16 scales, the fp32 gain."""
+    return rows * k * (4 + 4 + 4 + 1) + rows * (k // 32) * 2 + 4 * k
+
+
+def bench_norm(args):
+    import torch
+
+    import oracle
+    import workloads as wl
+    from decode_q8_amd import q8
+    dev = torch.device("cuda", 0)
+    k = wl.LLAMA_HIDDEN
+    cases = []
+    for rows in wl.NORM_ROWS:
+        x, res, gain = wl.norm_inputs(wl.NORM, rows, rows, k)
+        c = dict(rows=rows, k=k, x=x, res=res, gain=gain, xt=torch.from_numpy(x).to(dev),
+                 rt=torch.from_numpy(res).to(dev), gt=torch.from_numpy(gain).to(dev),
+                 ro=torch.empty((rows, k), dtype=torch.float32, device=dev),
+                 q=torch.empty(q8.q8_quantized_bytes(rows, k), dtype=torch.uint8, device=dev))
+        cases.append(c)
+    torch.cuda.synchronize()
+    # the producer is checked against the oracle before it is timed (full rows)
+    for c in cases:
+        q8.q8_rmsnorm_quantize(c["xt"], c["rt"], c["ro"], c["gt"], c["rows"], k, wl.NORM_EPS, c["q"])
+        ro_ref, q_ref = oracle.rmsnorm_quantize(c["x"], c["res"], c["gain"], wl.NORM_EPS)
+        torch.cuda.synchronize()
+        assert np.array_equal(c["q"].cpu().numpy(), q_ref), f"rows={c['rows']}: codes differ from the oracle"
+        assert np.array_equal(c["ro"].cpu().numpy().view(np.uint32), ro_ref.view(np.uint32))
+    stream = torch.cuda.Stream()
+    timed = cases[1:]  # the prefill launches; the decode row (cases[0]) is latency only
+    assert cases[0]["rows"] == 1 and all(c["rows"] > 1 for c in timed)
+    nbytes = np.array([norm_bytes(c["rows"], k) for c in timed], dtype=np.float64)
+    # Every timed pass works on its own copy of the buffers, enough copies that
+    # their footprint (>= 1 GiB) exceeds the GPU's caches (4 MB L2 per XCD,
+    # 256 MB Infinity Cache): each launch reads its inputs from HBM, as a
+    # producer reading a freshly written residual stream of a large model would
+    # at worst.
+    copies = max(2, int(np.ceil((1 << 30) / nbytes.sum())))
+    sets = [[dict(c, xt=c["xt"].clone(), rt=c["rt"].clone(), ro=torch.empty_like(c["ro"]),
+                  q=torch.empty_like(c["q"])) for c in cases] for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def run_cases(sel):
+        def run(s, timers=None):
+            for i, c in enumerate(sel):
+                if timers is not None:
+                    timers[i].start()
+                q8.q8_rmsnorm_quantize(c["xt"], c["rt"], c["ro"], c["gt"], c["rows"], k, wl.NORM_EPS, c["q"],
+                                       s.cuda_stream)
+                if timers is not None:
+                    timers[i].stop()
+        return run
+
+    # a step: the three prefill launches; one graph holds a step on every copy
+    ms_all, graph = graph_time(run_cases([c for st in sets for c in st if c["rows"] > 1]), stream, args.steps,
+                               args.warmup)
+    ms_per_step = ms_all / copies
+    # per-launch durations: one launch size over every copy, back to back in a
+    # graph of its own (a launch of a few microseconds is shorter than the
+    # overhead of an event pair around it)
+    ms = np.array([graph_time(run_cases([st[i + 1] for st in sets]), stream, args.steps, 2)[0] / copies
+                   for i in range(len(timed))])
+    ms_row1 = graph_time(run_cases([st[0] for st in sets]), stream, args.steps, 2)[0] / copies
+    value = nbytes.sum() / (ms_per_step * 1e-3) / 1e9
+    big = int(np.argmax(nbytes))
+    cpu = None
+    if not args.no_cpu_baseline:
+        c = timed[big]
+        sec, reps = timed_repeat(lambda: oracle.rmsnorm_quantize(c["x"], c["res"], c["gain"], wl.NORM_EPS),
+                                 min_seconds=3.0)
+        cpu = {"value": round(norm_bytes(c["rows"], k) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": f"the {c['rows']}-row launch, {reps} repetitions, single-threaded"}
+    config = {
+        "workload": f"fused residual + RMSNorm + Q8_0 quantize: rows in {{188, 752, 2048}} x hidden {k} "
+                    "(Llama-3.2-1B prefill tokens), residual stream with 1% outlier channels x20",
+        "bytes_per_step": int(nbytes.sum()),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "GBs_by_rows": {str(c["rows"]): round(nbytes[i] / (ms[i] * 1e-3) / 1e9, 1) for i, c in enumerate(timed)},
+        "decode_row_launch_us": round(float(ms_row1) * 1e3, 3),
+        "buffer_copies": copies,
+        "hip_graph": True,
+    }
+    roof = hbm_roofline("q8k::rmsnorm_quantize_kernel", float(nbytes[big]), float(ms[big]))
+    roof["traffic"] = profiled_traffic("rmsnorm_quantize_prefill.txt", "decode_q8_amd/csrc/norm.hip")
+    roof["note"] = f"the {timed[big]['rows']}-row launch (the largest of the step)"
+    return base_record(args, "fused residual+RMSNorm+Q8_0 quantize HBM GB/s (%HBM peak)", value, "GB/s",
+                       ms_per_step, "f32 (fp64 sum of squares), int8 out", config, roof, cpu)
+
+
+# --------------------------------------------------------------------------
 
 def bench_copy(args):
     """1 GiB device-to-device copy: known bytes for calibrating byte counters."""
@@ -608,7 +704,7 @@ def main():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
     fn = {"decode": bench_decode, "batched": bench_decode, "single": bench_single, "prefill": bench_prefill,
-          "moe": bench_moe, "copy": bench_copy}[args.workload]
+          "moe": bench_moe, "norm": bench_norm, "copy": bench_copy}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
 

@@ -29,9 +29,11 @@ from .q8 import (  # noqa: F401
     q8_quantize_rows,
     q8_quantized_bytes,
     q8_repack_weights,
+    q8_rmsnorm_quantize,
     q8_status_str,
     quantize,
     quantize_matmul,
     repack,
+    rmsnorm_quantize,
     workspace,
 )

@@ -22,6 +22,13 @@ std::atomic<int8_t> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Do [a, a + na) and [b, b + nb) share a byte?  (NULL never overlaps.)
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
 int check_device() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return Q8_ERR_DEVICE;
@@ -163,6 +170,28 @@ int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m,
     const int dev = check_device();
     if (dev != Q8_OK) return dev;
     return launched(q8k::launch_gemv_sequence(hs, count, m, workspace, stream));
+}
+
+int q8_rmsnorm_quantize(const float *x, const float *residual_in, float *residual_out, const float *weight,
+                        int64_t rows, int64_t k, float eps, void *q_out, hipStream_t stream) {
+    if (!x || !weight || !q_out || rows < 0 || k <= 0) return Q8_ERR_ARG;
+    if (!(eps >= 0.0f) || eps > 3.4e38f) return Q8_ERR_ARG;  // rejects NaN, negatives and infinity
+    if (k % Q8_BLOCK || k > q8k::NORM_MAX_K || rows > INT32_MAX) return Q8_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(weight) || !aligned16(q_out) || !aligned16(residual_in) ||
+        !aligned16(residual_out))
+        return Q8_ERR_ALIGN;
+    if (rows == 0) return Q8_OK;
+    // aliasing: residual_out may coincide exactly with x or residual_in; no other overlap
+    const size_t fb = (size_t)rows * (size_t)k * 4, qb = q8_quantized_bytes(rows, k);
+    if (overlap(q_out, qb, x, fb) || overlap(q_out, qb, residual_in, fb) || overlap(q_out, qb, residual_out, fb) ||
+        overlap(q_out, qb, weight, (size_t)k * 4))
+        return Q8_ERR_ARG;
+    if (residual_out && residual_out != x && overlap(residual_out, fb, x, fb)) return Q8_ERR_ARG;
+    if (residual_out && residual_out != residual_in && overlap(residual_out, fb, residual_in, fb)) return Q8_ERR_ARG;
+    if (residual_out && overlap(residual_out, fb, weight, (size_t)k * 4)) return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_rmsnorm_quantize(x, residual_in, residual_out, weight, rows, k, eps, q_out, stream));
 }
 
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k) {

@@ -46,6 +46,11 @@ struct SeqHostStep {
 size_t gemv_sequence_workspace_bytes(const SeqHostStep *steps, int count, int64_t m);
 hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, void *workspace, hipStream_t s);
 
+// Residual add + RMSNorm + quantization to Q8_LAYOUT_ACT (k <= 16384).
+constexpr int64_t NORM_MAX_K = 16384;
+hipError_t launch_rmsnorm_quantize(const float *x, const float *res_in, float *res_out, const float *w,
+                                   int64_t rows, int64_t k, float eps, void *q_out, hipStream_t s);
+
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s);
 

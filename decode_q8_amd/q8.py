@@ -22,6 +22,8 @@ Q8_BLOCK_BYTES = 34
 Q8_TILE_ROWS = 64
 Q8_GEMV_MAX_ROWS = 8
 Q8_SEQUENCE_MAX_STEPS = 72
+Q8_ABI_VERSION = 3
+Q8_NORM_MAX_K = 16384
 
 
 class q8_gemv_step(ctypes.Structure):
@@ -42,6 +44,7 @@ SIGNATURES = {
     "q8_quantize_matmul": ([_P, _I64, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
     "q8_sequence_workspace_bytes": ([_P, _I, _I64], _SZ),
     "q8_quantize_matmul_sequence": ([_P, _I, _I64, _P, _SZ, _P], _I),
+    "q8_rmsnorm_quantize": ([_P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P], _I),
     "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
     "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
 }
@@ -161,6 +164,12 @@ def q8_quantize_matmul(x, ld_x: int, m: int, w, layout: int, n: int, k: int, y, 
                                            workspace_bytes, _stream(stream)), "q8_quantize_matmul")
 
 
+def q8_rmsnorm_quantize(x, residual_in, residual_out, weight, rows: int, k: int, eps: float, q_out,
+                        stream=None) -> int:
+    return _check(lib().q8_rmsnorm_quantize(_ptr(x), _ptr(residual_in), _ptr(residual_out), _ptr(weight), rows, k,
+                                            float(eps), _ptr(q_out), _stream(stream)), "q8_rmsnorm_quantize")
+
+
 def q8_grouped_matmul(x_q, x_rows: int, x_per_pair: int, topk_ids, tokens: int, topk: int, w_experts,
                       n_experts: int, expert_stride_bytes: int, n: int, k: int, y, workspace, workspace_bytes: int,
                       stream=None) -> int:
@@ -216,3 +225,17 @@ def matmul(x_q, m: int, w, layout: int, n: int, k: int, ws=None, stream=None):
         ws = workspace(m, n, k, w.device)
     q8_matmul(x_q, m, w, layout, n, k, y, n, ws, 0 if ws is None else ws.numel(), stream)
     return y
+
+
+def rmsnorm_quantize(x, residual, weight, eps: float, residual_out="in_place", stream=None):
+    """fp32 [rows][k] CUDA tensors -> new uint8 Q8_LAYOUT_ACT tensor of the
+    normalized rows.  residual (or None) is updated in place to residual + x
+    unless residual_out names another tensor (or None: not stored)."""
+    import torch
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.is_contiguous()
+    rows, k = x.shape
+    if isinstance(residual_out, str):
+        residual_out = residual
+    out = torch.empty(q8_quantized_bytes(rows, k), dtype=torch.uint8, device=x.device)
+    q8_rmsnorm_quantize(x, residual, residual_out, weight, rows, k, eps, out, stream)
+    return out

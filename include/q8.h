@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 2u  /* 2: adds q8_gemv_step and the sequence entry points */
+#define Q8_ABI_VERSION 3u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize */
 #define Q8_BLOCK 32          /* values per block */
 #define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
 #define Q8_TILE_ROWS 64      /* rows per packed record */
@@ -204,6 +204,34 @@ size_t q8_sequence_workspace_bytes(const q8_gemv_step *steps, int count, int64_t
  *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/* Fused producer of a GEMM input: residual add + RMSNorm + quantization of
+ * each row to Q8_LAYOUT_ACT in one pass ("ferro" README, "How the iGPU path
+ * is fast", item 3: residual add, norm and int8 quantization fused, the
+ * producer emitting the next matmul's int8 input).  The pages name the fusion
+ * but not the norm; this is Llama's RMSNorm, per row:
+ *   h_j = fp32(residual_in_j + x_j)   (h_j = x_j when residual_in is NULL)
+ *   ss  = sum_j (double)h_j^2 in a fixed order: partial p_t (t = 0..511)
+ *         sums the j with floor(j / 4) == t mod 512 in increasing j, then
+ *         p_t += p_{t+s} for t < s, s = 256, 128, ..., 1; ss = p_0
+ *   r   = fp32(1 / sqrt(ss / k + eps)), each fp64 operation correctly rounded
+ *   n_j = fp32(fp32(h_j * r) * weight_j)
+ * then n is quantized per 32-value block exactly as q8_quantize_rows does.
+ * Codes, scales and h are deterministic (bit-identical for any rows count).
+ *  x            device fp32 [rows][k] (row stride k), 16-byte aligned.
+ *  residual_in  device fp32 [rows][k] or NULL (a norm without residual add).
+ *  residual_out device fp32 [rows][k] receiving h, or NULL; may be the same
+ *               buffer as x or residual_in (in-place update of the residual
+ *               stream), otherwise must not overlap them.
+ *  weight       device fp32 [k], the norm's per-channel gain.
+ *  eps          >= 0 and finite.
+ *  q_out        device, q8_quantized_bytes(rows, k) bytes (Q8_LAYOUT_ACT, the
+ *               input of q8_matmul); must not overlap the other buffers.
+ *  k % 32 == 0, k <= 16384; 0 <= rows <= 2^31 - 1 (rows == 0: no launch).
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE,
+ *  Q8_ERR_LAUNCH. */
+int q8_rmsnorm_quantize(const float *x, const float *residual_in, float *residual_out, const float *weight,
+                        int64_t rows, int64_t k, float eps, void *q_out, hipStream_t stream);
 
 /* Workspace bytes q8_grouped_matmul needs. */
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k);

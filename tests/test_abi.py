@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert q8.q8_abi_version() == 2
+    m = re.search(r"#define Q8_ABI_VERSION (\d+)u", open(HEADER).read())
+    assert int(m.group(1)) == q8.Q8_ABI_VERSION == q8.q8_abi_version() == 3
     for s in range(7):
         assert q8.status_str(s).startswith("Q8_")
     assert q8.status_str(99) == "Q8_ERR_UNKNOWN"
@@ -187,6 +188,30 @@ def test_sequence_workspace_and_validation():
     assert _seq([o], 1, ws=D + 8) == q8.Q8_ERR_ALIGN
 
 
+def test_rmsnorm_quantize_validation():
+    f = "q8_rmsnorm_quantize"
+    E = 0x7F0000400000
+    assert _raw(f, None, B, B, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, B, None, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, B, C, 1, 2048, 1e-5, None, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, B, C, -1, 2048, 1e-5, D, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, B, C, 1, 0, 1e-5, D, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, B, C, 1, 2048, -1e-5, D, None) == q8.Q8_ERR_ARG      # eps < 0
+    assert _raw(f, A, B, B, C, 1, 2048, float("nan"), D, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, B, C, 1, 2048, float("inf"), D, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, B, C, 1, 2040, 1e-5, D, None) == q8.Q8_ERR_SHAPE     # k % 32
+    assert _raw(f, A, B, B, C, 1, q8.Q8_NORM_MAX_K + 32, 1e-5, D, None) == q8.Q8_ERR_SHAPE
+    assert _raw(f, A, B, B, C, 2 ** 31, 2048, 1e-5, D, None) == q8.Q8_ERR_SHAPE
+    assert _raw(f, A + 4, B, B, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, B + 8, B, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, B, B, C, 1, 2048, 1e-5, D + 4, None) == q8.Q8_ERR_ALIGN
+    # q_out overlapping an input, residual_out partially overlapping x
+    assert _raw(f, A, B, B, C, 1, 2048, 1e-5, A + 4096, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, A + 16, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, B, E, C, 1, 2048, 1e-5, C + 16, None) == q8.Q8_ERR_ARG  # q_out over the weight
+    assert _raw(f, A, B, B, C, 0, 2048, 1e-5, D, None) == q8.Q8_OK            # no rows: no launch
+
+
 def _no_gpu():
     import torch
     return torch.cuda.device_count() == 0
@@ -197,3 +222,5 @@ def test_valid_request_without_device_reports_device_error():
     assert _raw("q8_quantize_rows", A, 64, 1, 64, 2, B, None) == q8.Q8_ERR_DEVICE
     assert _raw("q8_matmul", A, 1, B, 1, 131072, 2048, C, 131072, None, 0, None) == q8.Q8_ERR_DEVICE
     assert _seq([(A, 2048, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_DEVICE
+    assert _raw("q8_rmsnorm_quantize", A, B, B, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_DEVICE
+    assert _raw("q8_rmsnorm_quantize", A, None, A, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_DEVICE  # in place on x

@@ -18,6 +18,10 @@ Recipe (every tensor is independent of every other one):
   * routing: uniform(0, 1) logits [tokens x experts]; each token takes the
     top-k experts by logit (ties go to the lower expert id), slots ordered by
     descending logit.
+  * norm (the fused residual + RMSNorm + quantize producer): the residual
+    stream N(0, 1) with the prefill outlier recipe (round(0.01 * K) channels
+    x 20), the layer output added to it N(0, 1), the per-channel gain
+    1 + 0.1 * N(0, 1);
   * base seed of workload i is 20261202 + i.
 
 Shapes (out x in = N x K):
@@ -32,6 +36,8 @@ Shapes (out x in = N x K):
     (2048, 8192)}.
   * moe:     256 experts, gate and up [2048x7168], down [7168x2048]; 16 tokens,
     top-8 routing, token rows [16x7168], down inputs [128x2048].
+  * norm:    rows in {1, 188, 752, 2048} (decode and prefill tokens) x hidden
+    2048 (Llama-3.2-1B), plus hidden 7168 (the MoE model).
 """
 from __future__ import annotations
 
@@ -52,9 +58,10 @@ TAG_ACT = 2
 TAG_ROUTE = 3
 TAG_PERM = 4
 TAG_OUTLIER = 5
+TAG_GAIN = 6
 
 # Workload indices (offsets from BASE_SEED).
-SINGLE, DECODE, BATCHED, PREFILL, MOE = 0, 1, 2, 3, 4
+SINGLE, DECODE, BATCHED, PREFILL, MOE, NORM = 0, 1, 2, 3, 4, 5
 
 LLAMA_HIDDEN = 2048
 LLAMA_LAYERS = 16
@@ -81,6 +88,9 @@ MOE_TOKENS = 16
 MOE_TOPK = 8
 # (name, N, K) of one expert's matrices.
 MOE_MATS = (("gate", MOE_FFN, MOE_HIDDEN), ("up", MOE_FFN, MOE_HIDDEN), ("down", MOE_HIDDEN, MOE_FFN))
+
+NORM_ROWS = (1, 188, 752, 2048)
+NORM_EPS = 1e-5
 
 
 def generator(workload: int, tag: tuple) -> np.random.Generator:
@@ -115,6 +125,16 @@ def outlier_channels(workload: int, index: int, k: int, group: int = 0) -> np.nd
     count = int(round(OUTLIER_FRACTION * k))
     g = generator(workload, (TAG_OUTLIER, group, index))
     return np.sort(g.choice(k, size=count, replace=False))
+
+
+def norm_inputs(workload: int, index: int, rows: int, k: int):
+    """(x, residual, gain) for the residual + RMSNorm + quantize producer:
+    fp32 [rows][k] layer output N(0, 1), fp32 [rows][k] residual stream N(0, 1)
+    with outlier channels, fp32 [k] gain 1 + 0.1 * N(0, 1)."""
+    x = activation(workload, 2 * index, rows, k)
+    res = activation(workload, 2 * index + 1, rows, k, outliers=True)
+    gain = np.float32(1.0) + normal(workload, (TAG_GAIN, 0, index), (k,), 0.1)
+    return x, res, gain.astype(np.float32)
 
 
 def routing(workload: int, tokens: int, n_experts: int, topk: int, group: int = 0) -> np.ndarray:
