@@ -63,8 +63,14 @@ def lib() -> ctypes.CDLL:
         L.q8ref_matmul_points.argtypes = [P, I64, P, I64, I64, P, P, I64, P, P]
         L.q8ref_grouped_matmul.argtypes = [P, I64, I, P, I64, I, P, I64, I64, I64, I64, P, P, I]
         L.q8ref_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, ctypes.c_float, P, P]
+        L.q8ref_exp_nonpos.argtypes = [ctypes.c_double]
+        L.q8ref_exp_nonpos.restype = ctypes.c_double
+        L.q8ref_moe_route.argtypes = [P, I64, I64, I, I, P, P]
+        L.q8ref_swiglu_quantize.argtypes = [P, I64, P, I64, I64, I64, P]
+        L.q8ref_moe_combine.argtypes = [P, I64, P, I64, I, I64, P, P]
         for name in ("q8ref_quantize_rows", "q8ref_pack", "q8ref_unpack", "q8ref_block_terms",
-                     "q8ref_matmul", "q8ref_matmul_points", "q8ref_grouped_matmul", "q8ref_rmsnorm_quantize"):
+                     "q8ref_matmul", "q8ref_matmul_points", "q8ref_grouped_matmul", "q8ref_rmsnorm_quantize",
+                     "q8ref_moe_route", "q8ref_swiglu_quantize", "q8ref_moe_combine"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,6 +143,45 @@ def rmsnorm_quantize(x: np.ndarray, res_in: np.ndarray, w: np.ndarray, eps: floa
                                         _p(res_out), _p(q)),
            "rmsnorm_quantize")
     return res_out, q
+
+
+def exp_nonpos(x: float) -> float:
+    """e^x for x <= 0 by the fixed fp64 algorithm (q8ref_exp_nonpos)."""
+    return lib().q8ref_exp_nonpos(float(x))
+
+
+def moe_route(logits: np.ndarray, topk: int, normalize: bool = True):
+    """fp32 [tokens][experts] router logits -> (int32 ids [tokens][topk], fp32 weights [tokens][topk])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    tokens, E = logits.shape
+    ids = np.empty((tokens, topk), np.int32)
+    w = np.empty((tokens, topk), np.float32)
+    _check(lib().q8ref_moe_route(_p(logits), tokens, E, int(topk), int(bool(normalize)), _p(ids), _p(w)), "moe_route")
+    return ids, w
+
+
+def swiglu_quantize(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """fp32 [rows][n] gate and up -> ACT buffer of silu(gate) * up."""
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    up = np.ascontiguousarray(up, dtype=np.float32)
+    rows, n = gate.shape
+    assert up.shape == (rows, n)
+    q = np.empty(quantized_bytes(rows, n), np.uint8)
+    _check(lib().q8ref_swiglu_quantize(_p(gate), n, _p(up), n, rows, n, _p(q)), "swiglu_quantize")
+    return q
+
+
+def moe_combine(y: np.ndarray, w: np.ndarray):
+    """fp32 y [tokens*topk][n] and weights [tokens][topk] -> (fp32 out [tokens][n], fp64 S [tokens][n])."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    tokens, topk = w.shape
+    n = y.shape[1]
+    assert y.shape[0] == tokens * topk
+    out = np.empty((tokens, n), np.float32)
+    S = np.empty((tokens, n), np.float64)
+    _check(lib().q8ref_moe_combine(_p(y), n, _p(w), tokens, topk, n, _p(out), _p(S)), "moe_combine")
+    return out, S
 
 
 def act_planes(buf: np.ndarray, rows: int, k: int):

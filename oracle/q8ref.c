@@ -357,3 +357,103 @@ int q8ref_grouped_matmul(const uint8_t *x_act, int64_t x_rows, int x_per_pair, c
     free(one);
     return Q8REF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* around the routed experts: exp, router, SwiGLU, combine                  */
+/* ------------------------------------------------------------------------ */
+
+double q8ref_exp_nonpos(double x) {
+    if (x < -745.5) return 0.0;
+    /* C1: ln 2 truncated to a multiple of 2^-32; C2: the rest, rounded */
+    const double inv_ln2 = 0x1.71547652b82fep+0, C1 = 0x1.62e42fee00000p-1, C2 = 0x1.a39ef35793c76p-33;
+    const double kd = rint(x * inv_ln2);
+    const double r = (x - kd * C1) - kd * C2;
+    double fact = 1.0;
+    double c[14];
+    for (int i = 0; i < 14; i++) {
+        if (i > 0) fact *= (double)i; /* i! is exact in fp64 for i <= 22 */
+        c[i] = 1.0 / fact;
+    }
+    double p = c[13];
+    for (int i = 12; i >= 0; i--) p = p * r + c[i];
+    return ldexp(p, (int)kd);
+}
+
+int q8ref_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int topk, int normalize, int32_t *ids,
+                    float *weights) {
+    if (!logits || !ids || !weights || tokens < 0 || n_experts <= 0 || topk < 1 || topk > n_experts)
+        return Q8REF_EARG;
+    char *taken = malloc((size_t)n_experts);
+    if (!taken) return Q8REF_EARG;
+    for (int64_t t = 0; t < tokens; t++) {
+        const float *l = logits + t * n_experts;
+        memset(taken, 0, (size_t)n_experts);
+        /* selection: repeatedly the largest remaining logit, ties to the lower id */
+        for (int j = 0; j < topk; j++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < n_experts; e++)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+            taken[best] = 1;
+            ids[t * topk + j] = (int32_t)best;
+        }
+        const double m = (double)l[ids[t * topk]];
+        double D = 0.0;
+        if (normalize) {
+            for (int j = 0; j < topk; j++) D += q8ref_exp_nonpos((double)l[ids[t * topk + j]] - m);
+        } else {
+            double P[64];
+            for (int i = 0; i < 64; i++) {
+                P[i] = 0.0;
+                for (int64_t e = i; e < n_experts; e += 64) P[i] += q8ref_exp_nonpos((double)l[e] - m);
+            }
+            for (int s = 32; s >= 1; s /= 2)
+                for (int i = 0; i < s; i++) P[i] += P[i + s];
+            D = P[0];
+        }
+        for (int j = 0; j < topk; j++)
+            weights[t * topk + j] = (float)(q8ref_exp_nonpos((double)l[ids[t * topk + j]] - m) / D);
+    }
+    free(taken);
+    return Q8REF_OK;
+}
+
+int q8ref_swiglu_quantize(const float *gate, int64_t ld_gate, const float *up, int64_t ld_up, int64_t rows, int64_t n,
+                          uint8_t *q_out) {
+    if (!gate || !up || !q_out || rows < 0 || n <= 0 || ld_gate < n || ld_up < n) return Q8REF_EARG;
+    if (n % QK) return Q8REF_ESHAPE;
+    const int64_t nb = n / QK;
+    float h[QK];
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            for (int j = 0; j < QK; j++) {
+                const double g = (double)gate[r * ld_gate + b * QK + j];
+                const double u = (double)up[r * ld_up + b * QK + j];
+                const double e = q8ref_exp_nonpos(-fabs(g));
+                const double s = g >= 0.0 ? g / (1.0 + e) : (g * e) / (1.0 + e);
+                h[j] = (float)(s * u);
+            }
+            int8_t q[QK];
+            const uint16_t d = q8ref_quantize_block(h, q, NULL);
+            memcpy(q_out + r * n + b * QK, q, QK);
+            put16(q_out + rows * n + (r * nb + b) * 2, d);
+        }
+    }
+    return Q8REF_OK;
+}
+
+int q8ref_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t tokens, int topk, int64_t n, float *out,
+                      double *Sc) {
+    if (!y || !w || !out || tokens < 0 || topk < 1 || n <= 0 || ld_y < n) return Q8REF_EARG;
+    for (int64_t t = 0; t < tokens; t++)
+        for (int64_t c = 0; c < n; c++) {
+            double acc = 0.0, S = 0.0;
+            for (int j = 0; j < topk; j++) {
+                const double v = (double)w[t * topk + j] * (double)y[(t * topk + j) * ld_y + c];
+                acc += v;
+                S += fabs(v);
+            }
+            out[t * n + c] = (float)acc;
+            if (Sc) Sc[t * n + c] = S;
+        }
+    return Q8REF_OK;
+}

@@ -114,6 +114,55 @@ int q8ref_grouped_matmul(const uint8_t *x_act, int64_t x_rows, int x_per_pair, c
                          int64_t tokens, int topk, const uint8_t *w_rows, int64_t n_experts,
                          int64_t expert_stride, int64_t n, int64_t k, float *y, double *S, int threads);
 
+/* ---- around the routed experts: router, SwiGLU, weighted combine ---------
+ * The pages name device routing, the real router's expert ids and weights,
+ * and a sparse-MoE layer ("Ferrule" README: completed foundation, "device
+ * routing"; runtime decision: the real router determines expert ids and
+ * weights; status table: an OLMoE sparse-MoE path), without formulas.  The
+ * readings taken (Mixtral/DeepSeek/OLMoE-style MoE):
+ *  - exp is evaluated by one fixed fp64 algorithm for x <= 0, so that both
+ *    sides reach the same fp32 results where they decide integer codes and
+ *    expert weights (q8ref_exp_nonpos below);
+ *  - top-k: the k largest logits, ties to the lower expert id, slots in
+ *    descending logit order (ties ascending id);
+ *  - weights: softmax, either over the k selected logits (normalize = 1) or
+ *    over all experts, keeping the selected ones (normalize = 0);
+ *  - SwiGLU: h = silu(gate) * up, silu(g) = g / (1 + e^-g);
+ *  - combine: out_t = sum_j w_tj * y_(t*topk+j). */
+
+/* e^x for x <= 0 (x < -745.5 gives +0), fp64: k = rint(x * fp64(1/ln2));
+ * r = (x - k*C1) - k*C2 with C1 = ln2 truncated to a multiple of 2^-32 (k*C1
+ * is exact) and C2 = fp64(ln2 - C1); p = Horner evaluation of
+ * sum_{i=0..13} r^i / i! (coefficients fp64(1 / i!), each step one multiply
+ * and one add, no fused operations); result ldexp(p, k).  Truncation error
+ * below 1e-17 relative; a few fp64 ulps in all. */
+double q8ref_exp_nonpos(double x);
+
+/* Router: logits fp32 [tokens][n_experts] -> ids int32 [tokens][topk] and
+ * weights fp32 [tokens][topk].  With m = the largest logit of the token and
+ * e_i = q8ref_exp_nonpos((double)l_i - (double)m):
+ *   normalize = 1: D = sum of e over the selected experts in slot order
+ *   normalize = 0: D = sum of e over all experts in a fixed order: partial
+ *                  P_l = sum of e_i over i = l, l + 64, ... ascending, for
+ *                  l = 0..63, then P_l += P_{l+s} for l < s, s = 32..1
+ *   w_j = fp32(e_{id_j} / D).
+ * Returns Q8REF_OK or Q8REF_EARG (sizes, topk outside 1..n_experts). */
+int q8ref_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int topk, int normalize, int32_t *ids,
+                    float *weights);
+
+/* SwiGLU + quantization: gate, up fp32 [rows][n] (row strides ld_gate,
+ * ld_up) -> ACT buffer of h [rows][n]:
+ *   e = q8ref_exp_nonpos(-|g|); s = g >= 0 ? g / (1 + e) : (g * e) / (1 + e)
+ *   (fp64, the same value as g / (1 + e^-g) up to rounding);
+ *   h = fp32(s * (double)u); then the block quantizer.  n % 32 == 0. */
+int q8ref_swiglu_quantize(const float *gate, int64_t ld_gate, const float *up, int64_t ld_up, int64_t rows, int64_t n,
+                          uint8_t *q_out);
+
+/* Weighted combine: out[t][c] = sum_j w[t][j] * y[t*topk + j][c] accumulated
+ * in fp64, rounded once; Sc (may be NULL) receives sum_j |w[t][j] * y[..][c]|. */
+int q8ref_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t tokens, int topk, int64_t n, float *out,
+                      double *Sc);
+
 #ifdef __cplusplus
 }
 #endif
