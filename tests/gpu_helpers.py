@@ -33,6 +33,26 @@ def quantize(x: np.ndarray, layout: int) -> torch.Tensor:
     return q8.quantize(xt, layout)
 
 
+def ref_quantize(a: np.ndarray, layout: int) -> np.ndarray:
+    """The oracle's own quantization of host fp32 rows (expected values and
+    oracle inputs never come from the GPU); large inputs split over threads
+    by row ranges."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    a = np.ascontiguousarray(a, np.float32)
+    rows, k = a.shape
+    if rows * k < (1 << 22):
+        return oracle.quantize_rows(a, layout)
+    step = (rows + 7) // 8
+    parts = list(ThreadPoolExecutor(8).map(lambda r0: oracle.quantize_rows(a[r0:r0 + step], layout),
+                                           range(0, rows, step)))
+    if layout == oracle.LAYOUT_ROWS:
+        return np.concatenate(parts)
+    codes = np.concatenate([p[: p.size // 34 * 32] for p in parts])
+    scales = np.concatenate([p[p.size // 34 * 32:] for p in parts])
+    return np.concatenate([codes, scales])
+
+
 def weights_packed(w: np.ndarray):
     """Host fp32 [n][k] -> (rows-layout device buffer, packed device buffer)."""
     n, k = w.shape

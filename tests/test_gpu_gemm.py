@@ -6,7 +6,7 @@ import pytest
 import oracle
 import workloads as wl
 from decode_q8_amd import q8
-from tests.gpu_helpers import bits_equal, check_tol, down, quantize, require_gpu, weights_packed
+from tests.gpu_helpers import bits_equal, check_tol, down, quantize, ref_quantize, require_gpu, weights_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,8 @@ def test_parity(m, n, k):
     w = wl.weight(wl.PREFILL, 50 + n, n, k)
     xq = quantize(x, q8.Q8_LAYOUT_ACT)
     wr, wp = weights_packed(w)
-    y_ref, S = oracle.matmul(down(xq), m, down(wr), n, k, threads=8)
+    y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                             threads=8)
     check_tol(_gemm(xq, m, wp, n, k), y_ref, S, f"gemm m={m} n={n} k={k}")
 
 
@@ -71,5 +72,6 @@ def test_prefill_full_size_sampled(m, n, k):
     ni = rng.integers(0, n, 1024)
     mi[:4] = [0, m - 1, 0, m - 1]
     ni[:4] = [0, n - 1, n - 1, 0]
-    y_ref, S = oracle.matmul_points(down(xq), m, down(wr), n, k, mi, ni)
+    y_ref, S = oracle.matmul_points(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                                    mi, ni)
     check_tol(y[mi, ni], y_ref, S, f"prefill m={m} n={n} k={k}")

@@ -9,7 +9,7 @@ import torch
 import oracle
 import workloads as wl
 from decode_q8_amd import q8
-from tests.gpu_helpers import bits_equal, check_tol, down, quantize, require_gpu, up, weights_packed
+from tests.gpu_helpers import bits_equal, check_tol, down, quantize, ref_quantize, require_gpu, up, weights_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,8 @@ def test_parity_packed_and_rows(m, n, k):
     x, w = _case(m, n, k, seed=n + m)
     xq = quantize(x, q8.Q8_LAYOUT_ACT)
     wr, wp = weights_packed(w)
-    y_ref, S = oracle.matmul(down(xq), m, down(wr), n, k, threads=8)
+    y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                             threads=8)
     yp = _gemv(xq, m, wp, q8.Q8_LAYOUT_PACKED, n, k)
     check_tol(yp, y_ref, S, f"packed m={m} n={n} k={k}")
     yr = _gemv(xq, m, wr, q8.Q8_LAYOUT_ROWS, n, k)
@@ -52,7 +53,7 @@ def test_rows_layout_ragged_n(n, k):
     x, w = _case(3, n, k, seed=n)
     xq = quantize(x, q8.Q8_LAYOUT_ACT)
     wr = quantize(w, q8.Q8_LAYOUT_ROWS)
-    y_ref, S = oracle.matmul(down(xq), 3, down(wr), n, k)
+    y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), 3, ref_quantize(w, oracle.LAYOUT_ROWS), n, k)
     check_tol(_gemv(xq, 3, wr, q8.Q8_LAYOUT_ROWS, n, k), y_ref, S, f"rows n={n}")
 
 
@@ -96,7 +97,8 @@ def test_long_rows_wide_matrix_m8():
     y = _gemv(xq, m, wp, 1, n, k)
     rng = np.random.default_rng(21)
     mi, ni = rng.integers(0, m, 2048), rng.integers(0, n, 2048)
-    y_ref, S = oracle.matmul_points(down(xq), m, down(wr), n, k, mi, ni)
+    y_ref, S = oracle.matmul_points(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                                    mi, ni)
     check_tol(y[mi, ni], y_ref, S, "m=8 k=8448")
     for i in (0, 5):
         yi = _gemv(quantize(x[i:i + 1], q8.Q8_LAYOUT_ACT), 1, wp, 1, n, k)
@@ -156,7 +158,8 @@ def test_single_gemv_full_size():
     x = wl.activation(wl.SINGLE, 0, 1, k)
     xq = quantize(x, q8.Q8_LAYOUT_ACT)
     wr, wp = weights_packed(w)
-    y_ref, S = oracle.matmul(down(xq), 1, down(wr), n, k, threads=8)
+    y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), 1, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                             threads=8)
     yp = _gemv(xq, 1, wp, 1, n, k)
     check_tol(yp, y_ref, S, "single 2048x2048")
     assert bits_equal(yp, _gemv(xq, 1, wr, 0, n, k))
@@ -170,7 +173,7 @@ def test_decode_shapes_full_size_sampled(name, n, k):
     w = wl.weight(wl.BATCHED, 1000 + n + k, n, k)
     x = wl.activation(wl.BATCHED, 1000 + n + k, 8, k)
     wr, wp = weights_packed(w)
-    wr_h = down(wr)
+    wr_h = ref_quantize(w, oracle.LAYOUT_ROWS)
     rng = np.random.default_rng(n + k)
     y1 = None
     for m in (1, 8):
@@ -178,7 +181,7 @@ def test_decode_shapes_full_size_sampled(name, n, k):
         y = _gemv(xq, m, wp, 1, n, k)
         mi = rng.integers(0, m, 512)
         ni = rng.integers(0, n, 512)
-        y_ref, S = oracle.matmul_points(down(xq), m, wr_h, n, k, mi, ni)
+        y_ref, S = oracle.matmul_points(ref_quantize(x[:m], oracle.LAYOUT_ACT), m, wr_h, n, k, mi, ni)
         check_tol(y[mi, ni], y_ref, S, f"{name} m={m}")
         if m == 1:
             y1 = y

@@ -8,7 +8,7 @@ import torch
 import oracle
 import workloads as wl
 from decode_q8_amd import q8
-from tests.gpu_helpers import bits_equal, check_tol, down, quantize, require_gpu, up
+from tests.gpu_helpers import bits_equal, check_tol, down, quantize, ref_quantize, require_gpu, up
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,7 @@ def _gpu():
 
 def _experts(E, n, k, seed, only=None):
     """Packed experts laid out back to back; returns (device buffer, stride,
-    rows-layout device buffers of the generated experts)."""
+    the oracle's own row-contiguous quantization of each generated expert)."""
     stride = q8.q8_quantized_bytes(n, k)
     buf = torch.zeros(E * stride, dtype=torch.uint8, device="cuda")
     rows = {}
@@ -30,7 +30,7 @@ def _experts(E, n, k, seed, only=None):
         w = wl.weight(wl.MOE, e, n, k, group=seed)
         wr = quantize(w, q8.Q8_LAYOUT_ROWS)
         q8.q8_repack_weights(wr, n, k, buf[e * stride:(e + 1) * stride])
-        rows[e] = wr
+        rows[e] = ref_quantize(w, oracle.LAYOUT_ROWS)
     return buf, stride, rows
 
 
@@ -55,8 +55,9 @@ def test_parity_and_single_gemv_equality(tokens, topk, E, n, k, per_pair):
     buf, stride, wrows = _experts(E, n, k, seed=tokens)
     y, status = _grouped(xq, rows, per_pair, ids, E, buf, stride, n, k)
     assert status == 0
-    w_all = np.concatenate([down(wrows[e]) for e in range(E)])
-    y_ref, S = oracle.grouped_matmul(down(xq), rows, per_pair, ids, w_all, E, stride, n, k, threads=8)
+    w_all = np.concatenate([wrows[e] for e in range(E)])
+    y_ref, S = oracle.grouped_matmul(ref_quantize(x, oracle.LAYOUT_ACT), rows, per_pair, ids, w_all, E, stride, n, k,
+                                     threads=8)
     check_tol(y, y_ref, S, "grouped")
     for t in range(tokens):
         for j in range(topk):
@@ -104,7 +105,7 @@ def test_moe_full_size_sampled(mat):
         one = oracle.quantize_rows(x[xr:xr + 1], oracle.LAYOUT_ACT)
         assert np.array_equal(one, np.concatenate([xq_h[xr * k:(xr + 1) * k],
                                                    xq_h[rows * k + xr * (k // 32) * 2:rows * k + (xr + 1) * (k // 32) * 2]]))
-        y_ref, S = oracle.matmul(one, 1, down(wrows[e]), n, k, threads=8)
+        y_ref, S = oracle.matmul(one, 1, wrows[e], n, k, threads=8)
         check_tol(y[p:p + 1], y_ref, S, f"moe {name} pair {p}")
     for p in range(T * K8):
         t, j = divmod(p, K8)

@@ -9,7 +9,7 @@ import torch
 import oracle
 import workloads as wl
 from decode_q8_amd import q8
-from tests.gpu_helpers import bits_equal, check_tol, dev, down, require_gpu, up, weights_packed
+from tests.gpu_helpers import bits_equal, check_tol, dev, down, ref_quantize, require_gpu, up, weights_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -123,9 +123,9 @@ def test_codes_feed_the_gemv():
     xt, rt, gt = up(x), up(res), up(gain)
     qt = q8.rmsnorm_quantize(xt, rt, gt, EPS)
     w = wl.weight(wl.NORM, 55, n, k)
-    wr, wp = weights_packed(w)
+    _, wp = weights_packed(w)
     y = down(q8.matmul(qt, rows, wp, q8.Q8_LAYOUT_PACKED, n, k))
     _, q_ref = oracle.rmsnorm_quantize(x, res, gain, EPS)
-    y_ref, S = oracle.matmul(q_ref, rows, down(wr), n, k)
+    y_ref, S = oracle.matmul(q_ref, rows, ref_quantize(w, oracle.LAYOUT_ROWS), n, k)
     check_tol(y, y_ref, S, "norm -> GEMV")
     assert bits_equal(down(rt), (res + x).astype(np.float32))

@@ -6,7 +6,7 @@ import pytest
 import oracle
 import workloads as wl
 from decode_q8_amd import q8
-from tests.gpu_helpers import down, quantize, require_gpu
+from tests.gpu_helpers import down, quantize, ref_quantize, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -21,9 +21,8 @@ def test_repack_matches_oracle(n, k):
     w = wl.weight(wl.SINGLE, 100 + n, n, k)
     wr = quantize(w, q8.Q8_LAYOUT_ROWS)
     wp = q8.repack(wr, n, k)
-    rows = down(wr)
+    rows_ref = ref_quantize(w, oracle.LAYOUT_ROWS)
+    assert np.array_equal(down(wr), rows_ref)
     got = down(wp)
-    assert got.size == rows.size == n * k // 32 * 34
-    ref = oracle.pack(rows, n, k)
-    assert np.array_equal(got, ref)
-    assert np.array_equal(oracle.unpack(got, n, k), rows)
+    assert got.size == rows_ref.size == n * k // 32 * 34
+    assert np.array_equal(got, oracle.pack(rows_ref, n, k))

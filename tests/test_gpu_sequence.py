@@ -10,7 +10,7 @@ import torch
 import oracle
 import workloads as wl
 from decode_q8_amd import q8
-from tests.gpu_helpers import bits_equal, check_tol, dev, down, quantize, require_gpu, up, weights_packed
+from tests.gpu_helpers import bits_equal, check_tol, dev, down, ref_quantize, require_gpu, up, weights_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -26,10 +26,10 @@ def _chain(shapes, m, seed):
     steps = []
     for i, (n, k) in enumerate(shapes):
         w = wl.weight(wl.BATCHED, seed + 7 * i, n, k)
-        wr, wp = weights_packed(w)
-        x = up(wl.activation(wl.BATCHED, seed + 7 * i + 1, m, k))
+        _, wp = weights_packed(w)
+        xh = wl.activation(wl.BATCHED, seed + 7 * i + 1, m, k)
         y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev())
-        steps.append(dict(n=n, k=k, w=wp, wr=wr, x=x, y=y))
+        steps.append(dict(n=n, k=k, w=wp, w_host=w, x_host=xh, x=up(xh), y=y))
     return steps
 
 
@@ -66,10 +66,10 @@ def test_decode_layers_bit_identical_to_single_launches(m):
         y = down(s["y"])
         assert bits_equal(y, _single(s, m)), f"step {i} ({s['n']}x{s['k']}) differs from its own launch"
         if i in (0, 3, len(steps) - 1):
-            xq = down(quantize(down(s["x"]), q8.Q8_LAYOUT_ACT))
             mi = rng.integers(0, m, 256)
             ni = rng.integers(0, s["n"], 256)
-            y_ref, S = oracle.matmul_points(xq, m, down(s["wr"]), s["n"], s["k"], mi, ni)
+            y_ref, S = oracle.matmul_points(ref_quantize(s["x_host"], oracle.LAYOUT_ACT), m,
+                                            ref_quantize(s["w_host"], oracle.LAYOUT_ROWS), s["n"], s["k"], mi, ni)
             check_tol(y[mi, ni], y_ref, S, f"sequence step {i} m={m}")
 
 
