@@ -14,6 +14,8 @@
 #include "launch.hpp"
 
 static_assert(Q8_SEQUENCE_MAX_STEPS == q8k::SEQ_MAX_STEPS, "sequence length limit");
+static_assert(Q8_ROUTE_MAX_EXPERTS == q8k::ROUTE_MAX_EXPERTS && Q8_ROUTE_MAX_TOPK == q8k::ROUTE_MAX_TOPK,
+              "router limits");
 
 namespace {
 
@@ -192,6 +194,51 @@ int q8_rmsnorm_quantize(const float *x, const float *residual_in, float *residua
     const int dev = check_device();
     if (dev != Q8_OK) return dev;
     return launched(q8k::launch_rmsnorm_quantize(x, residual_in, residual_out, weight, rows, k, eps, q_out, stream));
+}
+
+int q8_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int topk, int normalize, int32_t *ids,
+                 float *weights, hipStream_t stream) {
+    if (!logits || !ids || !weights || tokens < 0 || n_experts <= 0 || topk < 1) return Q8_ERR_ARG;
+    if (topk > n_experts || n_experts > Q8_ROUTE_MAX_EXPERTS || topk > Q8_ROUTE_MAX_TOPK || tokens > INT32_MAX)
+        return Q8_ERR_SHAPE;
+    if (((uintptr_t)logits & 3u) || ((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u)) return Q8_ERR_ALIGN;
+    if (tokens == 0) return Q8_OK;
+    const size_t pb = (size_t)tokens * (size_t)topk * 4;
+    if (overlap(ids, pb, weights, pb) || overlap(ids, pb, logits, (size_t)tokens * (size_t)n_experts * 4) ||
+        overlap(weights, pb, logits, (size_t)tokens * (size_t)n_experts * 4))
+        return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_moe_route(logits, tokens, n_experts, topk, normalize ? 1 : 0, ids, weights, stream));
+}
+
+int q8_swiglu_quantize(const float *gate, int64_t ld_gate, const float *up, int64_t ld_up, int64_t rows, int64_t n,
+                       void *q_out, hipStream_t stream) {
+    if (!gate || !up || !q_out || rows < 0 || n <= 0 || ld_gate < n || ld_up < n) return Q8_ERR_ARG;
+    if (n % Q8_BLOCK) return Q8_ERR_SHAPE;
+    if (!aligned16(gate) || !aligned16(up) || !aligned16(q_out) || ld_gate % 4 || ld_up % 4) return Q8_ERR_ALIGN;
+    if (rows == 0) return Q8_OK;
+    const size_t qb = q8_quantized_bytes(rows, n);
+    if (overlap(q_out, qb, gate, (size_t)((rows - 1) * ld_gate + n) * 4) ||
+        overlap(q_out, qb, up, (size_t)((rows - 1) * ld_up + n) * 4))
+        return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_swiglu_quantize(gate, ld_gate, up, ld_up, rows, n, q_out, stream));
+}
+
+int q8_moe_combine(const float *y, int64_t ld_y, const float *weights, int64_t tokens, int topk, int64_t n, float *out,
+                   int64_t ld_out, hipStream_t stream) {
+    if (!y || !weights || !out || tokens < 0 || topk < 1 || n <= 0 || ld_y < n || ld_out < n) return Q8_ERR_ARG;
+    if (n % 4) return Q8_ERR_SHAPE;
+    if (!aligned16(y) || !aligned16(out) || ((uintptr_t)weights & 3u) || ld_y % 4 || ld_out % 4) return Q8_ERR_ALIGN;
+    if (tokens == 0) return Q8_OK;
+    if (overlap(out, (size_t)((tokens - 1) * ld_out + n) * 4, y, (size_t)((tokens * topk - 1) * ld_y + n) * 4) ||
+        overlap(out, (size_t)((tokens - 1) * ld_out + n) * 4, weights, (size_t)tokens * (size_t)topk * 4))
+        return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_moe_combine(y, ld_y, weights, tokens, topk, n, out, ld_out, stream));
 }
 
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k) {

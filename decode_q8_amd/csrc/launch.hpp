@@ -51,6 +51,16 @@ constexpr int64_t NORM_MAX_K = 16384;
 hipError_t launch_rmsnorm_quantize(const float *x, const float *res_in, float *res_out, const float *w,
                                    int64_t rows, int64_t k, float eps, void *q_out, hipStream_t s);
 
+// Around the routed experts: router, SwiGLU + quantization, weighted combine.
+constexpr int ROUTE_MAX_EXPERTS = 1024;
+constexpr int ROUTE_MAX_TOPK = 32;
+hipError_t launch_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int topk, int normalize,
+                            int32_t *ids, float *weights, hipStream_t s);
+hipError_t launch_swiglu_quantize(const float *gate, int64_t ld_gate, const float *up, int64_t ld_up, int64_t rows,
+                                  int64_t n, void *q_out, hipStream_t s);
+hipError_t launch_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t tokens, int topk, int64_t n,
+                              float *out, int64_t ld_out, hipStream_t s);
+
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s);
 

@@ -24,6 +24,8 @@ Q8_GEMV_MAX_ROWS = 8
 Q8_SEQUENCE_MAX_STEPS = 72
 Q8_ABI_VERSION = 3
 Q8_NORM_MAX_K = 16384
+Q8_ROUTE_MAX_EXPERTS = 1024
+Q8_ROUTE_MAX_TOPK = 32
 
 
 class q8_gemv_step(ctypes.Structure):
@@ -45,6 +47,9 @@ SIGNATURES = {
     "q8_sequence_workspace_bytes": ([_P, _I, _I64], _SZ),
     "q8_quantize_matmul_sequence": ([_P, _I, _I64, _P, _SZ, _P], _I),
     "q8_rmsnorm_quantize": ([_P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P], _I),
+    "q8_moe_route": ([_P, _I64, _I64, _I, _I, _P, _P, _P], _I),
+    "q8_swiglu_quantize": ([_P, _I64, _P, _I64, _I64, _I64, _P, _P], _I),
+    "q8_moe_combine": ([_P, _I64, _P, _I64, _I, _I64, _P, _I64, _P], _I),
     "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
     "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
 }
@@ -168,6 +173,21 @@ def q8_rmsnorm_quantize(x, residual_in, residual_out, weight, rows: int, k: int,
                         stream=None) -> int:
     return _check(lib().q8_rmsnorm_quantize(_ptr(x), _ptr(residual_in), _ptr(residual_out), _ptr(weight), rows, k,
                                             float(eps), _ptr(q_out), _stream(stream)), "q8_rmsnorm_quantize")
+
+
+def q8_moe_route(logits, tokens: int, n_experts: int, topk: int, normalize: bool, ids, weights, stream=None) -> int:
+    return _check(lib().q8_moe_route(_ptr(logits), tokens, n_experts, topk, int(bool(normalize)), _ptr(ids),
+                                     _ptr(weights), _stream(stream)), "q8_moe_route")
+
+
+def q8_swiglu_quantize(gate, ld_gate: int, up, ld_up: int, rows: int, n: int, q_out, stream=None) -> int:
+    return _check(lib().q8_swiglu_quantize(_ptr(gate), ld_gate, _ptr(up), ld_up, rows, n, _ptr(q_out),
+                                           _stream(stream)), "q8_swiglu_quantize")
+
+
+def q8_moe_combine(y, ld_y: int, weights, tokens: int, topk: int, n: int, out, ld_out: int, stream=None) -> int:
+    return _check(lib().q8_moe_combine(_ptr(y), ld_y, _ptr(weights), tokens, topk, n, _ptr(out), ld_out,
+                                       _stream(stream)), "q8_moe_combine")
 
 
 def q8_grouped_matmul(x_q, x_rows: int, x_per_pair: int, topk_ids, tokens: int, topk: int, w_experts,

@@ -71,7 +71,8 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 3u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize */
+#define Q8_ABI_VERSION 3u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize and the
+                              MoE router, SwiGLU and combine entry points */
 #define Q8_BLOCK 32          /* values per block */
 #define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
 #define Q8_TILE_ROWS 64      /* rows per packed record */
@@ -261,6 +262,67 @@ size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, i
 int q8_grouped_matmul(const void *x_q, int64_t x_rows, int x_per_pair, const int32_t *topk_ids, int64_t tokens,
                       int topk, const void *w_experts, int64_t n_experts, int64_t expert_stride_bytes, int64_t n,
                       int64_t k, float *y, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- The steps either side of the routed-expert GEMVs ("Ferrule" README:
+ * device routing; the real router decides expert ids and weights; a sparse-MoE
+ * execution path).  A mixture-of-experts layer on a token batch is
+ *   q8_moe_route -> q8_grouped_matmul (gate||up, x_per_pair = 0)
+ *   -> q8_swiglu_quantize -> q8_grouped_matmul (down, x_per_pair = 1)
+ *   -> q8_moe_combine.
+ * The pages give no formulas; these are Mixtral/DeepSeek/OLMoE-style readings.
+ * Wherever a result is an integer or is reproduced bit for bit (expert ids,
+ * weights, SwiGLU codes), e^x (x <= 0) is one fixed fp64 algorithm of
+ * correctly rounded basic operations:
+ *   k = rint(x * fp64(1/ln 2)), r = (x - k*C1) - k*C2 (C1 = ln 2 truncated to
+ *   a multiple of 2^-32, C2 = fp64(ln 2 - C1)), p = Horner sum of r^i / i!
+ *   for i = 13..0 with coefficients fp64(1/i!), one multiply and one add per
+ *   step; e^x = ldexp(p, k); x < -745.5 gives +0. */
+
+#define Q8_ROUTE_MAX_EXPERTS 1024
+#define Q8_ROUTE_MAX_TOPK 32
+
+/* Router: top-k experts per token and their weights.
+ *  logits   device fp32 [tokens][n_experts] (finite values; NaN is outside
+ *           the contract), 4-byte aligned.
+ *  ids      device int32 [tokens][topk]: the k largest logits, ties to the
+ *           lower expert id, slots in descending logit order.
+ *  weights  device fp32 [tokens][topk]: with m the largest logit and
+ *           e_i = exp((double)l_i - m):
+ *             normalize != 0: w_j = fp32(e_j / D), D = sum of the selected
+ *               e in slot order (softmax over the selected experts);
+ *             normalize == 0: D = sum over all experts, as 64 partials (experts
+ *               l, l + 64, ... ascending, l = 0..63) folded P_l += P_{l+s},
+ *               s = 32..1 (softmax over all experts, selected ones kept).
+ *  1 <= topk <= min(n_experts, 32), n_experts <= 1024, tokens >= 0.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int topk, int normalize, int32_t *ids,
+                 float *weights, hipStream_t stream);
+
+/* SwiGLU between the gate/up and the down GEMVs, quantized for the down GEMV:
+ *   s = g / (1 + e^-g) evaluated in fp64 as (e = exp(-|g|))
+ *       g >= 0 ? g / (1 + e) : (g * e) / (1 + e),
+ *   h = fp32(s * (double)u), quantized per 32-value block as
+ *   q8_quantize_rows does, into Q8_LAYOUT_ACT.
+ *  gate, up  device fp32 [rows][n], row strides ld_gate, ld_up (>= n, % 4),
+ *            16-byte aligned (gate and up may be the two halves of one
+ *            fused gate||up output row).
+ *  q_out     device, q8_quantized_bytes(rows, n), 16-byte aligned, no overlap.
+ *  n % 32 == 0; rows == 0 is a no-op.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_swiglu_quantize(const float *gate, int64_t ld_gate, const float *up, int64_t ld_up, int64_t rows, int64_t n,
+                       void *q_out, hipStream_t stream);
+
+/* Weighted combine of the routed outputs:
+ *   out[t][c] = sum_j weights[t][j] * y[t*topk + j][c]
+ * in fp32, j ascending, each product and each sum rounded (so within
+ * 2 * topk * 2^-24 * sum_j |w y| of the exact value).
+ *  y        device fp32 [tokens*topk][n], row stride ld_y.
+ *  weights  device fp32 [tokens][topk].
+ *  out      device fp32 [tokens][n], row stride ld_out; must not overlap y.
+ *  n % 4 == 0, ld_y and ld_out >= n and % 4 == 0, y and out 16-byte aligned.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_moe_combine(const float *y, int64_t ld_y, const float *weights, int64_t tokens, int topk, int64_t n, float *out,
+                   int64_t ld_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

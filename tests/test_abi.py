@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -212,6 +212,48 @@ def test_rmsnorm_quantize_validation():
     assert _raw(f, A, B, B, C, 0, 2048, 1e-5, D, None) == q8.Q8_OK            # no rows: no launch
 
 
+def test_moe_route_validation():
+    f = "q8_moe_route"
+    assert _raw(f, None, 16, 256, 8, 1, B, C, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 16, 256, 8, 1, None, C, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 16, 256, 8, 1, B, None, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, -1, 256, 8, 1, B, C, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 16, 0, 1, 1, B, C, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 16, 256, 0, 1, B, C, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 16, 4, 8, 1, B, C, None) == q8.Q8_ERR_SHAPE          # topk > n_experts
+    assert _raw(f, A, 16, 2048, 8, 1, B, C, None) == q8.Q8_ERR_SHAPE       # n_experts > 1024
+    assert _raw(f, A, 16, 256, 33, 1, B, C, None) == q8.Q8_ERR_SHAPE       # topk > 32
+    assert _raw(f, A + 2, 16, 256, 8, 1, B, C, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 16, 256, 8, 1, B + 2, C, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 16, 256, 8, 1, B, B + 64, None) == q8.Q8_ERR_ARG     # ids and weights overlap
+    assert _raw(f, A, 0, 256, 8, 1, B, C, None) == q8.Q8_OK                # no tokens: no launch
+
+
+def test_swiglu_validation():
+    f = "q8_swiglu_quantize"
+    assert _raw(f, None, 4096, B, 4096, 128, 2048, C, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 4096, B, 4096, 128, 2048, None, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 1000, B, 4096, 128, 2048, C, None) == q8.Q8_ERR_ARG  # ld_gate < n
+    assert _raw(f, A, 4096, B, 4096, -1, 2048, C, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 4096, B, 4096, 128, 2040, C, None) == q8.Q8_ERR_SHAPE  # n % 32
+    assert _raw(f, A + 4, 4096, B, 4096, 128, 2048, C, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 4098, B, 4096, 128, 2048, C, None) == q8.Q8_ERR_ALIGN  # ld % 4
+    assert _raw(f, A, 4096, A + 8192, 4096, 128, 2048, A + 4096, None) == q8.Q8_ERR_ARG  # q_out over gate
+    assert _raw(f, A, 4096, B, 4096, 0, 2048, C, None) == q8.Q8_OK
+
+
+def test_combine_validation():
+    f = "q8_moe_combine"
+    assert _raw(f, None, 7168, B, 16, 8, 7168, C, 7168, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 7168, B, 16, 0, 7168, C, 7168, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 7000, B, 16, 8, 7168, C, 7168, None) == q8.Q8_ERR_ARG   # ld_y < n
+    assert _raw(f, A, 7168, B, 16, 8, 7166, C, 7168, None) == q8.Q8_ERR_SHAPE  # n % 4
+    assert _raw(f, A + 4, 7168, B, 16, 8, 7168, C, 7168, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 7168, B + 1, 16, 8, 7168, C, 7168, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 7168, B, 16, 8, 7168, A + 1024, 7168, None) == q8.Q8_ERR_ARG  # out over y
+    assert _raw(f, A, 7168, B, 0, 8, 7168, C, 7168, None) == q8.Q8_OK
+
+
 def _no_gpu():
     import torch
     return torch.cuda.device_count() == 0
@@ -224,3 +266,6 @@ def test_valid_request_without_device_reports_device_error():
     assert _seq([(A, 2048, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_DEVICE
     assert _raw("q8_rmsnorm_quantize", A, B, B, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_DEVICE
     assert _raw("q8_rmsnorm_quantize", A, None, A, C, 1, 2048, 1e-5, D, None) == q8.Q8_ERR_DEVICE  # in place on x
+    assert _raw("q8_moe_route", A, 16, 256, 8, 1, B, C, None) == q8.Q8_ERR_DEVICE
+    assert _raw("q8_swiglu_quantize", A, 4096, A + 8192, 4096, 128, 2048, C, None) == q8.Q8_ERR_DEVICE
+    assert _raw("q8_moe_combine", A, 7168, B, 16, 8, 7168, 0x7F0000400000, 7168, None) == q8.Q8_ERR_DEVICE

@@ -137,9 +137,16 @@ def norm_inputs(workload: int, index: int, rows: int, k: int):
     return x, res, gain.astype(np.float32)
 
 
+def router_logits(workload: int, tokens: int, n_experts: int, group: int = 0) -> np.ndarray:
+    """fp32 [tokens][n_experts] router logits, uniform(0, 1)."""
+    return generator(workload, (TAG_ROUTE, group, 0)).random((tokens, n_experts), dtype=np.float32)
+
+
 def routing(workload: int, tokens: int, n_experts: int, topk: int, group: int = 0) -> np.ndarray:
-    """int32 [tokens][topk] expert ids: top-k of uniform logits per token."""
-    logits = generator(workload, (TAG_ROUTE, group, 0)).random((tokens, n_experts), dtype=np.float32)
+    """int32 [tokens][topk] expert ids: top-k of uniform logits per token
+    (input generation for the routed-expert GEMV alone; the library's router
+    computes the same selection on the device)."""
+    logits = router_logits(workload, tokens, n_experts, group)
     # Stable sort of the negated logits: descending logit, ties to the lower id.
     order = np.argsort(-logits, axis=1, kind="stable")
     return np.ascontiguousarray(order[:, :topk].astype(np.int32))
