@@ -17,8 +17,9 @@ replayed.
 Other workloads (same JSON line format): ``single`` (one 2048x2048 GEMV),
 ``batched`` (the decode step with ``--m`` rows per GEMV), ``prefill`` (the
 int8-MFMA GEMM at M in {188, 752, 2048} x (N, K) in {(2048, 2048),
-(8192, 2048), (2048, 8192)}), ``moe`` (routed-expert GEMVs: 256 experts,
-16 tokens, top-8; gate, up and down), ``norm`` (the fused residual + RMSNorm +
+(8192, 2048), (2048, 8192)}), ``moe`` (a mixture-of-experts layer on the
+device: router over 256 experts, top-8 of 16 tokens, fused gate||up and down
+routed GEMVs, SwiGLU, weighted combine), ``norm`` (the fused residual + RMSNorm +
 Q8_0 quantize producer at the prefill row counts, hidden 2048), ``copy`` (a
 device copy of 1 GiB, used to calibrate rocprofv3's byte counters).
 
@@ -497,87 +498,117 @@ def bench_prefill(args):
 # --------------------------------------------------------------------------
 
 def bench_moe(args):
+    """One mixture-of-experts layer on the device: router -> fused gate||up
+    routed GEMV -> SwiGLU + quantize -> down routed GEMV -> weighted combine."""
     import torch
 
     import oracle
     import workloads as wl
     from decode_q8_amd import q8
     dev = torch.device("cuda", 0)
-    E, T, K8 = wl.MOE_EXPERTS, wl.MOE_TOKENS, wl.MOE_TOPK
-    ids = wl.routing(wl.MOE, T, E, K8)
-    ids_d = torch.from_numpy(ids).to(dev)
-    used = sorted(set(int(e) for e in np.unique(ids)))
-    mats = []
-    for mi, (name, n, k) in enumerate(wl.MOE_MATS):
-        stride = q8.q8_quantized_bytes(n, k)
-        buf = torch.empty(E * stride, dtype=torch.uint8, device=dev)
-        host = {}
-        for e0 in range(0, E, 16):
-            es = list(range(e0, min(E, e0 + 16)))
-            ws = wl.many(lambda e: wl.weight(wl.MOE, e, n, k, group=mi), [(e,) for e in es], args.threads)
-            for e, w in zip(es, ws):
-                wr = q8.quantize(torch.from_numpy(w).to(dev), q8.Q8_LAYOUT_ROWS)
-                q8.q8_repack_weights(wr, n, k, buf[e * stride:(e + 1) * stride])
-                if not args.no_cpu_baseline and e in used[:2]:
-                    host[e] = oracle_rows(w, args.threads)
-            del ws
-        per_pair = 1 if name == "down" else 0
-        rows = T * K8 if per_pair else T
-        x = wl.activation(wl.MOE, 100 + mi, rows, k)
-        xq = q8.quantize(torch.from_numpy(x).to(dev), q8.Q8_LAYOUT_ACT)
-        need = q8.q8_grouped_workspace_bytes(T, K8, E, n, k)
-        mats.append(dict(name=name, n=n, k=k, stride=stride, buf=buf, rows=rows, per_pair=per_pair, x=x, xq=xq,
-                         y=torch.empty((T * K8, n), dtype=torch.float32, device=dev),
-                         ws=torch.empty(need, dtype=torch.uint8, device=dev), need=need, host=host))
+    E, T, K8, H, F = wl.MOE_EXPERTS, wl.MOE_TOKENS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
+    P = T * K8
+    logits = wl.router_logits(wl.MOE, T, E)
+    ids_h = wl.routing(wl.MOE, T, E, K8)  # the same selection the device router makes (tested)
+    used = sorted(set(int(e) for e in np.unique(ids_h)))
+    s_gu, s_d = q8.q8_quantized_bytes(2 * F, H), q8.q8_quantized_bytes(H, F)
+    # every expert has its place in HBM; only the routed ones are generated
+    # (the kernels read nothing else)
+    gu = torch.zeros(E * s_gu, dtype=torch.uint8, device=dev)
+    dn = torch.zeros(E * s_d, dtype=torch.uint8, device=dev)
+    host = {}
+    for e0 in range(0, len(used), 8):
+        es = used[e0:e0 + 8]
+        gen = wl.many(lambda e: (wl.weight(wl.MOE, e, F, H, group=0), wl.weight(wl.MOE, e, F, H, group=1),
+                                 wl.weight(wl.MOE, e, H, F, group=2)), [(e,) for e in es], args.threads)
+        for e, (wg, wu, wd) in zip(es, gen):
+            w_gu = np.concatenate([wg, wu])
+            q8.q8_repack_weights(q8.quantize(torch.from_numpy(w_gu).to(dev), q8.Q8_LAYOUT_ROWS), 2 * F, H,
+                                 gu[e * s_gu:(e + 1) * s_gu])
+            q8.q8_repack_weights(q8.quantize(torch.from_numpy(wd).to(dev), q8.Q8_LAYOUT_ROWS), H, F,
+                                 dn[e * s_d:(e + 1) * s_d])
+            if not args.no_cpu_baseline and e in used[:2]:
+                host[e] = (oracle_rows(w_gu, args.threads), oracle_rows(wd, args.threads))
+        del gen
+    x = wl.activation(wl.MOE, 100, T, H)
+    xq = q8.quantize(torch.from_numpy(x).to(dev), q8.Q8_LAYOUT_ACT)
+    lg = torch.from_numpy(logits).to(dev)
+    ids = torch.empty((T, K8), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K8), dtype=torch.float32, device=dev)
+    y_gu = torch.empty((P, 2 * F), dtype=torch.float32, device=dev)
+    hq = torch.empty(q8.q8_quantized_bytes(P, F), dtype=torch.uint8, device=dev)
+    y_d = torch.empty((P, H), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    need = max(q8.q8_grouped_workspace_bytes(T, K8, E, 2 * F, H), q8.q8_grouped_workspace_bytes(T, K8, E, H, F))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
-    stream = torch.cuda.Stream()
+    stages = ["route", "gate_up", "swiglu", "down", "combine"]
 
     def run(s, timers=None):
-        for i, c in enumerate(mats):
+        st = s.cuda_stream
+        calls = [lambda: q8.q8_moe_route(lg, T, E, K8, True, ids, wts, st),
+                 lambda: q8.q8_grouped_matmul(xq, T, 0, ids, T, K8, gu, E, s_gu, 2 * F, H, y_gu, ws, need, st),
+                 lambda: q8.q8_swiglu_quantize(y_gu, 2 * F, y_gu[:, F:], 2 * F, P, F, hq, st),
+                 lambda: q8.q8_grouped_matmul(hq, P, 1, ids, T, K8, dn, E, s_d, H, F, y_d, ws, need, st),
+                 lambda: q8.q8_moe_combine(y_d, H, wts, T, K8, H, out, H, st)]
+        for i, c in enumerate(calls):
             if timers is not None:
                 timers[i].start()
-            q8.q8_grouped_matmul(c["xq"], c["rows"], c["per_pair"], ids_d, T, K8, c["buf"], E, c["stride"], c["n"],
-                                 c["k"], c["y"], c["ws"], c["need"], s.cuda_stream)
+            c()
             if timers is not None:
                 timers[i].stop()
 
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run(stream)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_h), "device router disagrees with the host routing"
+    assert int(ws[:4].view(torch.int32).cpu()[0]) == 0, "an expert id was out of range"
     ms_per_step, graph = graph_time(run, stream, args.steps, args.warmup)
-    ms = per_launch_ms(run, len(mats), stream, graph, reps=max(1, min(args.steps, 10)))
+    ms = per_launch_ms(run, len(stages), stream, graph, reps=max(1, min(args.steps, 10)))
     U = len(used)
-    wbytes = np.array([U * c["stride"] for c in mats], dtype=np.float64)
-    abytes = np.array([wbytes[i] + c["rows"] * (c["k"] // 32) * 34 + 4 * T * K8 * c["n"] for i, c in enumerate(mats)])
-    value = wbytes.sum() / (ms_per_step * 1e-3) / 1e9
+    w_gu_bytes, w_d_bytes = float(U * s_gu), float(U * s_d)
+    wbytes = w_gu_bytes + w_d_bytes
+    value = wbytes / (ms_per_step * 1e-3) / 1e9
+    # the dominant launch: the fused gate||up routed GEMV (weights, token rows, outputs)
+    gu_bytes = w_gu_bytes + T * (H // 32) * 34 + 4 * P * 2 * F
     cpu = None
     if not args.no_cpu_baseline:
-        # bounded sample: every pair routed to the first two used experts
-        t0 = time.time()
-        nb = 0
-        for c in mats:
-            xa = oracle.quantize_rows(c["x"], oracle.LAYOUT_ACT)
-            for e, rows_e in c["host"].items():
-                pairs = [p for p in range(T * K8) if ids.reshape(-1)[p] == e]
-                for p in pairs:
-                    xr = p if c["per_pair"] else p // K8
-                    one = oracle.quantize_rows(c["x"][xr:xr + 1], oracle.LAYOUT_ACT)
-                    oracle.matmul(one, 1, rows_e, c["n"], c["k"], threads=args.threads)
-                    nb += c["stride"]
-        dt = time.time() - t0
-        cpu = {"value": round(nb / dt / 1e9, 3), "unit": "GB/s", "cores": args.threads, "kind": "oracle",
-               "sample": f"every routed pair of 2 experts per matrix (one matmul per pair), {dt:.2f} s"}
+        # bounded sample: the whole layer for the pairs routed to the first two
+        # experts, repeated for a few seconds
+        sample = [(p, e) for e in host for p in range(P) if ids_h.reshape(-1)[p] == e]
+
+        def oracle_sample():
+            for p, e in sample:
+                rows_gu, rows_d = host[e]
+                xa = oracle.quantize_rows(x[p // K8:p // K8 + 1], oracle.LAYOUT_ACT)
+                yg, _ = oracle.matmul(xa, 1, rows_gu, 2 * F, H, threads=args.threads)
+                hq1 = oracle.swiglu_quantize(yg[:, :F], yg[:, F:])
+                oracle.matmul(hq1, 1, rows_d, H, F, threads=args.threads)
+
+        sec, reps = timed_repeat(oracle_sample, min_seconds=5.0, max_reps=10000)
+        nb = len(sample) * (s_gu + s_d)
+        cpu = {"value": round(nb / sec / 1e9, 3), "unit": "GB/s", "cores": args.threads, "kind": "oracle",
+               "sample": f"gate||up, SwiGLU and down of the {len(sample)} pairs routed to 2 experts, "
+                         f"{reps} repetitions"}
     config = {
-        "workload": "MoE grouped GEMV: 256 experts (gate, up 2048x7168; down 7168x2048), 16 tokens, top-8 of "
-                    "uniform logits",
+        "workload": "MoE layer: router over 256 experts (top-8, softmax over the selected), fused gate||up "
+                    "(2x 2048x7168) and down (7168x2048) routed GEMVs per expert, SwiGLU, weighted combine; "
+                    "16 tokens, hidden 7168",
         "distinct_experts": U,
         "expected_distinct_experts": round(256 * (1 - (1 - 8 / 256) ** 16), 2),
-        "weight_bytes_per_step": int(wbytes.sum()),
+        "weight_bytes_per_step": int(wbytes),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "GBs_by_matrix": {c["name"]: round(wbytes[i] / (ms[i] * 1e-3) / 1e9, 1) for i, c in enumerate(mats)},
+        "us_by_stage": {name: round(float(ms[i]) * 1e3, 2) for i, name in enumerate(stages)},
+        "GBs_by_gemv": {"gate_up": round(w_gu_bytes / (ms[1] * 1e-3) / 1e9, 1),
+                        "down": round(w_d_bytes / (ms[3] * 1e-3) / 1e9, 1)},
         "hip_graph": True,
     }
-    roof = hbm_roofline("q8k::grouped_gemv_kernel", float(abytes.mean()), float(ms.mean()))
+    roof = hbm_roofline("q8k::grouped_gemv_kernel", gu_bytes, float(ms[1]))
     roof["traffic"] = profiled_traffic("grouped_gemv_moe.txt",
                                        ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
-    roof["note"] = "launch time includes the expert-grouping kernel that precedes the GEMV in each call"
+    roof["note"] = ("the fused gate||up launch; its time includes the expert-grouping kernel that precedes the "
+                    "GEMV in each call")
     return base_record(args, "Q8_0 routed-expert GEMV weight GB/s (%HBM peak)", value, "GB/s", ms_per_step,
                        "int8xint8->int32, fp32 scale/sum", config, roof, cpu)
 

@@ -143,26 +143,51 @@ hipError_t launch_gemv_f32(const float *x, int64_t ld_x, int64_t m, const void *
 constexpr int GROUP_THREADS = 1024;
 constexpr int ID_CHUNK = 4096;
 
-__device__ __forceinline__ int block_exclusive_scan(int v, int *sh) {
-    // Hillis-Steele inclusive scan over GROUP_THREADS values, then shift.
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < GROUP_THREADS; off <<= 1) {
-        const int add = tid >= off ? sh[tid - off] : 0;
-        __syncthreads();
-        sh[tid] += add;
-        __syncthreads();
+// Exclusive prefix sum over the GROUP_THREADS threads of the workgroup: a
+// shuffle scan inside each wave, the wave totals scanned by wave 0, two
+// barriers in all.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *wave_tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
     }
-    const int incl = sh[tid];
+    if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
-    return incl - v;
+    if (wave == 0) {
+        int w = lane < GROUP_THREADS / 64 ? wave_tot[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < GROUP_THREADS / 64; off <<= 1) {
+            const int t = __shfl_up(w, off);
+            if (lane >= off) w += t;
+        }
+        if (lane < GROUP_THREADS / 64) wave_tot[lane] = w;  // inclusive over waves
+    }
+    __syncthreads();
+    return (wave ? wave_tot[wave - 1] : 0) + incl - v;
+}
+
+// Occurrences of `id` in chunk[0, len): four ids per LDS read, unrolled so
+// that several reads are in flight.
+__device__ __forceinline__ int count_in_chunk(const int32_t *chunk, int len, int id) {
+    int cnt = 0;
+    const int4 *c4 = reinterpret_cast<const int4 *>(chunk);
+    const int n4 = len >> 2;
+#pragma unroll 8
+    for (int j = 0; j < n4; j++) {
+        const int4 v = c4[j];
+        cnt += (v.x == id) + (v.y == id) + (v.z == id) + (v.w == id);
+    }
+    for (int j = n4 << 2; j < len; j++) cnt += (chunk[j] == id);
+    return cnt;
 }
 
 __global__ __launch_bounds__(GROUP_THREADS) void group_pairs_kernel(const int32_t *__restrict__ ids, int64_t pairs,
                                                                    int64_t n_experts, int32_t *__restrict__ ws) {
-    __shared__ int32_t chunk[ID_CHUNK];
-    __shared__ int scan_sh[GROUP_THREADS];
+    __shared__ __align__(16) int32_t chunk[ID_CHUNK];
+    __shared__ int scan_sh[GROUP_THREADS / 64];
     __shared__ int bad_sh;
     const int tid = threadIdx.x;
     const int E = (int)n_experts;
@@ -181,21 +206,23 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_pairs_kernel(const int32_
             bad |= (v < 0 || v >= E);
         }
         __syncthreads();
-        if (tid < E)
-            for (int j = 0; j < len; j++) cnt += (chunk[j] == tid);
+        if (tid < E) cnt += count_in_chunk(chunk, len, tid);
     }
     if (bad) atomicOr(&bad_sh, 1);
+    // one scan of (active flag, pair count): the flag in bits 17 and up (at
+    // most 1024 experts), the count below (at most 65536 pairs)
     const int is_active = (tid < E && cnt > 0) ? 1 : 0;
-    const int slot = block_exclusive_scan(is_active, scan_sh);
-    const int off = block_exclusive_scan(is_active ? cnt : 0, scan_sh);
+    const int packed = (is_active << 17) | (is_active ? cnt : 0);
+    const int excl = block_exclusive_scan(packed, scan_sh);
+    const int slot = excl >> 17, off = excl & 0x1ffff;
     if (is_active) {
         active[slot] = tid;
         offs[slot] = off;
     }
     if (tid == GROUP_THREADS - 1) {
-        const int n_active = slot + is_active;
-        ws[1] = n_active;
-        offs[n_active] = off + (is_active ? cnt : 0);
+        const int incl = excl + packed;
+        ws[1] = incl >> 17;
+        offs[incl >> 17] = incl & 0x1ffff;
     }
     __syncthreads();
     if (tid == 0) ws[0] = bad_sh ? 1 : 0;
@@ -203,12 +230,26 @@ __global__ __launch_bounds__(GROUP_THREADS) void group_pairs_kernel(const int32_
     int pos = off;
     for (int64_t base = 0; base < pairs; base += ID_CHUNK) {
         const int len = (int)((pairs - base) < ID_CHUNK ? (pairs - base) : ID_CHUNK);
-        __syncthreads();
-        for (int i = tid; i < len; i += GROUP_THREADS) chunk[i] = ids[base + i];
-        __syncthreads();
-        if (is_active)
-            for (int j = 0; j < len; j++)
+        if (pairs > ID_CHUNK) {  // a single chunk is still in LDS from the count
+            __syncthreads();
+            for (int i = tid; i < len; i += GROUP_THREADS) chunk[i] = ids[base + i];
+            __syncthreads();
+        }
+        if (is_active) {
+            const int4 *c4 = reinterpret_cast<const int4 *>(chunk);
+            const int n4 = len >> 2;
+#pragma unroll 8
+            for (int j = 0; j < n4; j++) {
+                const int4 v = c4[j];
+                const int32_t p0 = (int32_t)(base + 4 * j);
+                if (v.x == tid) list[pos++] = p0;
+                if (v.y == tid) list[pos++] = p0 + 1;
+                if (v.z == tid) list[pos++] = p0 + 2;
+                if (v.w == tid) list[pos++] = p0 + 3;
+            }
+            for (int j = n4 << 2; j < len; j++)
                 if (chunk[j] == tid) list[pos++] = (int32_t)(base + j);
+        }
     }
 }
 

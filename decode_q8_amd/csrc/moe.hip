@@ -48,26 +48,41 @@ __device__ __forceinline__ double exp_nonpos(double x) {
 // ---------------------------------------------------------------------------
 // Router: one wavefront per token.  Lane l holds the logits of experts
 // l, l + 64, ... (n_experts <= 1024).  Slot j is the arg-max over the experts
-// not yet taken, ties to the lower id: a wave-wide maximum of a 64-bit key
-// (order-preserving image of the logit, then the complemented id).
+// not yet taken, ties to the lower id: a wave-wide maximum of the logits'
+// order-preserving keys, then the minimum id among the lanes that hold it.
 // ---------------------------------------------------------------------------
 
 constexpr int ROUTE_MAX_PER_LANE = 16;  // n_experts <= 1024
 
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-    if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal: give them one key
-    uint32_t b = __builtin_bit_cast(uint32_t, v);
-    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // monotone in v
-    return ((uint64_t)b << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+// Order-preserving image of a finite fp32 value in uint32 (larger value,
+// larger key; -0 and +0 share a key since they compare equal).  Every key is
+// above 0, which therefore serves as "nothing left".
+__device__ __forceinline__ uint32_t value_key(float v) {
+    if (v == 0.0f) v = 0.0f;
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        const uint64_t o = __shfl_xor(k, s);
-        k = o > k ? o : k;
-    }
-    return k;
+// Wave-wide max / min of a uint32 through DPP lane moves (no LDS round trip):
+// swaps inside quads, mirrors inside half rows and rows, then the row
+// broadcasts 15 and 31; lane 63 ends with the result.
+template <bool MAX>
+__device__ __forceinline__ uint32_t dpp_op(uint32_t a, uint32_t b) {
+    return MAX ? (a > b ? a : b) : (a < b ? a : b);
+}
+
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
+#define Q8_DPP(ctrl, rows) \
+    x = dpp_op<MAX>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, ctrl, rows, 0xf, false))
+    Q8_DPP(0xb1, 0xf);   // quad_perm [1, 0, 3, 2]
+    Q8_DPP(0x4e, 0xf);   // quad_perm [2, 3, 0, 1]
+    Q8_DPP(0x141, 0xf);  // row_half_mirror
+    Q8_DPP(0x140, 0xf);  // row_mirror
+    Q8_DPP(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    Q8_DPP(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef Q8_DPP
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 __global__ __launch_bounds__(256) void moe_route_kernel(const float *__restrict__ logits, int32_t tokens,
@@ -90,17 +105,22 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *__restrict_
     float top = 0.0f;       // the largest logit (slot 0)
     float mine = 0.0f;      // lane j < topk: the logit of slot j
     for (int j = 0; j < topk; j++) {
-        uint64_t best = 0u;  // below every key: the id part alone is at least 2^32 - 1024
+        // this lane's best remaining expert (ascending ids, so ties keep the lower)
+        uint32_t bk = 0u, bid = 0xffffffffu;
 #pragma unroll
         for (int i = 0; i < ROUTE_MAX_PER_LANE; i++) {
             const int e = lane + 64 * i;
             if (i < per && e < n_experts && !((taken >> i) & 1u)) {
-                const uint64_t k = route_key(v[i], e);
-                best = k > best ? k : best;
+                const uint32_t k = value_key(v[i]);
+                if (k > bk) {
+                    bk = k;
+                    bid = (uint32_t)e;
+                }
             }
         }
-        best = wave_max_u64(best);
-        const int e = (int)(0xffffffffu - (uint32_t)best);
+        // the largest value over the wave, then the lowest id holding it
+        const uint32_t kmax = wave_reduce<true>(bk);
+        const int e = (int)wave_reduce<false>(bk == kmax ? bid : 0xffffffffu);
         if ((e & 63) == lane) taken |= 1u << (e >> 6);
         // the winning logit, from its owner lane
         float lv = 0.0f;
@@ -113,14 +133,12 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *__restrict_
         if (lane == 0) ids_t[j] = e;
     }
     const double m = (double)top;
+    const double ej = exp_nonpos((double)mine - m);  // lane j < topk: slot j's term, all slots at once
     double D;
     if (normalize) {
         // sum over the selected experts in slot order (every lane, sequentially)
         D = 0.0;
-        for (int j = 0; j < topk; j++) {
-            const float lj = __shfl(mine, j);
-            D += exp_nonpos((double)lj - m);
-        }
+        for (int j = 0; j < topk; j++) D += __shfl(ej, j);
     } else {
         // all experts: lane partials in ascending expert order, then a halving tree
         double P = 0.0;
@@ -133,7 +151,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *__restrict_
         for (int s = 32; s >= 1; s >>= 1) P += __shfl_down(P, s);
         D = __shfl(P, 0);
     }
-    if (lane < topk) w_t[lane] = (float)(exp_nonpos((double)mine - m) / D);
+    if (lane < topk) w_t[lane] = (float)(ej / D);
 }
 
 // ---------------------------------------------------------------------------
