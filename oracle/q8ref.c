@@ -457,3 +457,141 @@ int q8ref_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t toke
         }
     return Q8REF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Q8_0 KV cache: fused norm + rope + cache write; decode attention         */
+/* ------------------------------------------------------------------------ */
+
+/* KV block: fp32 scale kept as is */
+static float kv_quantize_block(const float *x, int8_t *q) {
+    float amax = 0.0f;
+    for (int j = 0; j < QK; j++) {
+        const float a = fabsf(x[j]);
+        if (a > amax) amax = a;
+    }
+    const float d = amax / 127.0f;
+    for (int j = 0; j < QK; j++) q[j] = d == 0.0f ? 0 : (int8_t)roundf(x[j] / d);
+    return d;
+}
+
+static void head_norm(float *x, int hd, const float *g, float eps) {
+    double p[64];
+    const int nc = hd / 4;
+    for (int c = 0; c < nc; c++) {
+        p[c] = 0.0;
+        for (int i = 0; i < 4; i++) p[c] += (double)x[4 * c + i] * (double)x[4 * c + i];
+    }
+    for (int st = nc / 2; st >= 1; st /= 2)
+        for (int c = 0; c < st; c++) p[c] += p[c + st];
+    const float r = (float)(1.0 / sqrt(p[0] / (double)hd + (double)eps));
+    for (int i = 0; i < hd; i++) {
+        const float xr = x[i] * r;
+        x[i] = xr * g[i];
+    }
+}
+
+static void head_rope(float *x, int hd, const float *c, const float *s) {
+    const int h = hd / 2;
+    for (int i = 0; i < h; i++) {
+        const float a = x[i], b = x[i + h];
+        const float ac = a * c[i], bs = b * s[i], bc = b * c[i], as = a * s[i];
+        x[i] = ac - bs;
+        x[i + h] = bc + as;
+    }
+}
+
+int q8ref_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim, const int32_t *positions,
+                   const float *cos_tab, const float *sin_tab, const float *q_gain, const float *k_gain, float eps,
+                   const int32_t *slots, float *q_out, int8_t *k_cache, float *k_scale, int8_t *v_cache,
+                   float *v_scale) {
+    if (!qkv || !positions || !cos_tab || !sin_tab || !slots || !q_out || !k_cache || !k_scale || !v_cache ||
+        !v_scale || tokens < 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv)
+        return Q8REF_EARG;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return Q8REF_ESHAPE;
+    const int hd = head_dim, nb = hd / QK, h2 = hd / 2;
+    const int64_t row = (int64_t)(n_heads + 2 * n_kv) * hd;
+    float x[256];
+    for (int64_t t = 0; t < tokens; t++) {
+        const float *r = qkv + t * row;
+        const float *c = cos_tab + (int64_t)positions[t] * h2, *s = sin_tab + (int64_t)positions[t] * h2;
+        for (int h = 0; h < n_heads; h++) {
+            memcpy(x, r + (int64_t)h * hd, sizeof(float) * hd);
+            if (q_gain) head_norm(x, hd, q_gain, eps);
+            head_rope(x, hd, c, s);
+            memcpy(q_out + (t * n_heads + h) * hd, x, sizeof(float) * hd);
+        }
+        const int64_t slot = slots[t];
+        for (int h = 0; h < n_kv; h++) {
+            memcpy(x, r + (int64_t)(n_heads + h) * hd, sizeof(float) * hd);
+            if (k_gain) head_norm(x, hd, k_gain, eps);
+            head_rope(x, hd, c, s);
+            for (int b = 0; b < nb; b++)
+                k_scale[(slot * n_kv + h) * nb + b] = kv_quantize_block(x + b * QK, k_cache + (slot * n_kv + h) * hd + b * QK);
+            memcpy(x, r + (int64_t)(n_heads + n_kv + h) * hd, sizeof(float) * hd);
+            for (int b = 0; b < nb; b++)
+                v_scale[(slot * n_kv + h) * nb + b] = kv_quantize_block(x + b * QK, v_cache + (slot * n_kv + h) * hd + b * QK);
+        }
+    }
+    return Q8REF_OK;
+}
+
+int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,
+                           const float *k_scale, const int8_t *v_cache, const float *v_scale, const int32_t *base,
+                           const int32_t *len, float scale, float *out, double *bound) {
+    if (!q || !k_cache || !k_scale || !v_cache || !v_scale || !base || !len || !out || seqs < 0 || n_heads <= 0 ||
+        n_kv <= 0 || n_heads % n_kv || head_dim <= 0 || head_dim % QK)
+        return Q8REF_EARG;
+    const int hd = head_dim, nb = hd / QK, G = n_heads / n_kv;
+    const double u = ldexp(1.0, -24);
+    for (int64_t sq = 0; sq < seqs; sq++) {
+        const int64_t L = len[sq];
+        if (L <= 0) return Q8REF_EARG;
+        double *sc = malloc(sizeof(double) * (size_t)L), *Sj = malloc(sizeof(double) * (size_t)L);
+        if (!sc || !Sj) {
+            free(sc);
+            free(Sj);
+            return Q8REF_EARG;
+        }
+        for (int h = 0; h < n_heads; h++) {
+            const int kvh = h / G;
+            const float *qh = q + (sq * n_heads + h) * hd;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < L; j++) {
+                const int64_t slot = base[sq] + j;
+                const int8_t *kr = k_cache + (slot * n_kv + kvh) * hd;
+                const float *ks = k_scale + (slot * n_kv + kvh) * nb;
+                double acc = 0.0, aabs = 0.0;
+                for (int d = 0; d < hd; d++) {
+                    const double kv = (double)kr[d] * (double)ks[d / QK];
+                    acc += (double)qh[d] * kv;
+                    aabs += fabs((double)qh[d] * kv);
+                }
+                sc[j] = (double)scale * acc;
+                Sj[j] = aabs;
+                if (sc[j] > mx) mx = sc[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < L; j++) {
+                sc[j] = exp(sc[j] - mx);
+                l += sc[j];
+            }
+            for (int d = 0; d < hd; d++) {
+                double o = 0.0, ob = 0.0;
+                for (int64_t j = 0; j < L; j++) {
+                    const int64_t slot = base[sq] + j;
+                    const double vv = (double)v_cache[(slot * n_kv + kvh) * hd + d] *
+                                      (double)v_scale[(slot * n_kv + kvh) * nb + d / QK];
+                    o += sc[j] * vv;
+                    ob += sc[j] * fabs(vv) *
+                          ((double)scale * Sj[j] * 2.0 * (hd + 2) * u + (96.0 + (double)L / 256.0) * u);
+                }
+                const double r = o / l;
+                out[(sq * n_heads + h) * hd + d] = (float)r;
+                if (bound) bound[(sq * n_heads + h) * hd + d] = ob / l + 2.0 * u * fabs(r);
+            }
+        }
+        free(sc);
+        free(Sj);
+    }
+    return Q8REF_OK;
+}

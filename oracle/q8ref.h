@@ -163,6 +163,50 @@ int q8ref_swiglu_quantize(const float *gate, int64_t ld_gate, const float *up, i
 int q8ref_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t tokens, int topk, int64_t n, float *out,
                       double *Sc);
 
+/* ---- Q8_0 KV cache ("ferro" README, "KV cache": K/V rows stored as int8 with
+ * one fp32 scale per 32 values, quantized in the fused norm + rope +
+ * cache-write kernel and dequantized in the attention kernels).  Readings:
+ *  - a KV block: d = fp32(amax / 127) kept as fp32 (not rounded to fp16),
+ *    q = roundf(x / d) (ties away from zero), d = 0 for an all-zero block;
+ *  - qkv rows hold n_heads query heads, then n_kv key heads, then n_kv value
+ *    heads, each head_dim values (one fused QKV projection per token);
+ *  - optional per-head RMSNorm of q and k (gains of head_dim values, NULL for
+ *    none): ss = sum of x^2 in fp64 as head_dim/4 partials of 4 consecutive
+ *    values (in order), folded p_c += p_{c+s} for s = head_dim/8, ..., 1;
+ *    r = fp32(1 / sqrt(ss / head_dim + eps)); n = fp32(fp32(x * r) * g);
+ *  - rotary embedding of q and k (after the norm) in the half-split layout:
+ *    for i < head_dim/2, with c = cos_tab[pos][i], s = sin_tab[pos][i]:
+ *      y_i        = fp32(fp32(x_i * c) - fp32(x_{i+h} * s))
+ *      y_{i+h}    = fp32(fp32(x_{i+h} * c) + fp32(x_i * s)),  h = head_dim/2;
+ *    the tables are inputs (model constants), fp32 [positions][head_dim/2];
+ *  - cache layout: int8 [slot][n_kv][head_dim] and fp32 scales
+ *    [slot][n_kv][head_dim/32], for K and V alike; token t writes slot
+ *    slots[t]; v is quantized as is (no norm, no rotation). */
+
+/* The fused norm + rope + cache write for `tokens` rows of qkv (fp32,
+ * [tokens][(n_heads + 2 n_kv) head_dim]); q_out fp32 [tokens][n_heads][head_dim]
+ * receives the normalized, rotated queries.  head_dim in {64, 128, 256}. */
+int q8ref_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim, const int32_t *positions,
+                   const float *cos_tab, const float *sin_tab, const float *q_gain, const float *k_gain, float eps,
+                   const int32_t *slots, float *q_out, int8_t *k_cache, float *k_scale, int8_t *v_cache,
+                   float *v_scale);
+
+/* Decode attention over the Q8 KV cache, one query row per sequence:
+ *   for query head h (kv head h / (n_heads / n_kv)), keys j < len[s] at slot
+ *   base[s] + j, dequantized k = q * d and v = q * d (exact in fp64):
+ *   s_j = scale * sum_d q_d k_jd;  p_j = exp(s_j - max);  out = sum p_j v_j / sum p_j
+ * all in fp64, out rounded once to fp32.  bound (may be NULL) receives, per
+ * output, an fp64 error budget for an fp32 evaluation whose dot products are
+ * sums of head_dim + 2 rounded terms, whose softmax sums and weighted sums run
+ * over at most 96 rounded steps inside a chunk of 256 keys plus one step per
+ * chunk (an error common to every p_j, such as that of the maximum, cancels
+ * in the normalization):
+ *   (sum_j p_j |v_jd| * (scale * S_j * 2 (head_dim + 2) u + (96 + len/256) u))
+ *   / sum_j p_j + 2 u |out|,  S_j = sum_d |q_d k_jd|,  u = 2^-24. */
+int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,
+                           const float *k_scale, const int8_t *v_cache, const float *v_scale, const int32_t *base,
+                           const int32_t *len, float scale, float *out, double *bound);
+
 #ifdef __cplusplus
 }
 #endif

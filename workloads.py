@@ -38,6 +38,8 @@ Shapes (out x in = N x K):
     top-8 routing, token rows [16x7168], down inputs [128x2048].
   * norm:    rows in {1, 188, 752, 2048} (decode and prefill tokens) x hidden
     2048 (Llama-3.2-1B), plus hidden 7168 (the MoE model).
+  * kv:      Llama-3.2-1B attention (32 query heads, 8 KV heads of 64) over a
+    Q8 KV cache: 16 sequences x 4096 cached positions, fused QKV rows N(0, 1).
 """
 from __future__ import annotations
 
@@ -61,7 +63,7 @@ TAG_OUTLIER = 5
 TAG_GAIN = 6
 
 # Workload indices (offsets from BASE_SEED).
-SINGLE, DECODE, BATCHED, PREFILL, MOE, NORM = 0, 1, 2, 3, 4, 5
+SINGLE, DECODE, BATCHED, PREFILL, MOE, NORM, KV = 0, 1, 2, 3, 4, 5, 6
 
 LLAMA_HIDDEN = 2048
 LLAMA_LAYERS = 16
@@ -91,6 +93,13 @@ MOE_MATS = (("gate", MOE_FFN, MOE_HIDDEN), ("up", MOE_FFN, MOE_HIDDEN), ("down",
 
 NORM_ROWS = (1, 188, 752, 2048)
 NORM_EPS = 1e-5
+
+# Llama-3.2-1B attention: 32 query heads, 8 key/value heads of 64.
+LLAMA_HEADS = 32
+LLAMA_KV_HEADS = 8
+LLAMA_HEAD_DIM = 64
+KV_SEQS = 16
+KV_CONTEXT = 4096
 
 
 def generator(workload: int, tag: tuple) -> np.random.Generator:
@@ -140,6 +149,24 @@ def norm_inputs(workload: int, index: int, rows: int, k: int):
 def router_logits(workload: int, tokens: int, n_experts: int, group: int = 0) -> np.ndarray:
     """fp32 [tokens][n_experts] router logits, uniform(0, 1)."""
     return generator(workload, (TAG_ROUTE, group, 0)).random((tokens, n_experts), dtype=np.float32)
+
+
+def rope_tables(max_pos: int, head_dim: int, theta: float = 500000.0):
+    """Rotary-embedding tables, a model constant handed to both sides as an
+    input: fp32 cos and sin [max_pos][head_dim/2] of pos * theta^(-2i/head_dim),
+    evaluated by numpy in fp64 and rounded once (Llama 3 uses theta = 500000)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * theta ** (-2.0 * i / head_dim)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def kv_inputs(workload: int, index: int, tokens: int, n_heads: int, n_kv: int, head_dim: int):
+    """(qkv fp32 [tokens][(n_heads + 2 n_kv) head_dim] N(0, 1), q gain, k gain
+    fp32 [head_dim] 1 + 0.1 N(0, 1)) for the KV-cache write."""
+    qkv = normal(workload, (TAG_ACT, 50, index), (tokens, (n_heads + 2 * n_kv) * head_dim))
+    qg = np.float32(1.0) + normal(workload, (TAG_GAIN, 50, index), (head_dim,), 0.1)
+    kg = np.float32(1.0) + normal(workload, (TAG_GAIN, 51, index), (head_dim,), 0.1)
+    return qkv, qg.astype(np.float32), kg.astype(np.float32)
 
 
 def routing(workload: int, tokens: int, n_experts: int, topk: int, group: int = 0) -> np.ndarray:
