@@ -68,8 +68,8 @@ def lib() -> ctypes.CDLL:
         L.q8ref_moe_route.argtypes = [P, I64, I64, I, I, P, P]
         L.q8ref_swiglu_quantize.argtypes = [P, I64, P, I64, I64, I64, P]
         L.q8ref_moe_combine.argtypes = [P, I64, P, I64, I, I64, P, P]
-        L.q8ref_kv_write.argtypes = [P, I64, I, I, I, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P]
-        L.q8ref_attention_decode.argtypes = [P, I64, I, I, I, P, P, P, P, P, P, ctypes.c_float, P, P]
+        L.q8ref_kv_write.argtypes = [P, I64, I, I, I, P, P, P, P, P, ctypes.c_float, P, I64, P, P, P, P, P]
+        L.q8ref_attention_decode.argtypes = [P, I64, I, I, I, P, P, P, P, I64, P, P, ctypes.c_float, P, P]
         for name in ("q8ref_kv_write", "q8ref_attention_decode",
                      "q8ref_quantize_rows", "q8ref_pack", "q8ref_unpack", "q8ref_block_terms",
                      "q8ref_matmul", "q8ref_matmul_points", "q8ref_grouped_matmul", "q8ref_rmsnorm_quantize",
@@ -190,7 +190,7 @@ def moe_combine(y: np.ndarray, w: np.ndarray):
 def kv_write(qkv, n_heads: int, n_kv: int, head_dim: int, positions, cos_tab, sin_tab, q_gain, k_gain, eps: float,
              slots, n_slots: int):
     """Fused norm + rope + Q8 KV cache write.  Returns (q_out fp32 [tokens][n_heads][head_dim],
-    k_cache int8 [n_slots][n_kv][head_dim], k_scale fp32 [n_slots][n_kv][head_dim/32], v_cache, v_scale);
+    k_cache int8 [n_kv][n_slots][head_dim], k_scale fp32 [n_kv][n_slots][head_dim/32], v_cache, v_scale);
     cache slots not written hold zeros."""
     qkv = np.ascontiguousarray(qkv, dtype=np.float32)
     tokens = qkv.shape[0]
@@ -201,29 +201,29 @@ def kv_write(qkv, n_heads: int, n_kv: int, head_dim: int, positions, cos_tab, si
     qg = None if q_gain is None else np.ascontiguousarray(q_gain, dtype=np.float32)
     kg = None if k_gain is None else np.ascontiguousarray(k_gain, dtype=np.float32)
     q_out = np.empty((tokens, n_heads, head_dim), np.float32)
-    kc = np.zeros((n_slots, n_kv, head_dim), np.int8)
-    vc = np.zeros((n_slots, n_kv, head_dim), np.int8)
-    ks = np.zeros((n_slots, n_kv, head_dim // 32), np.float32)
-    vs = np.zeros((n_slots, n_kv, head_dim // 32), np.float32)
+    kc = np.zeros((n_kv, n_slots, head_dim), np.int8)
+    vc = np.zeros((n_kv, n_slots, head_dim), np.int8)
+    ks = np.zeros((n_kv, n_slots, head_dim // 32), np.float32)
+    vs = np.zeros((n_kv, n_slots, head_dim // 32), np.float32)
     _check(lib().q8ref_kv_write(_p(qkv), tokens, n_heads, n_kv, head_dim, _p(positions), _p(cos_tab), _p(sin_tab),
                                 None if qg is None else _p(qg), None if kg is None else _p(kg), float(eps),
-                                _p(slots), _p(q_out), _p(kc), _p(ks), _p(vc), _p(vs)), "kv_write")
+                                _p(slots), n_slots, _p(q_out), _p(kc), _p(ks), _p(vc), _p(vs)), "kv_write")
     return q_out, kc, ks, vc, vs
 
 
 def attention_decode(q, k_cache, k_scale, v_cache, v_scale, base, length, scale: float):
-    """q fp32 [seqs][n_heads][head_dim]; caches as kv_write returns them ->
+    """q fp32 [seqs][n_heads][head_dim]; caches as kv_write returns them (head-major) ->
     (out fp32 [seqs][n_heads][head_dim], fp64 error budget of an fp32 evaluation)."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     seqs, n_heads, head_dim = q.shape
-    n_kv = k_cache.shape[1]
+    n_kv, n_slots = k_cache.shape[0], k_cache.shape[1]
     base = np.ascontiguousarray(base, dtype=np.int32)
     length = np.ascontiguousarray(length, dtype=np.int32)
     out = np.empty_like(q)
     bound = np.empty(q.shape, np.float64)
     _check(lib().q8ref_attention_decode(_p(q), seqs, n_heads, n_kv, head_dim, _p(np.ascontiguousarray(k_cache)),
                                         _p(np.ascontiguousarray(k_scale)), _p(np.ascontiguousarray(v_cache)),
-                                        _p(np.ascontiguousarray(v_scale)), _p(base), _p(length), float(scale),
+                                        _p(np.ascontiguousarray(v_scale)), n_slots, _p(base), _p(length), float(scale),
                                         _p(out), _p(bound)), "attention_decode")
     return out, bound
 

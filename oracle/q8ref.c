@@ -502,10 +502,10 @@ static void head_rope(float *x, int hd, const float *c, const float *s) {
 
 int q8ref_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim, const int32_t *positions,
                    const float *cos_tab, const float *sin_tab, const float *q_gain, const float *k_gain, float eps,
-                   const int32_t *slots, float *q_out, int8_t *k_cache, float *k_scale, int8_t *v_cache,
-                   float *v_scale) {
+                   const int32_t *slots, int64_t n_slots, float *q_out, int8_t *k_cache, float *k_scale,
+                   int8_t *v_cache, float *v_scale) {
     if (!qkv || !positions || !cos_tab || !sin_tab || !slots || !q_out || !k_cache || !k_scale || !v_cache ||
-        !v_scale || tokens < 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv)
+        !v_scale || tokens < 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || n_slots <= 0)
         return Q8REF_EARG;
     if (head_dim != 64 && head_dim != 128 && head_dim != 256) return Q8REF_ESHAPE;
     const int hd = head_dim, nb = hd / QK, h2 = hd / 2;
@@ -521,31 +521,33 @@ int q8ref_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int 
             memcpy(q_out + (t * n_heads + h) * hd, x, sizeof(float) * hd);
         }
         const int64_t slot = slots[t];
+        if (slot < 0 || slot >= n_slots) return Q8REF_EARG;
         for (int h = 0; h < n_kv; h++) {
+            const int64_t row = (int64_t)h * n_slots + slot; /* head-major cache rows */
             memcpy(x, r + (int64_t)(n_heads + h) * hd, sizeof(float) * hd);
             if (k_gain) head_norm(x, hd, k_gain, eps);
             head_rope(x, hd, c, s);
             for (int b = 0; b < nb; b++)
-                k_scale[(slot * n_kv + h) * nb + b] = kv_quantize_block(x + b * QK, k_cache + (slot * n_kv + h) * hd + b * QK);
+                k_scale[row * nb + b] = kv_quantize_block(x + b * QK, k_cache + row * hd + b * QK);
             memcpy(x, r + (int64_t)(n_heads + n_kv + h) * hd, sizeof(float) * hd);
             for (int b = 0; b < nb; b++)
-                v_scale[(slot * n_kv + h) * nb + b] = kv_quantize_block(x + b * QK, v_cache + (slot * n_kv + h) * hd + b * QK);
+                v_scale[row * nb + b] = kv_quantize_block(x + b * QK, v_cache + row * hd + b * QK);
         }
     }
     return Q8REF_OK;
 }
 
 int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,
-                           const float *k_scale, const int8_t *v_cache, const float *v_scale, const int32_t *base,
-                           const int32_t *len, float scale, float *out, double *bound) {
+                           const float *k_scale, const int8_t *v_cache, const float *v_scale, int64_t n_slots,
+                           const int32_t *base, const int32_t *len, float scale, float *out, double *bound) {
     if (!q || !k_cache || !k_scale || !v_cache || !v_scale || !base || !len || !out || seqs < 0 || n_heads <= 0 ||
-        n_kv <= 0 || n_heads % n_kv || head_dim <= 0 || head_dim % QK)
+        n_kv <= 0 || n_heads % n_kv || head_dim <= 0 || head_dim % QK || n_slots <= 0)
         return Q8REF_EARG;
     const int hd = head_dim, nb = hd / QK, G = n_heads / n_kv;
     const double u = ldexp(1.0, -24);
     for (int64_t sq = 0; sq < seqs; sq++) {
         const int64_t L = len[sq];
-        if (L <= 0) return Q8REF_EARG;
+        if (L <= 0 || base[sq] < 0 || base[sq] + L > n_slots) return Q8REF_EARG;
         double *sc = malloc(sizeof(double) * (size_t)L), *Sj = malloc(sizeof(double) * (size_t)L);
         if (!sc || !Sj) {
             free(sc);
@@ -557,9 +559,9 @@ int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, 
             const float *qh = q + (sq * n_heads + h) * hd;
             double mx = -INFINITY;
             for (int64_t j = 0; j < L; j++) {
-                const int64_t slot = base[sq] + j;
-                const int8_t *kr = k_cache + (slot * n_kv + kvh) * hd;
-                const float *ks = k_scale + (slot * n_kv + kvh) * nb;
+                const int64_t row = (int64_t)kvh * n_slots + base[sq] + j;
+                const int8_t *kr = k_cache + row * hd;
+                const float *ks = k_scale + row * nb;
                 double acc = 0.0, aabs = 0.0;
                 for (int d = 0; d < hd; d++) {
                     const double kv = (double)kr[d] * (double)ks[d / QK];
@@ -578,9 +580,8 @@ int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, 
             for (int d = 0; d < hd; d++) {
                 double o = 0.0, ob = 0.0;
                 for (int64_t j = 0; j < L; j++) {
-                    const int64_t slot = base[sq] + j;
-                    const double vv = (double)v_cache[(slot * n_kv + kvh) * hd + d] *
-                                      (double)v_scale[(slot * n_kv + kvh) * nb + d / QK];
+                    const int64_t row = (int64_t)kvh * n_slots + base[sq] + j;
+                    const double vv = (double)v_cache[row * hd + d] * (double)v_scale[row * nb + d / QK];
                     o += sc[j] * vv;
                     ob += sc[j] * fabs(vv) *
                           ((double)scale * Sj[j] * 2.0 * (hd + 2) * u + (96.0 + (double)L / 256.0) * u);

@@ -179,21 +179,23 @@ int q8ref_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t toke
  *      y_i        = fp32(fp32(x_i * c) - fp32(x_{i+h} * s))
  *      y_{i+h}    = fp32(fp32(x_{i+h} * c) + fp32(x_i * s)),  h = head_dim/2;
  *    the tables are inputs (model constants), fp32 [positions][head_dim/2];
- *  - cache layout: int8 [slot][n_kv][head_dim] and fp32 scales
- *    [slot][n_kv][head_dim/32], for K and V alike; token t writes slot
- *    slots[t]; v is quantized as is (no norm, no rotation). */
+ *  - cache layout, head-major (one head's positions contiguous): int8
+ *    [n_kv][n_slots][head_dim] and fp32 scales [n_kv][n_slots][head_dim/32],
+ *    for K and V alike; token t writes slot slots[t] of every head; v is
+ *    quantized as is (no norm, no rotation). */
 
 /* The fused norm + rope + cache write for `tokens` rows of qkv (fp32,
  * [tokens][(n_heads + 2 n_kv) head_dim]); q_out fp32 [tokens][n_heads][head_dim]
  * receives the normalized, rotated queries.  head_dim in {64, 128, 256}. */
 int q8ref_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim, const int32_t *positions,
                    const float *cos_tab, const float *sin_tab, const float *q_gain, const float *k_gain, float eps,
-                   const int32_t *slots, float *q_out, int8_t *k_cache, float *k_scale, int8_t *v_cache,
-                   float *v_scale);
+                   const int32_t *slots, int64_t n_slots, float *q_out, int8_t *k_cache, float *k_scale,
+                   int8_t *v_cache, float *v_scale);
 
 /* Decode attention over the Q8 KV cache, one query row per sequence:
  *   for query head h (kv head h / (n_heads / n_kv)), keys j < len[s] at slot
- *   base[s] + j, dequantized k = q * d and v = q * d (exact in fp64):
+ *   base[s] + j (base[s] + len[s] <= n_slots), dequantized k = q * d and
+ *   v = q * d (exact in fp64):
  *   s_j = scale * sum_d q_d k_jd;  p_j = exp(s_j - max);  out = sum p_j v_j / sum p_j
  * all in fp64, out rounded once to fp32.  bound (may be NULL) receives, per
  * output, an fp64 error budget for an fp32 evaluation whose dot products are
@@ -204,8 +206,8 @@ int q8ref_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int 
  *   (sum_j p_j |v_jd| * (scale * S_j * 2 (head_dim + 2) u + (96 + len/256) u))
  *   / sum_j p_j + 2 u |out|,  S_j = sum_d |q_d k_jd|,  u = 2^-24. */
 int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,
-                           const float *k_scale, const int8_t *v_cache, const float *v_scale, const int32_t *base,
-                           const int32_t *len, float scale, float *out, double *bound);
+                           const float *k_scale, const int8_t *v_cache, const float *v_scale, int64_t n_slots,
+                           const int32_t *base, const int32_t *len, float scale, float *out, double *bound);
 
 #ifdef __cplusplus
 }

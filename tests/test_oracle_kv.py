@@ -36,11 +36,11 @@ def test_write_identity_rotation_quantizes_raw_rows(hd):
     q, kc, ks, vc, vs = _write(qkv, H, Hk, hd, np.zeros(T, np.int32), _identity_tables(1, hd))
     assert np.array_equal(q.reshape(T, -1), qkv[:, :H * hd])
     for cache, scale, off in ((kc, ks, H * hd), (vc, vs, (H + Hk) * hd)):
-        rows = qkv[:, off:off + Hk * hd].reshape(T * Hk, hd)
+        rows = qkv[:, off:off + Hk * hd].reshape(T, Hk, hd).transpose(1, 0, 2).reshape(Hk * T, hd)
         codes, _ = oracle.act_planes(oracle.quantize_rows(rows, oracle.LAYOUT_ACT), T * Hk, hd)
-        assert np.array_equal(cache.reshape(T * Hk, hd), codes)
+        assert np.array_equal(cache.reshape(Hk * T, hd), codes)
         amax = np.abs(rows.reshape(T * Hk, hd // 32, 32)).max(axis=2)
-        assert np.array_equal(scale.reshape(T * Hk, hd // 32), (amax / np.float32(127.0)).astype(np.float32))
+        assert np.array_equal(scale.reshape(Hk * T, hd // 32), (amax / np.float32(127.0)).astype(np.float32))
 
 
 def test_write_rope_against_fp64_rotation():
@@ -93,31 +93,32 @@ def test_write_layout_and_slots():
         for h in range(H):
             assert np.all(q[t, h] == 10 * t + h + 1)
         for j in range(Hk):
-            assert np.all(kc[slots[t], j] == 127) and np.all(vc[slots[t], j] == 127)
-            assert np.all(ks[slots[t], j] == np.float32(10 * t + H + j + 1) / np.float32(127))
-            assert np.all(vs[slots[t], j] == np.float32(10 * t + H + Hk + j + 1) / np.float32(127))
+            assert np.all(kc[j, slots[t]] == 127) and np.all(vc[j, slots[t]] == 127)
+            assert np.all(ks[j, slots[t]] == np.float32(10 * t + H + j + 1) / np.float32(127))
+            assert np.all(vs[j, slots[t]] == np.float32(10 * t + H + Hk + j + 1) / np.float32(127))
     unused = [i for i in range(12) if i not in slots]
-    assert not kc[unused].any() and not vs[unused].any()
+    assert not kc[:, unused].any() and not vs[:, unused].any()
 
 
 def _cache(seed, slots, Hk, hd, scale_v=1.0):
+    """A random head-major cache: int8 [Hk][slots][hd], fp32 scales [Hk][slots][hd/32]."""
     g = _rng(seed)
-    kc = g.integers(-127, 128, (slots, Hk, hd)).astype(np.int8)
-    vc = g.integers(-127, 128, (slots, Hk, hd)).astype(np.int8)
-    ks = (g.random((slots, Hk, hd // 32)) * 0.02).astype(np.float32)
-    vs = (g.random((slots, Hk, hd // 32)) * 0.02 * scale_v).astype(np.float32)
+    kc = g.integers(-127, 128, (Hk, slots, hd)).astype(np.int8)
+    vc = g.integers(-127, 128, (Hk, slots, hd)).astype(np.int8)
+    ks = (g.random((Hk, slots, hd // 32)) * 0.02).astype(np.float32)
+    vs = (g.random((Hk, slots, hd // 32)) * 0.02 * scale_v).astype(np.float32)
     return kc, ks, vc, vs
 
 
 def _numpy_attention(q, kc, ks, vc, vs, base, length, scale):
     S, H, hd = q.shape
-    G = H // kc.shape[1]
+    G = H // kc.shape[0]
     out = np.empty((S, H, hd))
     for s in range(S):
         sl = slice(base[s], base[s] + length[s])
         for h in range(H):
-            k = kc[sl, h // G].astype(np.float64) * np.repeat(ks[sl, h // G].astype(np.float64), 32, axis=1)
-            v = vc[sl, h // G].astype(np.float64) * np.repeat(vs[sl, h // G].astype(np.float64), 32, axis=1)
+            k = kc[h // G, sl].astype(np.float64) * np.repeat(ks[h // G, sl].astype(np.float64), 32, axis=1)
+            v = vc[h // G, sl].astype(np.float64) * np.repeat(vs[h // G, sl].astype(np.float64), 32, axis=1)
             sc = scale * (k @ q[s, h].astype(np.float64))
             p = np.exp(sc - sc.max())
             out[s, h] = (p[:, None] * v).sum(0) / p.sum()
@@ -145,14 +146,14 @@ def test_attention_closed_forms():
     out, _ = oracle.attention_decode(q, kc, ks, vc, vs, np.array([10, 20], np.int32), np.array([1, 1], np.int32), 0.125)
     for s, slot in ((0, 10), (1, 20)):
         for h in range(H):
-            v = (vc[slot, h // 2].astype(np.float64) * np.repeat(vs[slot, h // 2], 32)).astype(np.float32)
+            v = (vc[h // 2, slot].astype(np.float64) * np.repeat(vs[h // 2, slot], 32)).astype(np.float32)
             assert np.array_equal(out[s, h], v)
     # scale 0: uniform weights, the mean of the value rows
     out0, _ = oracle.attention_decode(q, kc, ks, vc, vs, np.array([0, 0], np.int32), np.array([64, 7], np.int32), 0.0)
     for s, L in ((0, 64), (1, 7)):
-        v = vc[:L, :].astype(np.float64) * np.repeat(vs[:L], 32, axis=2)
+        v = vc[:, :L].astype(np.float64) * np.repeat(vs[:, :L], 32, axis=2)
         for h in range(H):
-            assert np.allclose(out0[s, h], v[:, h // 2].mean(0), rtol=1e-6, atol=1e-9)
+            assert np.allclose(out0[s, h], v[h // 2].mean(0), rtol=1e-6, atol=1e-9)
 
 
 def test_attention_fp32_evaluation_within_bound():
@@ -163,8 +164,8 @@ def test_attention_fp32_evaluation_within_bound():
     q = (_rng(9).standard_normal((1, H, hd)) * 4).astype(np.float32)
     scale = np.float32(1 / 8)
     out, bound = oracle.attention_decode(q, kc, ks, vc, vs, np.array([0], np.int32), np.array([L], np.int32), scale)
-    k = (kc[:, 0].astype(np.float32) * np.repeat(ks[:, 0], 32, axis=1)).astype(np.float32)
-    v = (vc[:, 0].astype(np.float32) * np.repeat(vs[:, 0], 32, axis=1)).astype(np.float32)
+    k = (kc[0].astype(np.float32) * np.repeat(ks[0], 32, axis=1)).astype(np.float32)
+    v = (vc[0].astype(np.float32) * np.repeat(vs[0], 32, axis=1)).astype(np.float32)
     for h in range(H):
         sc = np.array([np.float32(scale) * np.float32(np.dot(k[j], q[0, h])) for j in range(L)], np.float32)
         p = np.exp(sc - sc.max()).astype(np.float32)
