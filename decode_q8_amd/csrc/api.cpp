@@ -241,6 +241,70 @@ int q8_moe_combine(const float *y, int64_t ld_y, const float *weights, int64_t t
     return launched(q8k::launch_moe_combine(y, ld_y, weights, tokens, topk, n, out, ld_out, stream));
 }
 
+int q8_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim, const int32_t *positions,
+                int64_t max_pos, const float *cos_tab, const float *sin_tab, const float *q_gain, const float *k_gain,
+                float eps, const int32_t *slots, int64_t n_slots, float *q_out, int8_t *k_cache, float *k_scale,
+                int8_t *v_cache, float *v_scale, int32_t *status, hipStream_t stream) {
+    if (!qkv || !positions || !cos_tab || !sin_tab || !slots || !q_out || !k_cache || !k_scale || !v_cache ||
+        !v_scale || tokens < 0 || n_heads <= 0 || n_kv <= 0 || max_pos <= 0 || n_slots <= 0)
+        return Q8_ERR_ARG;
+    if ((q_gain || k_gain) && (!(eps >= 0.0f) || eps > 3.4e38f)) return Q8_ERR_ARG;
+    if (n_heads % n_kv || (head_dim != 64 && head_dim != 128 && head_dim != 256)) return Q8_ERR_SHAPE;
+    if (tokens > INT32_MAX || max_pos > INT32_MAX || (int64_t)tokens * (n_heads + 2 * n_kv) * head_dim > INT64_MAX / 8)
+        return Q8_ERR_SHAPE;
+    if (!aligned16(qkv) || !aligned16(cos_tab) || !aligned16(sin_tab) || !aligned16(q_gain) || !aligned16(k_gain) ||
+        !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)k_scale & 3u) ||
+        ((uintptr_t)v_scale & 3u) || ((uintptr_t)positions & 3u) || ((uintptr_t)slots & 3u) ||
+        ((uintptr_t)status & 3u))
+        return Q8_ERR_ALIGN;
+    if (tokens == 0) return Q8_OK;
+    if (overlap(q_out, (size_t)tokens * n_heads * head_dim * 4, qkv,
+                (size_t)tokens * (n_heads + 2 * n_kv) * head_dim * 4))
+        return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_kv_write(qkv, tokens, n_heads, n_kv, head_dim, positions, max_pos, cos_tab, sin_tab,
+                                         q_gain, k_gain, eps, slots, n_slots, q_out, k_cache, k_scale, v_cache,
+                                         v_scale, status, stream));
+}
+
+static bool attention_shape_ok(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len) {
+    if (seqs < 0 || n_heads <= 0 || n_kv <= 0 || max_len <= 0 || n_heads % n_kv) return false;
+    const int G = n_heads / n_kv;
+    return (head_dim == 64 || head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8) && max_len <= INT32_MAX &&
+           seqs <= 65535 && n_kv <= 65535;
+}
+
+size_t q8_attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len) {
+    if (!attention_shape_ok(seqs, n_heads, n_kv, head_dim, max_len)) return 0;
+    return q8k::attention_workspace_bytes(seqs, n_heads, n_kv, head_dim, max_len);
+}
+
+int q8_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,
+                        const float *k_scale, const int8_t *v_cache, const float *v_scale, int64_t n_slots,
+                        const int32_t *base, const int32_t *len, int64_t max_len, float scale, float *out,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k_cache || !k_scale || !v_cache || !v_scale || !base || !len || !out || seqs < 0 || n_heads <= 0 ||
+        n_kv <= 0 || n_slots <= 0 || max_len <= 0)
+        return Q8_ERR_ARG;
+    if (!(scale == scale) || scale > 3.4e38f || scale < -3.4e38f) return Q8_ERR_ARG;
+    if (!attention_shape_ok(seqs, n_heads, n_kv, head_dim, max_len)) return Q8_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)k_scale & 3u) ||
+        ((uintptr_t)v_scale & 3u) || ((uintptr_t)base & 3u) || ((uintptr_t)len & 3u))
+        return Q8_ERR_ALIGN;
+    if (seqs == 0) return Q8_OK;
+    const size_t need = q8k::attention_workspace_bytes(seqs, n_heads, n_kv, head_dim, max_len);
+    if (!workspace || workspace_bytes < need) return Q8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return Q8_ERR_ALIGN;
+    if (overlap(out, (size_t)seqs * n_heads * head_dim * 4, q, (size_t)seqs * n_heads * head_dim * 4) ||
+        overlap(workspace, need, out, (size_t)seqs * n_heads * head_dim * 4))
+        return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_attention_decode(q, seqs, n_heads, n_kv, head_dim, k_cache, k_scale, v_cache, v_scale,
+                                                 n_slots, base, len, max_len, scale, out, workspace, stream));
+}
+
 size_t q8_grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts, int64_t n, int64_t k) {
     (void)n;
     (void)k;

@@ -1,0 +1,403 @@
+// Q8 KV cache ("ferro" README, "KV cache": K/V rows stored as int8 with one
+// fp32 scale per 32 values, quantized in the fused norm + rope + cache-write
+// kernel and dequantized inside attention).
+//
+// kv_write_kernel: for each token and head of a fused QKV row, HD/4 lanes hold
+// the head (4 values each).  Optional per-head RMSNorm (fp64 sum of squares:
+// one partial per lane over its 4 values in order, then a halving fold over
+// the lanes), rotary embedding in the half-split layout from caller tables
+// (the partner value i +- HD/2 is HD/8 lanes away), then K and V heads are
+// quantized per 32 values (8 lanes, 3-step butterfly for the amax) with the
+// scale kept in fp32, into a head-major cache [kv head][slot][HD].
+//
+// attn_partial_kernel / attn_combine_kernel: decode attention (one query row
+// per sequence) in fixed chunks of 256 cached positions, so the arithmetic of
+// a sequence depends only on its own length.  A workgroup takes one chunk of
+// one (sequence, kv head) for the G query heads sharing that kv head: each of
+// its 4 waves scores 64 keys (lane = key: the key row is dequantized once and
+// dotted with the G queries), the chunk's softmax runs in the exp2 domain,
+// then the lanes turn to dimensions and accumulate p * v over the wave's keys
+// from LDS; the 4 waves' sums are added in order.  The combine kernel rescales
+// the chunks' (max, sum, weighted sum) and divides, chunks in order.
+#include <math.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace q8k {
+
+// ---------------------------------------------------------------------------
+// Fused norm + rope + cache write
+// ---------------------------------------------------------------------------
+
+template <int HD>
+__global__ __launch_bounds__(256) void kv_write_kernel(const float *__restrict__ qkv, int32_t tokens, int32_t n_heads,
+                                                       int32_t n_kv, const int32_t *__restrict__ positions,
+                                                       int32_t max_pos, const float *__restrict__ cos_tab,
+                                                       const float *__restrict__ sin_tab,
+                                                       const float *__restrict__ q_gain,
+                                                       const float *__restrict__ k_gain, float eps,
+                                                       const int32_t *__restrict__ slots, int64_t n_slots,
+                                                       float *__restrict__ q_out, int8_t *__restrict__ k_cache,
+                                                       float *__restrict__ k_scale, int8_t *__restrict__ v_cache,
+                                                       float *__restrict__ v_scale, int32_t *__restrict__ status) {
+    constexpr int LPH = HD / 4;  // lanes per head (16, 32 or 64: heads never straddle waves)
+    constexpr int NB = HD / 32;
+    const int heads = n_heads + 2 * n_kv;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t grp = gid / LPH;
+    const int l = (int)(gid % LPH);
+    bool valid = grp < (int64_t)tokens * heads;
+    const int t = valid ? (int)(grp / heads) : 0;
+    const int h = valid ? (int)(grp % heads) : 0;
+    const int kind = h < n_heads ? 0 : (h < n_heads + n_kv ? 1 : 2);  // q, k, v
+    int pos = 0;
+    int64_t slot = 0;
+    if (valid) {
+        pos = positions[t];
+        slot = slots[t];
+        if (pos < 0 || pos >= max_pos || slot < 0 || slot >= n_slots) {
+            if (status && l == 0) __hip_atomic_store(status, 1 /* Q8_ERR_ARG */, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+            valid = false;
+        }
+    }
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+        const float4 v = *reinterpret_cast<const float4 *>(qkv + ((int64_t)t * heads + h) * HD + 4 * l);
+        x[0] = v.x;
+        x[1] = v.y;
+        x[2] = v.z;
+        x[3] = v.w;
+    }
+    // per-head RMSNorm (every lane joins the shuffles; applied where a gain is given)
+    const float *gain = kind == 0 ? q_gain : (kind == 1 ? k_gain : nullptr);
+    double p = (double)x[0] * (double)x[0];
+    p += (double)x[1] * (double)x[1];
+    p += (double)x[2] * (double)x[2];
+    p += (double)x[3] * (double)x[3];
+#pragma unroll
+    for (int s = LPH / 2; s >= 1; s >>= 1) p += __shfl_down(p, s, LPH);
+    const double ss = __shfl(p, 0, LPH);
+    if (valid && gain) {
+        const float r = (float)(1.0 / sqrt(ss / (double)HD + (double)eps));
+        const float4 g = *reinterpret_cast<const float4 *>(gain + 4 * l);
+        const float gg[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float xr = x[e] * r;
+            x[e] = xr * gg[e];
+        }
+    }
+    // rotary embedding of q and k: lane l < LPH/2 holds x_i, its partner x_{i+HD/2}
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) y[e] = __shfl_xor(x[e], LPH / 2, LPH);
+    if (valid && kind != 2) {
+        const bool lo = l < LPH / 2;
+        const int i0 = 4 * (lo ? l : l - LPH / 2);
+        const float4 c4 = *reinterpret_cast<const float4 *>(cos_tab + (int64_t)pos * (HD / 2) + i0);
+        const float4 s4 = *reinterpret_cast<const float4 *>(sin_tab + (int64_t)pos * (HD / 2) + i0);
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            if (lo) {  // x_i = a, partner b = x_{i+h}
+                const float ac = x[e] * cc[e], bs = y[e] * sn[e];
+                x[e] = ac - bs;
+            } else {   // x_{i+h} = b, partner a = x_i
+                const float bc = x[e] * cc[e], as = y[e] * sn[e];
+                x[e] = bc + as;
+            }
+        }
+    }
+    // quantize K and V per 32 values (8 lanes), scale kept in fp32
+    float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    if (!valid) return;
+    if (kind == 0) {
+        *reinterpret_cast<float4 *>(q_out + ((int64_t)t * n_heads + h) * HD + 4 * l) =
+            make_float4(x[0], x[1], x[2], x[3]);
+        return;
+    }
+    const float d = amax / 127.0f;
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        int qv = 0;
+        if (d != 0.0f) qv = (int)roundf(x[e] / d);
+        packed |= ((uint32_t)qv & 0xffu) << (8 * e);
+    }
+    const int kvh = kind == 1 ? h - n_heads : h - n_heads - n_kv;
+    const int64_t row = (int64_t)kvh * n_slots + slot;
+    int8_t *cache = kind == 1 ? k_cache : v_cache;
+    float *scale = kind == 1 ? k_scale : v_scale;
+    *reinterpret_cast<uint32_t *>(cache + row * HD + 4 * l) = packed;
+    if ((l & 7) == 0) scale[row * NB + (l >> 3)] = d;
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention
+// ---------------------------------------------------------------------------
+
+constexpr int ATT_CHUNK = 256;  // cached positions per workgroup (4 waves x 64)
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float x) {
+    // butterfly: every lane ends with the same sum, in one fixed order
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s);
+    return x;
+}
+
+__device__ __forceinline__ float byte_f32(uint32_t w, int i) {
+    return (float)((int32_t)(w << (24 - 8 * i)) >> 24);  // sign-extended int8 -> exact fp32
+}
+
+// A sequence's cached range is usable: 1 <= len <= max_len, inside the cache.
+__device__ __forceinline__ bool seq_ok(int32_t b, int32_t L, int32_t max_len, int64_t n_slots) {
+    return L >= 1 && L <= max_len && b >= 0 && (int64_t)b + L <= n_slots;
+}
+
+// Partial results per (sequence, kv head, chunk): for each of the G heads the
+// chunk maximum (log2 domain), the chunk sum of p and the HD weighted sums.
+template <int HD, int G>
+__global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restrict__ q, int32_t n_heads,
+                                                           int32_t n_kv, const int8_t *__restrict__ k_cache,
+                                                           const float *__restrict__ k_scale,
+                                                           const int8_t *__restrict__ v_cache,
+                                                           const float *__restrict__ v_scale, int64_t n_slots,
+                                                           const int32_t *__restrict__ base,
+                                                           const int32_t *__restrict__ len, int32_t max_len,
+                                                           float scale_log2, float *__restrict__ part,
+                                                           int32_t *__restrict__ status) {
+    constexpr int NB = HD / 32;
+    constexpr int W16 = HD / 16;  // 16-byte words per cached row
+    constexpr int DPL = HD / 64;  // dimensions per lane in the weighted sum
+    __shared__ __align__(16) int8_t vt[4][64][HD];
+    __shared__ float vsc[4][64][NB];
+    __shared__ __align__(16) float pl[4][64][G];
+    __shared__ float accw[4][G][HD];
+    __shared__ float redm[4][G], reds[4][G];
+    const int sp = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    const int splits = gridDim.x;
+    if ((sp | kvh | s) == 0 && threadIdx.x == 0)  // the status word of this call starts clear
+        __hip_atomic_store(status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t L = len[s], b0 = base[s];
+    if (!seq_ok(b0, L, max_len, n_slots)) return;  // the combine kernel reports it
+    const int c0 = sp * ATT_CHUNK;
+    if (c0 >= L) return;  // the whole workgroup: this chunk is past the sequence
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+
+    // the G query rows: the same for every lane, read with scalar loads
+    const float *qg = q + ((int64_t)s * n_heads + (int64_t)kvh * G) * HD;
+
+    const int j = c0 + 64 * w + lane;
+    const bool valid = j < L;
+    const int64_t row = (int64_t)kvh * n_slots + b0 + (valid ? j : 0);
+    uint4 kr[W16];
+    float ks[NB];
+#pragma unroll
+    for (int i = 0; i < W16; i++) {
+        kr[i] = valid ? reinterpret_cast<const uint4 *>(k_cache + row * HD)[i] : make_uint4(0, 0, 0, 0);
+        const uint4 vv = valid ? reinterpret_cast<const uint4 *>(v_cache + row * HD)[i] : make_uint4(0, 0, 0, 0);
+        reinterpret_cast<uint4 *>(&vt[w][lane][0])[i] = vv;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        ks[b] = valid ? k_scale[row * NB + b] : 0.0f;
+        vsc[w][lane][b] = valid ? v_scale[row * NB + b] : 0.0f;
+    }
+    __syncthreads();
+
+    // scores of this lane's key for the G heads, per 32-value block then scaled
+    float sc[G];
+#pragma unroll
+    for (int g = 0; g < G; g++) sc[g] = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        float kf[32];  // this block's 32 key values, converted once for the G heads
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const uint4 &u = kr[b * 2 + i / 16];
+            const uint32_t word = (i & 15) < 4 ? u.x : (i & 15) < 8 ? u.y : (i & 15) < 12 ? u.z : u.w;
+            kf[i] = byte_f32(word, i & 3);
+        }
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; i += 4) {
+                const float4 qv = *reinterpret_cast<const float4 *>(qg + g * HD + 32 * b + i);
+                a = a + qv.x * kf[i];
+                a = a + qv.y * kf[i + 1];
+                a = a + qv.z * kf[i + 2];
+                a = a + qv.w * kf[i + 3];
+            }
+            sc[g] = sc[g] + a * ks[b];
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; g++) sc[g] = valid ? sc[g] * scale_log2 : -INFINITY;
+
+    // chunk softmax (exp2 domain): maximum over the 4 waves, then p and its sum
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const float m = wave_max_f32(sc[g]);
+        if (lane == 0) redm[w][g] = m;
+    }
+    __syncthreads();
+    float p[G];
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+        const float m = fmaxf(fmaxf(redm[0][g], redm[1][g]), fmaxf(redm[2][g], redm[3][g]));
+        p[g] = valid ? __builtin_amdgcn_exp2f(sc[g] - m) : 0.0f;
+        pl[w][lane][g] = p[g];
+        const float ls = wave_sum_f32(p[g]);
+        if (lane == 0) reds[w][g] = ls;
+    }
+    __syncthreads();
+
+    // weighted sum of V over this wave's 64 keys: lanes are dimensions now
+    float acc[DPL][G];
+#pragma unroll
+    for (int e = 0; e < DPL; e++)
+#pragma unroll
+        for (int g = 0; g < G; g++) acc[e][g] = 0.0f;
+#pragma unroll 4
+    for (int jj = 0; jj < 64; jj++) {
+        float pj[G];
+#pragma unroll
+        for (int g = 0; g < G; g++) pj[g] = pl[w][jj][g];
+#pragma unroll
+        for (int e = 0; e < DPL; e++) {
+            const int d = lane + 64 * e;
+            const float vv = (float)vt[w][jj][d] * vsc[w][jj][d >> 5];
+#pragma unroll
+            for (int g = 0; g < G; g++) acc[e][g] = acc[e][g] + pj[g] * vv;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; e++)
+#pragma unroll
+        for (int g = 0; g < G; g++) accw[w][g][lane + 64 * e] = acc[e][g];
+    __syncthreads();
+
+    float *o = part + (((int64_t)s * n_kv + kvh) * splits + sp) * (G * (HD + 2));
+    for (int i = tid; i < G * HD; i += 256) {
+        const int g = i / HD, d = i % HD;
+        o[g * (HD + 2) + 2 + d] = ((accw[0][g][d] + accw[1][g][d]) + accw[2][g][d]) + accw[3][g][d];
+    }
+    if (tid < G) {
+        const int g = tid;
+        o[g * (HD + 2)] = fmaxf(fmaxf(redm[0][g], redm[1][g]), fmaxf(redm[2][g], redm[3][g]));
+        o[g * (HD + 2) + 1] = ((reds[0][g] + reds[1][g]) + reds[2][g]) + reds[3][g];
+    }
+}
+
+template <int HD, int G>
+__global__ __launch_bounds__(64) void attn_combine_kernel(int32_t n_heads, int32_t n_kv, int64_t n_slots,
+                                                          const int32_t *__restrict__ base,
+                                                          const int32_t *__restrict__ len, int32_t max_len,
+                                                          int32_t splits, const float *__restrict__ part,
+                                                          float *__restrict__ out, int32_t *__restrict__ status) {
+    constexpr int DPL = HD / 64;
+    const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+    const int kvh = h / G, g = h % G;
+    const int32_t L = len[s];
+    float *o = out + ((int64_t)s * n_heads + h) * HD;
+    if (!seq_ok(base[s], L, max_len, n_slots)) {
+        if (lane == 0) __hip_atomic_store(status, 1 /* Q8_ERR_ARG */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int e = 0; e < DPL; e++) o[lane + 64 * e] = __builtin_nanf("");
+        return;
+    }
+    const int nsp = (L + ATT_CHUNK - 1) / ATT_CHUNK;
+    const float *pb = part + ((int64_t)s * n_kv + kvh) * splits * (G * (HD + 2)) + g * (HD + 2);
+    float M = -INFINITY;
+    for (int c = 0; c < nsp; c++) M = fmaxf(M, pb[(int64_t)c * G * (HD + 2)]);
+    float den = 0.0f, num[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; e++) num[e] = 0.0f;
+    for (int c = 0; c < nsp; c++) {
+        const float *pc = pb + (int64_t)c * G * (HD + 2);
+        const float f = __builtin_amdgcn_exp2f(pc[0] - M);
+        den = den + f * pc[1];
+#pragma unroll
+        for (int e = 0; e < DPL; e++) num[e] = num[e] + f * pc[2 + lane + 64 * e];
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; e++) o[lane + 64 * e] = num[e] / den;
+}
+
+// Host side ---------------------------------------------------------------
+
+hipError_t launch_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim,
+                           const int32_t *positions, int64_t max_pos, const float *cos_tab, const float *sin_tab,
+                           const float *q_gain, const float *k_gain, float eps, const int32_t *slots, int64_t n_slots,
+                           float *q_out, int8_t *k_cache, float *k_scale, int8_t *v_cache, float *v_scale,
+                           int32_t *status, hipStream_t s) {
+    const int64_t threads = tokens * (n_heads + 2 * n_kv) * (head_dim / 4);
+    if (threads == 0) return hipSuccess;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+#define Q8_KVW(HD)                                                                                                 \
+    hipLaunchKernelGGL(kv_write_kernel<HD>, grid, dim3(256), 0, s, qkv, (int32_t)tokens, n_heads, n_kv, positions, \
+                       (int32_t)max_pos, cos_tab, sin_tab, q_gain, k_gain, eps, slots, n_slots, q_out, k_cache,   \
+                       k_scale, v_cache, v_scale, status)
+    switch (head_dim) {
+        case 64: Q8_KVW(64); break;
+        case 128: Q8_KVW(128); break;
+        case 256: Q8_KVW(256); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef Q8_KVW
+    return hipGetLastError();
+}
+
+size_t attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len) {
+    const int64_t splits = (max_len + ATT_CHUNK - 1) / ATT_CHUNK;
+    return 256 + (size_t)seqs * n_kv * splits * (n_heads / n_kv) * (head_dim + 2) * 4;
+}
+
+template <int HD, int G>
+static hipError_t launch_attn(const float *q, int64_t seqs, int n_heads, int n_kv, const int8_t *k_cache,
+                              const float *k_scale, const int8_t *v_cache, const float *v_scale, int64_t n_slots,
+                              const int32_t *base, const int32_t *len, int64_t max_len, float scale, float *out,
+                              void *ws, hipStream_t s) {
+    const int32_t splits = (int32_t)((max_len + ATT_CHUNK - 1) / ATT_CHUNK);
+    int32_t *status = (int32_t *)ws;
+    float *part = (float *)((uint8_t *)ws + 256);
+    const float scale_log2 = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL((attn_partial_kernel<HD, G>), dim3((unsigned)splits, (unsigned)n_kv, (unsigned)seqs), dim3(256),
+                       0, s, q, n_heads, n_kv, k_cache, k_scale, v_cache, v_scale, n_slots, base, len,
+                       (int32_t)max_len, scale_log2, part, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_combine_kernel<HD, G>), dim3((unsigned)n_heads, (unsigned)seqs), dim3(64), 0, s, n_heads,
+                       n_kv, n_slots, base, len, (int32_t)max_len, splits, part, out, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim,
+                                   const int8_t *k_cache, const float *k_scale, const int8_t *v_cache,
+                                   const float *v_scale, int64_t n_slots, const int32_t *base, const int32_t *len,
+                                   int64_t max_len, float scale, float *out, void *ws, hipStream_t s) {
+    if (seqs == 0) return hipSuccess;
+    const int G = n_heads / n_kv;
+#define Q8_ATT(HD, GG) \
+    if (head_dim == HD && G == GG) \
+        return launch_attn<HD, GG>(q, seqs, n_heads, n_kv, k_cache, k_scale, v_cache, v_scale, n_slots, base, len, \
+                                   max_len, scale, out, ws, s);
+    Q8_ATT(64, 1) Q8_ATT(64, 2) Q8_ATT(64, 4) Q8_ATT(64, 8)
+    Q8_ATT(128, 1) Q8_ATT(128, 2) Q8_ATT(128, 4) Q8_ATT(128, 8)
+#undef Q8_ATT
+    return hipErrorInvalidValue;
+}
+
+}  // namespace q8k

@@ -61,6 +61,18 @@ hipError_t launch_swiglu_quantize(const float *gate, int64_t ld_gate, const floa
 hipError_t launch_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t tokens, int topk, int64_t n,
                               float *out, int64_t ld_out, hipStream_t s);
 
+// Q8 KV cache: fused norm + rope + cache write; decode attention.
+hipError_t launch_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim,
+                           const int32_t *positions, int64_t max_pos, const float *cos_tab, const float *sin_tab,
+                           const float *q_gain, const float *k_gain, float eps, const int32_t *slots, int64_t n_slots,
+                           float *q_out, int8_t *k_cache, float *k_scale, int8_t *v_cache, float *v_scale,
+                           int32_t *status, hipStream_t s);
+size_t attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len);
+hipError_t launch_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim,
+                                   const int8_t *k_cache, const float *k_scale, const int8_t *v_cache,
+                                   const float *v_scale, int64_t n_slots, const int32_t *base, const int32_t *len,
+                                   int64_t max_len, float scale, float *out, void *ws, hipStream_t s);
+
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s);
 

@@ -50,6 +50,11 @@ SIGNATURES = {
     "q8_moe_route": ([_P, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "q8_swiglu_quantize": ([_P, _I64, _P, _I64, _I64, _I64, _P, _P], _I),
     "q8_moe_combine": ([_P, _I64, _P, _I64, _I, _I64, _P, _I64, _P], _I),
+    "q8_kv_write": ([_P, _I64, _I, _I, _I, _P, _I64, _P, _P, _P, _P, ctypes.c_float, _P, _I64, _P, _P, _P, _P, _P,
+                     _P, _P], _I),
+    "q8_attention_workspace_bytes": ([_I64, _I, _I, _I, _I64], _SZ),
+    "q8_attention_decode": ([_P, _I64, _I, _I, _I, _P, _P, _P, _P, _I64, _P, _P, _I64, ctypes.c_float, _P, _P, _SZ,
+                             _P], _I),
     "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
     "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
 }
@@ -188,6 +193,28 @@ def q8_swiglu_quantize(gate, ld_gate: int, up, ld_up: int, rows: int, n: int, q_
 def q8_moe_combine(y, ld_y: int, weights, tokens: int, topk: int, n: int, out, ld_out: int, stream=None) -> int:
     return _check(lib().q8_moe_combine(_ptr(y), ld_y, _ptr(weights), tokens, topk, n, _ptr(out), ld_out,
                                        _stream(stream)), "q8_moe_combine")
+
+
+def q8_kv_write(qkv, tokens: int, n_heads: int, n_kv: int, head_dim: int, positions, max_pos: int, cos_tab, sin_tab,
+                q_gain, k_gain, eps: float, slots, n_slots: int, q_out, k_cache, k_scale, v_cache, v_scale,
+                status=None, stream=None) -> int:
+    return _check(lib().q8_kv_write(_ptr(qkv), tokens, n_heads, n_kv, head_dim, _ptr(positions), max_pos,
+                                    _ptr(cos_tab), _ptr(sin_tab), _ptr(q_gain), _ptr(k_gain), float(eps), _ptr(slots),
+                                    n_slots, _ptr(q_out), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+                                    _ptr(status), _stream(stream)), "q8_kv_write")
+
+
+def q8_attention_workspace_bytes(seqs: int, n_heads: int, n_kv: int, head_dim: int, max_len: int) -> int:
+    return lib().q8_attention_workspace_bytes(seqs, n_heads, n_kv, head_dim, max_len)
+
+
+def q8_attention_decode(q, seqs: int, n_heads: int, n_kv: int, head_dim: int, k_cache, k_scale, v_cache, v_scale,
+                        n_slots: int, base, length, max_len: int, scale: float, out, workspace, workspace_bytes: int,
+                        stream=None) -> int:
+    return _check(lib().q8_attention_decode(_ptr(q), seqs, n_heads, n_kv, head_dim, _ptr(k_cache), _ptr(k_scale),
+                                            _ptr(v_cache), _ptr(v_scale), n_slots, _ptr(base), _ptr(length), max_len,
+                                            float(scale), _ptr(out), _ptr(workspace), workspace_bytes,
+                                            _stream(stream)), "q8_attention_decode")
 
 
 def q8_grouped_matmul(x_q, x_rows: int, x_per_pair: int, topk_ids, tokens: int, topk: int, w_experts,

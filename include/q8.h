@@ -71,8 +71,8 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 3u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize and the
-                              MoE router, SwiGLU and combine entry points */
+#define Q8_ABI_VERSION 3u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize, the
+                              MoE router, SwiGLU and combine, and the Q8 KV cache entry points */
 #define Q8_BLOCK 32          /* values per block */
 #define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
 #define Q8_TILE_ROWS 64      /* rows per packed record */
@@ -323,6 +323,67 @@ int q8_swiglu_quantize(const float *gate, int64_t ld_gate, const float *up, int6
  *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_moe_combine(const float *y, int64_t ld_y, const float *weights, int64_t tokens, int topk, int64_t n, float *out,
                    int64_t ld_out, hipStream_t stream);
+
+/* ---- Q8 KV cache ("ferro" README, "KV cache": K/V rows stored as int8 with
+ * one fp32 scale per 32 values, quantized in the fused norm + rope +
+ * cache-write kernel, dequantized inside attention).  Cache layout, head-major
+ * so that one head's positions are contiguous:
+ *   k_cache, v_cache  int8 [n_kv][n_slots][head_dim]
+ *   k_scale, v_scale  fp32 [n_kv][n_slots][head_dim / 32]
+ * A block of 32 values x is stored as d = fp32(amax / 127) (kept in fp32) and
+ * q = round(x / d) (ties away from zero; d = 0 gives q = 0). */
+
+/* Fused per-head norm + rotary embedding + KV cache write for `tokens` rows
+ * of a fused QKV projection.
+ *  qkv        device fp32 [tokens][(n_heads + 2 n_kv) head_dim]: n_heads
+ *             query heads, then n_kv key heads, then n_kv value heads.
+ *  positions  device int32 [tokens], each in [0, max_pos).
+ *  cos_tab, sin_tab  device fp32 [max_pos][head_dim / 2] (model constants).
+ *  q_gain, k_gain    device fp32 [head_dim] or NULL: per-head RMSNorm of the
+ *             query / key heads before the rotation (ss = sum of x^2 in fp64
+ *             as head_dim/4 partials of 4 consecutive values, folded
+ *             p_c += p_{c+s} for s = head_dim/8 .. 1; r = fp32(1 / sqrt(ss /
+ *             head_dim + eps)); x = fp32(fp32(x * r) * gain)).
+ *  rotation   half-split: for i < head_dim/2 with c, s = tables[pos][i]:
+ *             x_i <- fp32(fp32(x_i c) - fp32(x_{i+h} s)),
+ *             x_{i+h} <- fp32(fp32(x_{i+h} c) + fp32(x_i s)),  h = head_dim/2.
+ *  slots      device int32 [tokens], each in [0, n_slots): the cache slot of
+ *             every head of that token.
+ *  q_out      device fp32 [tokens][n_heads][head_dim]: normalized, rotated q.
+ *  status     device int32 or NULL: set to Q8_ERR_ARG (never cleared) if a
+ *             position or slot is out of range; that token is not written.
+ *  head_dim in {64, 128, 256}; n_heads % n_kv == 0; all fp32 and int8 arrays
+ *  16-byte aligned except the scales (4-byte).  tokens == 0 is a no-op.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int head_dim, const int32_t *positions,
+                int64_t max_pos, const float *cos_tab, const float *sin_tab, const float *q_gain, const float *k_gain,
+                float eps, const int32_t *slots, int64_t n_slots, float *q_out, int8_t *k_cache, float *k_scale,
+                int8_t *v_cache, float *v_scale, int32_t *status, hipStream_t stream);
+
+/* Workspace bytes of q8_attention_decode (0 if the arguments are invalid). */
+size_t q8_attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len);
+
+/* Decode attention over the Q8 KV cache: one query row per sequence.  For
+ * query head h (kv head h / (n_heads / n_kv)) of sequence s, the keys and
+ * values of positions j < len[s] sit at slot base[s] + j:
+ *   s_j = scale * q . k_j,  out = sum_j e^(s_j - max) v_j / sum_j e^(s_j - max)
+ * with k, v dequantized (code * block scale).  Cached positions are taken in
+ * fixed chunks of 256, so a sequence's result depends only on its own data
+ * (bit-identical whatever the other sequences of the batch).
+ *  q          device fp32 [seqs][n_heads][head_dim] (q8_kv_write's q_out).
+ *  base, len  device int32 [seqs]: 1 <= len <= max_len, base >= 0,
+ *             base + len <= n_slots; a sequence violating this gets NaN
+ *             outputs and the status word set.
+ *  out        device fp32 [seqs][n_heads][head_dim].
+ *  workspace  device, >= q8_attention_workspace_bytes(...), 16-byte aligned;
+ *             its first int32 is the call's status (0, or Q8_ERR_ARG).
+ *  head_dim in {64, 128}; n_heads / n_kv in {1, 2, 4, 8}.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
+ *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,
+                        const float *k_scale, const int8_t *v_cache, const float *v_scale, int64_t n_slots,
+                        const int32_t *base, const int32_t *len, int64_t max_len, float scale, float *out,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

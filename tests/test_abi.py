@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -254,6 +254,63 @@ def test_combine_validation():
     assert _raw(f, A, 7168, B, 0, 8, 7168, C, 7168, None) == q8.Q8_OK
 
 
+def test_kv_write_validation():
+    f = "q8_kv_write"
+    E, F = 0x7F0000400000, 0x7F0000500000
+    ok = [A, 16, 32, 8, 64, B, 4096, C, D, None, None, 1e-5, E, 8192, F, A + 0x10000000, B + 0x10000000,
+          C + 0x10000000, D + 0x10000000, None, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["qkv", "tokens", "H", "Hk", "hd", "pos", "max_pos", "cos", "sin", "qg", "kg", "eps", "slots",
+                 "n_slots", "q_out", "kc", "ks", "vc", "vs", "status", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return _raw(f, *args)
+
+    assert call(qkv=None) == q8.Q8_ERR_ARG
+    assert call(pos=None) == q8.Q8_ERR_ARG
+    assert call(tokens=-1) == q8.Q8_ERR_ARG
+    assert call(max_pos=0) == q8.Q8_ERR_ARG
+    assert call(n_slots=0) == q8.Q8_ERR_ARG
+    assert call(qg=A + 0x20000000, eps=-1.0) == q8.Q8_ERR_ARG
+    assert call(H=30) == q8.Q8_ERR_SHAPE                     # n_heads % n_kv
+    assert call(hd=96) == q8.Q8_ERR_SHAPE
+    assert call(qkv=A + 4) == q8.Q8_ERR_ALIGN
+    assert call(ks=B + 0x10000002) == q8.Q8_ERR_ALIGN
+    assert call(q_out=A + 1024) == q8.Q8_ERR_ARG             # q_out over qkv
+    assert call(tokens=0) == q8.Q8_OK
+
+
+def test_attention_validation():
+    f = "q8_attention_decode"
+    assert q8.q8_attention_workspace_bytes(16, 32, 8, 64, 4096) == 256 + 16 * 8 * 16 * 4 * 66 * 4
+    assert q8.q8_attention_workspace_bytes(16, 32, 8, 96, 4096) == 0
+    assert q8.q8_attention_workspace_bytes(16, 48, 8, 64, 4096) == 0   # group of 6
+    need = q8.q8_attention_workspace_bytes(4, 8, 2, 64, 512)
+    E, F, G_, H_ = 0x7F0000400000, 0x7F0000500000, 0x7F0000600000, 0x7F0000700000
+    ok = [A, 4, 8, 2, 64, B, C, D, E, 1024, F, F + 64, 512, 0.125, G_, H_, need, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["q", "seqs", "H", "Hk", "hd", "kc", "ks", "vc", "vs", "n_slots", "base", "len", "max_len", "scale",
+                 "out", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return _raw(f, *args)
+
+    assert call(q=None) == q8.Q8_ERR_ARG
+    assert call(max_len=0) == q8.Q8_ERR_ARG
+    assert call(scale=float("nan")) == q8.Q8_ERR_ARG
+    assert call(hd=256) == q8.Q8_ERR_SHAPE
+    assert call(H=6) == q8.Q8_ERR_SHAPE                      # group of 3
+    assert call(q=A + 8) == q8.Q8_ERR_ALIGN
+    assert call(ws=None) == q8.Q8_ERR_WORKSPACE
+    assert call(wsb=need - 4) == q8.Q8_ERR_WORKSPACE
+    assert call(out=A + 64) == q8.Q8_ERR_ARG                 # out over q
+    assert call(seqs=0) == q8.Q8_OK
+
+
 def _no_gpu():
     import torch
     return torch.cuda.device_count() == 0
@@ -269,3 +326,9 @@ def test_valid_request_without_device_reports_device_error():
     assert _raw("q8_moe_route", A, 16, 256, 8, 1, B, C, None) == q8.Q8_ERR_DEVICE
     assert _raw("q8_swiglu_quantize", A, 4096, A + 8192, 4096, 128, 2048, C, None) == q8.Q8_ERR_DEVICE
     assert _raw("q8_moe_combine", A, 7168, B, 16, 8, 7168, 0x7F0000400000, 7168, None) == q8.Q8_ERR_DEVICE
+    assert _raw("q8_kv_write", A, 16, 32, 8, 64, B, 4096, C, D, None, None, 1e-5, 0x7F0000400000, 8192,
+                0x7F0000500000, A + 0x10000000, B + 0x10000000, C + 0x10000000, D + 0x10000000, None,
+                None) == q8.Q8_ERR_DEVICE
+    need = q8.q8_attention_workspace_bytes(4, 8, 2, 64, 512)
+    assert _raw("q8_attention_decode", A, 4, 8, 2, 64, B, C, D, 0x7F0000400000, 1024, 0x7F0000500000,
+                0x7F0000500040, 512, 0.125, 0x7F0000600000, 0x7F0000700000, need, None) == q8.Q8_ERR_DEVICE
