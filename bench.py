@@ -20,8 +20,10 @@ int8-MFMA GEMM at M in {188, 752, 2048} x (N, K) in {(2048, 2048),
 (8192, 2048), (2048, 8192)}), ``moe`` (a mixture-of-experts layer on the
 device: router over 256 experts, top-8 of 16 tokens, fused gate||up and down
 routed GEMVs, SwiGLU, weighted combine), ``norm`` (the fused residual + RMSNorm +
-Q8_0 quantize producer at the prefill row counts, hidden 2048), ``copy`` (a
-device copy of 1 GiB, used to calibrate rocprofv3's byte counters).
+Q8_0 quantize producer at the prefill row counts, hidden 2048), ``kv`` (a
+decode step's attention over a Q8 KV cache: 16 layers, 16 sequences x 4096
+positions), ``copy`` (a device copy of 1 GiB, used to calibrate rocprofv3's
+byte counters).
 
 The JSON line carries the metric, the roofline of the dominant kernel (its
 average launch duration measured with HIP events on the stream it runs on)
@@ -51,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "single", "batched", "prefill", "moe", "norm", "copy"])
+                    choices=["decode", "single", "batched", "prefill", "moe", "norm", "kv", "copy"])
     ap.add_argument("--m", type=int, default=1, help="rows per GEMV for --workload batched")
     ap.add_argument("--unfused", action="store_true", help="decode: separate quantize and GEMV launches")
     ap.add_argument("--per-matrix", action="store_true",
@@ -709,6 +711,122 @@ def bench_norm(args):
 
 
 # --------------------------------------------------------------------------
+# Q8 KV cache: cache write + decode attention
+# --------------------------------------------------------------------------
+
+def attention_bytes(S: int, Hk: int, hd: int, L: int, H: int) -> int:
+    """Algorithmic HBM bytes of one q8_attention_decode call: the K and V codes
+    and fp32 block scales of every cached position once, the queries and the
+    outputs."""
+    return S * Hk * L * (2 * hd + 2 * (hd // 32) * 4) + 2 * S * H * hd * 4
+
+
+def bench_kv(args):
+    """One decode step's attention for Llama-3.2-1B: per layer (16, each with
+    its own cache of 16 sequences x 4096 positions) the new token's fused
+    norm + rope + cache write, then decode attention over the cache."""
+    import torch
+
+    import oracle
+    import workloads as wl
+    from decode_q8_amd import q8
+    dev = torch.device("cuda", 0)
+    S, H, Hk, hd, L = wl.KV_SEQS, wl.LLAMA_HEADS, wl.LLAMA_KV_HEADS, wl.LLAMA_HEAD_DIM, wl.KV_CONTEXT
+    layers = wl.LLAMA_LAYERS
+    n_slots = S * L
+    cos_t, sin_t = wl.rope_tables(L, hd)
+    cos_d, sin_d = torch.from_numpy(cos_t).to(dev), torch.from_numpy(sin_t).to(dev)
+    # the step's new token of each sequence sits at position L - 1 (its slot
+    # was filled with the rest of the cache; the write refreshes it)
+    pos = torch.full((S,), L - 1, dtype=torch.int32, device=dev)
+    slots = torch.arange(S, dtype=torch.int32, device=dev) * L + (L - 1)
+    base = torch.arange(S, dtype=torch.int32, device=dev) * L
+    lens = torch.full((S,), L, dtype=torch.int32, device=dev)
+    need = q8.q8_attention_workspace_bytes(S, H, Hk, hd, L)
+    per_layer, host0 = [], None
+    caches = []
+    for l0 in range(0, layers, 8):
+        caches += wl.many(lambda layer: wl.kv_cache(wl.KV, layer, Hk, n_slots, hd),
+                          [(layer,) for layer in range(l0, min(layers, l0 + 8))], args.threads)
+    for layer in range(layers):
+        kc, ks, vc, vs = caches[layer]
+        caches[layer] = None
+        qkv, qg, kg = wl.kv_inputs(wl.KV, 3000 + layer, S, H, Hk, hd)
+        c = dict(kc=torch.from_numpy(kc).to(dev), ks=torch.from_numpy(ks).to(dev), vc=torch.from_numpy(vc).to(dev),
+                 vs=torch.from_numpy(vs).to(dev), qkv=torch.from_numpy(qkv).to(dev), qg=torch.from_numpy(qg).to(dev),
+                 kg=torch.from_numpy(kg).to(dev), q=torch.empty((S, H, hd), dtype=torch.float32, device=dev),
+                 out=torch.empty((S, H, hd), dtype=torch.float32, device=dev),
+                 ws=torch.zeros(need, dtype=torch.uint8, device=dev))
+        if layer == 0:
+            host0 = (kc, ks, vc, vs, qkv, qg, kg)
+        per_layer.append(c)
+        del kc, ks, vc, vs
+    torch.cuda.synchronize()
+    scale = 1.0 / np.sqrt(hd)
+
+    def write(c, st):
+        q8.q8_kv_write(c["qkv"], S, H, Hk, hd, pos, L, cos_d, sin_d, c["qg"], c["kg"], 1e-5, slots, n_slots, c["q"],
+                       c["kc"], c["ks"], c["vc"], c["vs"], None, st)
+
+    def attend(c, st):
+        q8.q8_attention_decode(c["q"], S, H, Hk, hd, c["kc"], c["ks"], c["vc"], c["vs"], n_slots, base, lens, L,
+                               scale, c["out"], c["ws"], need, st)
+
+    def run(s, timers=None):
+        for i, c in enumerate(per_layer):
+            write(c, s.cuda_stream)
+            if timers is not None:
+                timers[i].start()
+            attend(c, s.cuda_stream)
+            if timers is not None:
+                timers[i].stop()
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run(stream)
+    torch.cuda.synchronize()
+    # check layer 0 against the oracle chain on two sequences before timing
+    kc, ks, vc, vs, qkv, qg, kg = host0
+    sl = np.arange(S, dtype=np.int32) * L + (L - 1)
+    q_ref, kc1, ks1, vc1, vs1 = oracle.kv_write(qkv, H, Hk, hd, np.full(S, L - 1, np.int32), cos_t, sin_t, qg, kg,
+                                                1e-5, np.arange(S, dtype=np.int32), S)
+    assert np.array_equal(per_layer[0]["q"].cpu().numpy().view(np.uint32), q_ref.view(np.uint32)), "rotated queries"
+    kc[:, sl], ks[:, sl], vc[:, sl], vs[:, sl] = kc1, ks1, vc1, vs1
+    two = np.array([0, S - 1])
+    out_ref, bound = oracle.attention_decode(q_ref[two], kc, ks, vc, vs, (two * L).astype(np.int32),
+                                             np.full(2, L, np.int32), scale)
+    out0 = per_layer[0]["out"].cpu().numpy()[two]
+    assert np.all(np.abs(out0.astype(np.float64) - out_ref) <= bound), "attention outside the oracle's budget"
+    assert int(per_layer[0]["ws"][:4].view(torch.int32).cpu()[0]) == 0
+    ms_per_step, graph = graph_time(run, stream, args.steps, args.warmup)
+    ms = per_launch_ms(run, layers, stream, graph, reps=max(1, min(args.steps, 10)))
+    abytes = attention_bytes(S, Hk, hd, L, H)
+    kv_bytes = S * Hk * L * (2 * hd + 2 * (hd // 32) * 4) * layers
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        q1 = q_ref[:1]
+        sec, reps = timed_repeat(lambda: oracle.attention_decode(q1, kc, ks, vc, vs, np.zeros(1, np.int32),
+                                                                 np.full(1, L, np.int32), scale), min_seconds=3.0)
+        cpu = {"value": round(abytes / S / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"attention of one sequence (32 heads x 4096 positions) of one layer, {reps} repetitions"}
+    config = {
+        "workload": "Llama-3.2-1B decode-step attention over a Q8 KV cache: 16 layers, 16 sequences x 4096 cached "
+                    "positions, 32 query / 8 KV heads of 64; per layer the new tokens' fused norm + rope + cache "
+                    "write, then decode attention",
+        "kv_bytes_per_step": int(kv_bytes),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "attention_call_us": round(float(ms.mean()) * 1e3, 2),
+        "hip_graph": True,
+    }
+    roof = hbm_roofline("q8k::attn_partial_kernel + attn_combine_kernel", float(abytes), float(ms.mean()))
+    roof["traffic"] = profiled_traffic("attention_decode_kv.txt", "decode_q8_amd/csrc/kv.hip")
+    roof["note"] = "one attention call (the partial kernel and its small combine kernel), averaged over the 16 layers"
+    return base_record(args, "Q8 KV-cache decode attention HBM GB/s (%HBM peak)", value, "GB/s", ms_per_step,
+                       "int8 KV, fp32 softmax/accumulation", config, roof, cpu)
+
+
+# --------------------------------------------------------------------------
 
 def bench_copy(args):
     """1 GiB device-to-device copy: known bytes for calibrating byte counters."""
@@ -735,7 +853,7 @@ def main():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
     fn = {"decode": bench_decode, "batched": bench_decode, "single": bench_single, "prefill": bench_prefill,
-          "moe": bench_moe, "norm": bench_norm, "copy": bench_copy}[args.workload]
+          "moe": bench_moe, "norm": bench_norm, "kv": bench_kv, "copy": bench_copy}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
 

@@ -16,6 +16,7 @@
 static_assert(Q8_SEQUENCE_MAX_STEPS == q8k::SEQ_MAX_STEPS, "sequence length limit");
 static_assert(Q8_ROUTE_MAX_EXPERTS == q8k::ROUTE_MAX_EXPERTS && Q8_ROUTE_MAX_TOPK == q8k::ROUTE_MAX_TOPK,
               "router limits");
+static_assert(Q8_ATTENTION_MAX_LEN == q8k::ATT_MAX_LEN, "attention context limit");
 
 namespace {
 
@@ -271,7 +272,7 @@ int q8_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int hea
 static bool attention_shape_ok(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len) {
     if (seqs < 0 || n_heads <= 0 || n_kv <= 0 || max_len <= 0 || n_heads % n_kv) return false;
     const int G = n_heads / n_kv;
-    return (head_dim == 64 || head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8) && max_len <= INT32_MAX &&
+    return (head_dim == 64 || head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8) && max_len <= Q8_ATTENTION_MAX_LEN &&
            seqs <= 65535 && n_kv <= 65535;
 }
 

@@ -15,10 +15,12 @@
 // a sequence depends only on its own length.  A workgroup takes one chunk of
 // one (sequence, kv head) for the G query heads sharing that kv head: each of
 // its 4 waves scores 64 keys (lane = key: the key row is dequantized once and
-// dotted with the G queries), the chunk's softmax runs in the exp2 domain,
-// then the lanes turn to dimensions and accumulate p * v over the wave's keys
-// from LDS; the 4 waves' sums are added in order.  The combine kernel rescales
-// the chunks' (max, sum, weighted sum) and divides, chunks in order.
+// dotted with the G queries read as scalars), takes its own softmax in the
+// exp2 domain, then turns its lanes to dimensions and accumulates p * v over
+// its keys from a wave-local LDS tile; only then do the 4 waves meet, and
+// their sums are rescaled to the chunk maximum and added in order.  The
+// combine kernel rescales the chunks' (max, sum, weighted sum) and divides,
+// chunks in order.
 #include <math.h>
 
 #include "device.hpp"
@@ -143,18 +145,30 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const float *__restrict__
 
 constexpr int ATT_CHUNK = 256;  // cached positions per workgroup (4 waves x 64)
 
-__device__ __forceinline__ float wave_max_f32(float x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
-    return x;
+// Wave-wide max / sum through DPP lane moves (quad swaps, half-row and row
+// mirrors, row broadcasts 15 and 31; lane 63 ends with the result, read back
+// as a scalar): a fixed order of operations, and no LDS round trips.
+template <bool SUM>
+__device__ __forceinline__ float wave_reduce_f32(float x) {
+#define Q8_DPPF(ctrl, rows)                                                                                        \
+    {                                                                                                              \
+        const float y = __builtin_bit_cast(                                                                        \
+            float, __builtin_amdgcn_update_dpp(SUM ? 0 : __builtin_bit_cast(int, -INFINITY),                        \
+                                               __builtin_bit_cast(int, x), ctrl, rows, 0xf, false));               \
+        x = SUM ? x + y : fmaxf(x, y);                                                                             \
+    }
+    Q8_DPPF(0xb1, 0xf);   // quad_perm [1, 0, 3, 2]
+    Q8_DPPF(0x4e, 0xf);   // quad_perm [2, 3, 0, 1]
+    Q8_DPPF(0x141, 0xf);  // row_half_mirror
+    Q8_DPPF(0x140, 0xf);  // row_mirror
+    Q8_DPPF(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    Q8_DPPF(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef Q8_DPPF
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-__device__ __forceinline__ float wave_sum_f32(float x) {
-    // butterfly: every lane ends with the same sum, in one fixed order
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) x += __shfl_xor(x, s);
-    return x;
-}
+__device__ __forceinline__ float wave_max_f32(float x) { return wave_reduce_f32<false>(x); }
+__device__ __forceinline__ float wave_sum_f32(float x) { return wave_reduce_f32<true>(x); }
 
 __device__ __forceinline__ float byte_f32(uint32_t w, int i) {
     return (float)((int32_t)(w << (24 - 8 * i)) >> 24);  // sign-extended int8 -> exact fp32
@@ -180,10 +194,12 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     constexpr int NB = HD / 32;
     constexpr int W16 = HD / 16;  // 16-byte words per cached row
     constexpr int DPL = HD / 64;  // dimensions per lane in the weighted sum
+    // per wave: its 64 keys' V rows (later its G x HD weighted sums, G <= 16),
+    // their V block scales and softmax weights
     __shared__ __align__(16) int8_t vt[4][64][HD];
+    static_assert(G * HD * 4 <= 64 * HD, "the weighted sums fit in the wave's V tile");
     __shared__ float vsc[4][64][NB];
     __shared__ __align__(16) float pl[4][64][G];
-    __shared__ float accw[4][G][HD];
     __shared__ float redm[4][G], reds[4][G];
     const int sp = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int splits = gridDim.x;
@@ -214,7 +230,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
         ks[b] = valid ? k_scale[row * NB + b] : 0.0f;
         vsc[w][lane][b] = valid ? v_scale[row * NB + b] : 0.0f;
     }
-    __syncthreads();
 
     // scores of this lane's key for the G heads, per 32-value block then scaled
     float sc[G];
@@ -235,34 +250,30 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
 #pragma unroll
             for (int i = 0; i < 32; i += 4) {
                 const float4 qv = *reinterpret_cast<const float4 *>(qg + g * HD + 32 * b + i);
-                a = a + qv.x * kf[i];
-                a = a + qv.y * kf[i + 1];
-                a = a + qv.z * kf[i + 2];
-                a = a + qv.w * kf[i + 3];
+                a = __builtin_fmaf(qv.x, kf[i], a);
+                a = __builtin_fmaf(qv.y, kf[i + 1], a);
+                a = __builtin_fmaf(qv.z, kf[i + 2], a);
+                a = __builtin_fmaf(qv.w, kf[i + 3], a);
             }
-            sc[g] = sc[g] + a * ks[b];
+            sc[g] = __builtin_fmaf(a, ks[b], sc[g]);
         }
     }
 #pragma unroll
     for (int g = 0; g < G; g++) sc[g] = valid ? sc[g] * scale_log2 : -INFINITY;
 
-    // chunk softmax (exp2 domain): maximum over the 4 waves, then p and its sum
+    // this wave's softmax over its 64 keys (exp2 domain); waves run on
+    // independently until the one barrier that combines them
+    float mw[G], lw[G], p[G];
 #pragma unroll
     for (int g = 0; g < G; g++) {
-        const float m = wave_max_f32(sc[g]);
-        if (lane == 0) redm[w][g] = m;
-    }
-    __syncthreads();
-    float p[G];
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-        const float m = fmaxf(fmaxf(redm[0][g], redm[1][g]), fmaxf(redm[2][g], redm[3][g]));
-        p[g] = valid ? __builtin_amdgcn_exp2f(sc[g] - m) : 0.0f;
+        mw[g] = wave_max_f32(sc[g]);
+        p[g] = valid ? __builtin_amdgcn_exp2f(sc[g] - mw[g]) : 0.0f;
         pl[w][lane][g] = p[g];
-        const float ls = wave_sum_f32(p[g]);
-        if (lane == 0) reds[w][g] = ls;
+        lw[g] = wave_sum_f32(p[g]);
     }
-    __syncthreads();
+    // the wave reads back its own V rows from LDS: keep the writes above the reads
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
 
     // weighted sum of V over this wave's 64 keys: lanes are dimensions now
     float acc[DPL][G];
@@ -280,26 +291,61 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
             const int d = lane + 64 * e;
             const float vv = (float)vt[w][jj][d] * vsc[w][jj][d >> 5];
 #pragma unroll
-            for (int g = 0; g < G; g++) acc[e][g] = acc[e][g] + pj[g] * vv;
+            for (int g = 0; g < G; g++) acc[e][g] = __builtin_fmaf(pj[g], vv, acc[e][g]);
         }
     }
+    // the wave's sums go where its V tile was (read by no one else, and its
+    // own reads of it are done: LDS operations of a wave complete in order)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    float(*accw_w)[HD] = reinterpret_cast<float(*)[HD]>(&vt[w][0][0]);
 #pragma unroll
     for (int e = 0; e < DPL; e++)
 #pragma unroll
-        for (int g = 0; g < G; g++) accw[w][g][lane + 64 * e] = acc[e][g];
+        for (int g = 0; g < G; g++) accw_w[g][lane + 64 * e] = acc[e][g];
+    if (lane < G) {
+        // lane g publishes head g's (max, sum); the values are wave-uniform
+        float m = mw[0], l = lw[0];
+#pragma unroll
+        for (int g = 1; g < G; g++)
+            if (lane == g) {
+                m = mw[g];
+                l = lw[g];
+            }
+        redm[w][lane] = m;
+        reds[w][lane] = l;
+    }
     __syncthreads();
 
+    // the workgroup's chunk: rescale the 4 waves to the chunk maximum, in order
     float *o = part + (((int64_t)s * n_kv + kvh) * splits + sp) * (G * (HD + 2));
     for (int i = tid; i < G * HD; i += 256) {
         const int g = i / HD, d = i % HD;
-        o[g * (HD + 2) + 2 + d] = ((accw[0][g][d] + accw[1][g][d]) + accw[2][g][d]) + accw[3][g][d];
+        const float m = fmaxf(fmaxf(redm[0][g], redm[1][g]), fmaxf(redm[2][g], redm[3][g]));
+        float a = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) {
+            const float f = redm[ww][g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(redm[ww][g] - m);
+            a = __builtin_fmaf(f, reinterpret_cast<const float(*)[HD]>(&vt[ww][0][0])[g][d], a);
+        }
+        o[g * (HD + 2) + 2 + d] = a;
     }
     if (tid < G) {
         const int g = tid;
-        o[g * (HD + 2)] = fmaxf(fmaxf(redm[0][g], redm[1][g]), fmaxf(redm[2][g], redm[3][g]));
-        o[g * (HD + 2) + 1] = ((reds[0][g] + reds[1][g]) + reds[2][g]) + reds[3][g];
+        const float m = fmaxf(fmaxf(redm[0][g], redm[1][g]), fmaxf(redm[2][g], redm[3][g]));
+        float l = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ww++) {
+            const float f = redm[ww][g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(redm[ww][g] - m);
+            l = __builtin_fmaf(f, reds[ww][g], l);
+        }
+        o[g * (HD + 2)] = m;
+        o[g * (HD + 2) + 1] = l;
     }
 }
+
+constexpr int ATT_MAX_SPLITS = 256;
+static_assert(ATT_MAX_SPLITS * ATT_CHUNK == ATT_MAX_LEN, "the combine kernel holds every chunk of a sequence");
 
 template <int HD, int G>
 __global__ __launch_bounds__(64) void attn_combine_kernel(int32_t n_heads, int32_t n_kv, int64_t n_slots,
@@ -308,6 +354,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(int32_t n_heads, int32
                                                           int32_t splits, const float *__restrict__ part,
                                                           float *__restrict__ out, int32_t *__restrict__ status) {
     constexpr int DPL = HD / 64;
+    __shared__ float ml[ATT_MAX_SPLITS][2];  // each chunk's (max, sum)
     const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
     const int kvh = h / G, g = h % G;
     const int32_t L = len[s];
@@ -320,17 +367,34 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(int32_t n_heads, int32
     }
     const int nsp = (L + ATT_CHUNK - 1) / ATT_CHUNK;
     const float *pb = part + ((int64_t)s * n_kv + kvh) * splits * (G * (HD + 2)) + g * (HD + 2);
+    // every chunk's (max, sum) at once, one chunk per lane
+    for (int c = lane; c < nsp; c += 64) {
+        ml[c][0] = pb[(int64_t)c * G * (HD + 2)];
+        ml[c][1] = pb[(int64_t)c * G * (HD + 2) + 1];
+    }
+    __syncthreads();
     float M = -INFINITY;
-    for (int c = 0; c < nsp; c++) M = fmaxf(M, pb[(int64_t)c * G * (HD + 2)]);
+    for (int c = 0; c < nsp; c++) M = fmaxf(M, ml[c][0]);
     float den = 0.0f, num[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; e++) num[e] = 0.0f;
-    for (int c = 0; c < nsp; c++) {
-        const float *pc = pb + (int64_t)c * G * (HD + 2);
-        const float f = __builtin_amdgcn_exp2f(pc[0] - M);
-        den = den + f * pc[1];
+    // chunks in order; the weighted-sum loads of 8 chunks are issued together
+    for (int c0 = 0; c0 < nsp; c0 += 8) {
+        float v[8][DPL];
 #pragma unroll
-        for (int e = 0; e < DPL; e++) num[e] = num[e] + f * pc[2 + lane + 64 * e];
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int e = 0; e < DPL; e++)
+                v[i][e] = c0 + i < nsp ? pb[(int64_t)(c0 + i) * G * (HD + 2) + 2 + lane + 64 * e] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if (c0 + i < nsp) {
+                const float f = __builtin_amdgcn_exp2f(ml[c0 + i][0] - M);
+                den = __builtin_fmaf(f, ml[c0 + i][1], den);
+#pragma unroll
+                for (int e = 0; e < DPL; e++) num[e] = __builtin_fmaf(f, v[i][e], num[e]);
+            }
+        }
     }
 #pragma unroll
     for (int e = 0; e < DPL; e++) o[lane + 64 * e] = num[e] / den;

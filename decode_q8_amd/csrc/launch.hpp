@@ -67,6 +67,7 @@ hipError_t launch_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_
                            const float *q_gain, const float *k_gain, float eps, const int32_t *slots, int64_t n_slots,
                            float *q_out, int8_t *k_cache, float *k_scale, int8_t *v_cache, float *v_scale,
                            int32_t *status, hipStream_t s);
+constexpr int64_t ATT_MAX_LEN = 65536;  // cached positions per sequence
 size_t attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len);
 hipError_t launch_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim,
                                    const int8_t *k_cache, const float *k_scale, const int8_t *v_cache,

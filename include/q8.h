@@ -360,6 +360,8 @@ int q8_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int hea
                 float eps, const int32_t *slots, int64_t n_slots, float *q_out, int8_t *k_cache, float *k_scale,
                 int8_t *v_cache, float *v_scale, int32_t *status, hipStream_t stream);
 
+#define Q8_ATTENTION_MAX_LEN 65536  /* cached positions per sequence */
+
 /* Workspace bytes of q8_attention_decode (0 if the arguments are invalid). */
 size_t q8_attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len);
 
@@ -377,7 +379,8 @@ size_t q8_attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int hea
  *  out        device fp32 [seqs][n_heads][head_dim].
  *  workspace  device, >= q8_attention_workspace_bytes(...), 16-byte aligned;
  *             its first int32 is the call's status (0, or Q8_ERR_ARG).
- *  head_dim in {64, 128}; n_heads / n_kv in {1, 2, 4, 8}.
+ *  head_dim in {64, 128}; n_heads / n_kv in {1, 2, 4, 8};
+ *  max_len <= Q8_ATTENTION_MAX_LEN; seqs and n_kv <= 65535.
  *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
  *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,

@@ -287,6 +287,8 @@ def test_attention_validation():
     assert q8.q8_attention_workspace_bytes(16, 32, 8, 64, 4096) == 256 + 16 * 8 * 16 * 4 * 66 * 4
     assert q8.q8_attention_workspace_bytes(16, 32, 8, 96, 4096) == 0
     assert q8.q8_attention_workspace_bytes(16, 48, 8, 64, 4096) == 0   # group of 6
+    assert q8.q8_attention_workspace_bytes(1, 8, 8, 64, 65536) > 0
+    assert q8.q8_attention_workspace_bytes(1, 8, 8, 64, 65537) == 0     # beyond Q8_ATTENTION_MAX_LEN
     need = q8.q8_attention_workspace_bytes(4, 8, 2, 64, 512)
     E, F, G_, H_ = 0x7F0000400000, 0x7F0000500000, 0x7F0000600000, 0x7F0000700000
     ok = [A, 4, 8, 2, 64, B, C, D, E, 1024, F, F + 64, 512, 0.125, G_, H_, need, None]

@@ -169,6 +169,17 @@ def kv_inputs(workload: int, index: int, tokens: int, n_heads: int, n_kv: int, h
     return qkv, qg.astype(np.float32), kg.astype(np.float32)
 
 
+def kv_cache(workload: int, layer: int, n_kv: int, n_slots: int, head_dim: int):
+    """A filled Q8 KV cache for one layer (head-major): int8 codes uniform in
+    [-127, 127] and fp32 block scales |N(0, 1)| * 0.02 / 127, for K and V."""
+    g = generator(workload, (TAG_WEIGHT, 60 + layer, 0))
+    kc = g.integers(-127, 128, (n_kv, n_slots, head_dim), dtype=np.int8)
+    vc = g.integers(-127, 128, (n_kv, n_slots, head_dim), dtype=np.int8)
+    ks = (np.abs(g.standard_normal((n_kv, n_slots, head_dim // 32), dtype=np.float32)) * np.float32(0.02 / 127))
+    vs = (np.abs(g.standard_normal((n_kv, n_slots, head_dim // 32), dtype=np.float32)) * np.float32(0.02 / 127))
+    return kc, ks.astype(np.float32), vc, vs.astype(np.float32)
+
+
 def routing(workload: int, tokens: int, n_experts: int, topk: int, group: int = 0) -> np.ndarray:
     """int32 [tokens][topk] expert ids: top-k of uniform logits per token
     (input generation for the routed-expert GEMV alone; the library's router
