@@ -28,6 +28,8 @@
 
 namespace q8k {
 
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
 // ---------------------------------------------------------------------------
 // Fused norm + rope + cache write
 // ---------------------------------------------------------------------------
@@ -194,13 +196,15 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     constexpr int NB = HD / 32;
     constexpr int W16 = HD / 16;  // 16-byte words per cached row
     constexpr int DPL = HD / 64;  // dimensions per lane in the weighted sum
-    // per wave: its 64 keys' V rows (later its G x HD weighted sums, G <= 16),
-    // their V block scales and softmax weights
+    // per wave: its 64 keys' K rows (XOR-swizzled 16-byte chunks) and V rows
+    // (later its G x HD weighted sums, G <= 16), their block scales ([block]
+    // [key]) and the softmax weights
+    __shared__ __align__(16) int8_t kt[4][64 * HD];
     __shared__ __align__(16) int8_t vt[4][64][HD];
     static_assert(G * HD * 4 <= 64 * HD, "the weighted sums fit in the wave's V tile");
-    __shared__ float vsc[4][64][NB];
-    __shared__ __align__(16) float pl[4][64][G];
+    __shared__ float kss[4][NB][64], vss[4][NB][64];
     __shared__ float redm[4][G], reds[4][G];
+    static_assert(64 * G * 4 <= 64 * HD, "the softmax weights fit in the wave's K tile");
     const int sp = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int splits = gridDim.x;
     if ((sp | kvh | s) == 0 && threadIdx.x == 0)  // the status word of this call starts clear
@@ -214,22 +218,42 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     // the G query rows: the same for every lane, read with scalar loads
     const float *qg = q + ((int64_t)s * n_heads + (int64_t)kvh * G) * HD;
 
-    const int j = c0 + 64 * w + lane;
-    const bool valid = j < L;
-    const int64_t row = (int64_t)kvh * n_slots + b0 + (valid ? j : 0);
-    uint4 kr[W16];
-    float ks[NB];
+    // this wave's keys: rows r0 .. r0 + nv - 1 of the head's cache (nv >= 1 for
+    // wave 0; a wave past the end loads row r0 - 1 .. and masks everything)
+    const int kw = c0 + 64 * w;                        // first key of the wave
+    const int nv = min(max(L - kw, 0), 64);            // valid keys
+    const int64_t r0 = (int64_t)kvh * n_slots + b0 + (nv > 0 ? kw : L - 1);
+    const int last = nv > 0 ? nv - 1 : 0;
+    const bool valid = lane < nv;
+    // coalesced direct-to-LDS loads: each instruction moves 1 KB of whole rows
+    // (rows past the valid ones repeat the last valid row: in bounds, masked)
 #pragma unroll
-    for (int i = 0; i < W16; i++) {
-        kr[i] = valid ? reinterpret_cast<const uint4 *>(k_cache + row * HD)[i] : make_uint4(0, 0, 0, 0);
-        const uint4 vv = valid ? reinterpret_cast<const uint4 *>(v_cache + row * HD)[i] : make_uint4(0, 0, 0, 0);
-        reinterpret_cast<uint4 *>(&vt[w][lane][0])[i] = vv;
+    for (int t = 0; t < W16; t++) {
+        const int p16 = 64 * t + lane;                 // 16-byte position in the tile
+        const int r = p16 / W16, slot = p16 % W16;
+        const int rc = min(r, last);
+        const int chunk = slot ^ (r & (W16 - 1));      // the K row chunk stored at this slot
+        __builtin_amdgcn_global_load_lds(k_cache + (r0 + rc) * HD + chunk * 16, (lds_ptr)(&kt[w][0] + 1024 * t), 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds(v_cache + (r0 + rc) * HD + slot * 16, (lds_ptr)(&vt[w][0][0] + 1024 * t),
+                                         16, 0, 0);
     }
 #pragma unroll
     for (int b = 0; b < NB; b++) {
-        ks[b] = valid ? k_scale[row * NB + b] : 0.0f;
-        vsc[w][lane][b] = valid ? v_scale[row * NB + b] : 0.0f;
+        const int rc = min(lane, last);
+        __builtin_amdgcn_global_load_lds(k_scale + (r0 + rc) * NB + b, (lds_ptr)(&kss[w][b][0]), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(v_scale + (r0 + rc) * NB + b, (lds_ptr)(&vss[w][b][0]), 4, 0, 0);
     }
+    // the wave's own loads have landed in LDS (nothing else touches its tiles)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    uint4 kr[W16];
+    float ks[NB];
+#pragma unroll
+    for (int i = 0; i < W16; i++)
+        kr[i] = *reinterpret_cast<const uint4 *>(&kt[w][0] + lane * HD + 16 * (i ^ (lane & (W16 - 1))));
+#pragma unroll
+    for (int b = 0; b < NB; b++) ks[b] = kss[w][b][lane];
 
     // scores of this lane's key for the G heads, per 32-value block then scaled
     float sc[G];
@@ -263,12 +287,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
 
     // this wave's softmax over its 64 keys (exp2 domain); waves run on
     // independently until the one barrier that combines them
+    // the softmax weights [key][G] go where the wave's K rows were: every
+    // lane has read its row (LDS operations of a wave complete in order)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    float(*pl_w)[G] = reinterpret_cast<float(*)[G]>(&kt[w][0]);
     float mw[G], lw[G], p[G];
 #pragma unroll
     for (int g = 0; g < G; g++) {
         mw[g] = wave_max_f32(sc[g]);
         p[g] = valid ? __builtin_amdgcn_exp2f(sc[g] - mw[g]) : 0.0f;
-        pl[w][lane][g] = p[g];
+        pl_w[lane][g] = p[g];
         lw[g] = wave_sum_f32(p[g]);
     }
     // the wave reads back its own V rows from LDS: keep the writes above the reads
@@ -285,11 +314,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     for (int jj = 0; jj < 64; jj++) {
         float pj[G];
 #pragma unroll
-        for (int g = 0; g < G; g++) pj[g] = pl[w][jj][g];
+        for (int g = 0; g < G; g++) pj[g] = pl_w[jj][g];
 #pragma unroll
         for (int e = 0; e < DPL; e++) {
             const int d = lane + 64 * e;
-            const float vv = (float)vt[w][jj][d] * vsc[w][jj][d >> 5];
+            const float vv = (float)vt[w][jj][d] * vss[w][d >> 5][jj];
 #pragma unroll
             for (int g = 0; g < G; g++) acc[e][g] = __builtin_fmaf(pj[g], vv, acc[e][g]);
         }
