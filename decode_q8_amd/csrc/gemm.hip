@@ -12,13 +12,14 @@
 //                          256-value group (the first block multiplies),
 //   output             y = ((a_0 + a_1) + a_2) + ...   over the groups.
 // The order depends on k only, so each row is bit-identical for any m and
-// any row order.  Two VALU operations per output and block remain; with
-// packed fp32 unavailable they, not the MFMA, bound this kernel.
+// any row order.  Two VALU operations per output and block remain, on top of
+// the staging of the operands through LDS.
 //
 // Tiling: each wave owns a 32 x 64 output strip (1 x 2 MFMA tiles); a
-// workgroup of WM x WN waves owns a (32 WM) x (64 WN) tile: 128 x 128 (8
-// waves) for large problems, 64 x 64 (2 waves) when 128 x 128 tiles would
-// leave CUs idle.  The k loop runs in stages of 4 blocks (128 values).  Stages move
+// workgroup of WM x WN = 4 x 2 waves owns a 128 x 128 tile when the problem
+// has at least 256 such tiles; smaller problems run gemm_strip_kernel below
+// (32 x 64 strips, k split across 8 waves).  The k loop runs in stages of 4
+// blocks (128 values).  Stages move
 // from HBM straight into LDS with global_load_lds_dwordx4 / _dword (no
 // register staging), NS = 4 stages deep, so three stages are in flight while
 // one is computed.  Every wave issues exactly LOADS_PER_STAGE such loads per
@@ -28,7 +29,7 @@
 // block), which is all an exact integer dot needs.
 //
 // LDS stage layout (128 x 128: 34 KB, NS = 4 stages = 136 KB of gfx950's
-// 160 KB; 64 x 64: 17 KB, 68 KB for four stages):
+// 160 KB):
 //   A   activation rows: row r's 16-byte chunk c at r*128 + (c ^ (r & 7))*16
 //       (the XOR swizzle keeps the MFMA operand reads bank-conflict free)
 //   B   the weight tiles' 4 block records, as packed (8 KB per tile)
@@ -393,19 +394,15 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(const int8_t *__restric
 // Kernel by problem size: 128 x 128 tiles while they give every CU a
 // workgroup, else 32 x 64 strips with k split across the waves.  Each
 // output's arithmetic is the same in both, so rows stay bit-identical across m.
-int gemm_variant(int64_t m, int64_t n) {
-    const int64_t big = ((m + 127) / 128) * ((n + 127) / 128);
-    return big >= 256 ? 0 : 2;
-}
+// 128 x 128 tiles when there are at least 256 of them (one per CU), else strips.
+static bool gemm_tiled(int64_t m, int64_t n) { return ((m + 127) / 128) * ((n + 127) / 128) >= 256; }
 
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
                        hipStream_t s) {
     const int8_t *xq = (const int8_t *)x_q;
     const uint16_t *xs = (const uint16_t *)((const uint8_t *)x_q + m * k);
     const uint8_t *wb = (const uint8_t *)w;
-    const int v = gemm_variant(m, n);
-    if (v == 0) return launch_tiles<4, 2>(xq, xs, m, wb, n, k, y, ld_y, s);
-    if (v == 1) return launch_tiles<2, 1>(xq, xs, m, wb, n, k, y, ld_y, s);
+    if (gemm_tiled(m, n)) return launch_tiles<4, 2>(xq, xs, m, wb, n, k, y, ld_y, s);
     const dim3 grid((unsigned)(n / TILE_ROWS), (unsigned)((m + 31) / 32));
     hipLaunchKernelGGL(gemm_strip_kernel, grid, dim3(512), 0, s, xq, xs, m, wb, n, k, y, ld_y);
     return hipGetLastError();

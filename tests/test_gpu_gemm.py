@@ -47,8 +47,8 @@ def test_row_invariance_across_m_and_order():
 
 
 def test_row_invariance_across_tile_shapes():
-    """m = 1024 on n = 4096 runs 128 x 128 workgroups, m = 100 the 64 x 64
-    ones: the rows they share are still bit-identical."""
+    """m = 1024 on n = 4096 runs 128 x 128 workgroups, m = 100 the k-split
+    strip kernel: the rows they share are still bit-identical."""
     n, k = 4096, 512
     x = wl.activation(wl.PREFILL, 61, 1024, k, outliers=True)
     _, wp = weights_packed(wl.weight(wl.PREFILL, 61, n, k))
