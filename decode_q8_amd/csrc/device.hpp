@@ -37,6 +37,19 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int c) {
 // everything derived from it stays scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// Maximum over each aligned group of 8 lanes, left in all 8 (DPP lane moves:
+// swap neighbours, swap pairs, then mirror the two halves of the 8 lanes).
+// fmaxf is exact, so the order of the moves does not change the result.
+__device__ __forceinline__ float max_over_8_lanes(float x) {
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf,
+                                                                      false)));  // quad_perm [1, 0, 3, 2]
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf,
+                                                                      false)));  // quad_perm [2, 3, 0, 1]
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf,
+                                                                      false)));  // row_half_mirror
+    return x;
+}
+
 // Sum of the 8 block terms of one group, in the fixed tree order
 // ((t0+t1)+(t2+t3))+((t4+t5)+(t6+t7)).
 __device__ __forceinline__ float tree8(const float (&t)[8]) {

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, i
     extern __shared__ float lds_u[];  // [groups of this workgroup][M][64]
     __shared__ int last_wg;
     tile_unit<M, LAYOUT, ACT, ONE>(xq, ld_x, xs, w, n, k, y, ld_y, (int64_t)blockIdx.y, (int)blockIdx.x,
-                                   (int)gridDim.x, segs_per_wg, ctr, part, lds_u, &last_wg, NoWait());
+                                   (int)gridDim.x, segs_per_wg, ctr, part, lds_u, &last_wg, false, NoWait());
 }
 
 constexpr int GEMV_MAX_WAVES = 8;

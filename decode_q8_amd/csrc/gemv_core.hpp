@@ -108,10 +108,7 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 
 #pragma unroll
     for (int m = 0; m < M; m++) {
         const float4 v = xv[m];
-        float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         const float d = amax / 127.0f;
         int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
         if (d != 0.0f) {
@@ -147,13 +144,15 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 
 // the wave owns groups [0, G) of its row and chains in registers in the
 // canonical two-level order.  wbase/gstride: address of group 0 of this lane
 // and the step between groups in memory.
-// wait_inputs() runs after the first group's weight loads are issued and
-// before any activation is read; every wave calls it, also a wave without a
-// group, so it may contain a workgroup barrier.
+// hooks.before() runs before the first group's weight loads are issued;
+// hooks() runs after they are issued and before any activation is read;
+// hooks.after() runs once the first activation loads are issued (work that may
+// overlap them).  Every wave calls all three, also a wave without a group, so
+// hooks() may contain a workgroup barrier.
 template <int M, int LAYOUT, bool TO_LDS, typename ACT, bool ONE, typename Wait>
 __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride, int g0, int g1, int step,
                                            const ACT *const (&xrow)[M], const uint16_t *const (&srow)[M],
-                                           float (&acc)[M], float *lds, int lane, Wait &&wait_inputs) {
+                                           float (&acc)[M], float *lds, int lane, Wait &&hooks) {
     // ONE: the caller guarantees at most one group (g0 + step >= g1), so no
     // second register buffer is allocated (17 VGPRs x 4 fewer per lane, more
     // waves per SIMD to keep loads in flight).
@@ -163,13 +162,17 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
     constexpr bool F32 = sizeof(ACT) == 4;
     float4 xv[M], xn[M];
     const bool any = g0 < g1;
+    hooks.before();
     if (any) load_group<LAYOUT>(cur, wbase + g0 * gstride);
-    wait_inputs();
-    if (!any) return;
+    hooks();
     if constexpr (F32) {
+        if (any) {
 #pragma unroll
-        for (int m = 0; m < M; m++) xv[m] = *reinterpret_cast<const float4 *>(xrow[m] + g0 * GROUP_K + 4 * lane);
+            for (int m = 0; m < M; m++) xv[m] = *reinterpret_cast<const float4 *>(xrow[m] + g0 * GROUP_K + 4 * lane);
+        }
     }
+    hooks.after();
+    if (!any) return;
     for (int g = g0; g < g1; g += step) {
         if (!ONE && g + step < g1) {
             if constexpr (F32) {
@@ -215,7 +218,9 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
 }
 
 struct NoWait {
+    __device__ void before() const {}
     __device__ void operator()() const {}
+    __device__ void after() const {}
 };
 
 // One workgroup's share of one 64-row tile: segments [wi * segs_per_wg, ...)
@@ -237,16 +242,18 @@ struct NoWait {
 // non-coherent L2), performed at the device-coherent point like the counter;
 // every thread waits for its exchanges before the barrier that precedes the
 // counter increment, and the last workgroup reads only after that increment
-// returned the final count.  Every thread of the workgroup calls this
-// (it contains barriers); lds_u holds [groups of the workgroup][M][64] floats.
-// Workspace: uint32 counters [tiles] (256-byte aligned), then fp32 segment sums
-// [S][M][n].
+// returned the final count.  handover = true skips the counter: the
+// workgroup only leaves its segment sums (complete when it returns) for a
+// later finish_split (the sequence kernel's next step chains them).  Every
+// thread of the workgroup calls this (it contains barriers); lds_u holds
+// [groups of the workgroup][M][64] floats.  Workspace: uint32 counters [tiles]
+// (256-byte aligned), then fp32 segment sums [S][M][n].
 template <int M, int LAYOUT, typename ACT, bool ONE, typename Wait>
 __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld_x, const uint16_t *__restrict__ xs,
                                           const uint8_t *__restrict__ w, int64_t n, int64_t k, float *__restrict__ y,
                                           int64_t ld_y, int64_t T, int wi, int wgs_per_tile, int segs_per_wg,
                                           uint32_t *__restrict__ ctr, float *__restrict__ part, float *lds_u,
-                                          int *last_wg, Wait &&wait_inputs) {
+                                          int *last_wg, bool handover, Wait &&hooks) {
     const int lane = threadIdx.x & 63;
     const int wv = wave_id();
     const int W = blockDim.x >> 6;
@@ -269,7 +276,7 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
     float unused[M];
     // wave wv takes the workgroup's groups ga + wv, ga + wv + W, ...; each sum lands in its group's LDS slot
     row_groups<M, LAYOUT, true, ACT, ONE>(wbase, gstride, ga + wv, gb, W, xrow, srow, unused,
-                                          lds_u + wv * M * TILE_ROWS, lane, wait_inputs);
+                                          lds_u + wv * M * TILE_ROWS, lane, hooks);
     __syncthreads();
 
     const int t = threadIdx.x;  // the plan gives at least M waves: one thread per (m, row)
@@ -281,8 +288,14 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
     if (chain_thread) {
         for (int64_t sj = s0; sj < s1; sj++) {
             const int64_t gs = sj * SEG_GROUPS, ge = (gs + SEG_GROUPS) < G ? (gs + SEG_GROUPS) : G;
-            float sv = lds_u[((gs - ga) * M + cm) * TILE_ROWS + cr];
-            for (int64_t g = gs + 1; g < ge; g++) sv += lds_u[((g - ga) * M + cm) * TILE_ROWS + cr];
+            float v[SEG_GROUPS];  // the segment's group sums, all LDS reads in flight at once
+#pragma unroll
+            for (int j = 0; j < SEG_GROUPS; j++)
+                v[j] = gs + j < ge ? lds_u[((gs + j - ga) * M + cm) * TILE_ROWS + cr] : 0.0f;
+            float sv = v[0];
+#pragma unroll
+            for (int j = 1; j < SEG_GROUPS; j++)
+                if (gs + j < ge) sv += v[j];
             if (wgs_per_tile == 1) {
                 acc = sj == 0 ? sv : acc + sv;
             } else if (out_ok) {
@@ -296,6 +309,7 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
         return;
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's exchanges have completed
+    if (handover) return;
     __syncthreads();
     if (t == 0) {
         const uint32_t old = __hip_atomic_fetch_add(&ctr[T], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -321,5 +335,38 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
     if (t == 0) __hip_atomic_exchange(&ctr[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+// Chains the handed-over segment sums of tiles T = first, first + stride, ...
+// (< tiles) of a split GEMV and writes their outputs: output (m, row) is
+// ((S_0 + S_1) + S_2) + ..., exactly the chain of tile_unit's last
+// workgroup.  The sums are read with exchanges (returning them to zero) at
+// the device-coherent point where the handing-over workgroups left them.
+// Any number of threads may call this; each takes whole outputs.
+template <int M>
+__device__ __forceinline__ void finish_split(float *__restrict__ part, float *__restrict__ y, int64_t ld_y, int n,
+                                             int S, int first, int stride) {
+    const int tiles = n / TILE_ROWS;
+    for (int T = first; T < tiles; T += stride) {
+        for (int i = threadIdx.x; i < M * TILE_ROWS; i += blockDim.x) {
+            const int cm = i / TILE_ROWS, row = T * TILE_ROWS + i % TILE_ROWS;
+            float acc = 0.0f;
+            uint32_t *pp = (uint32_t *)&part[(int64_t)cm * n + row];
+            const int64_t seg_stride = (int64_t)M * n;  // between consecutive segments' sums
+            for (int b0 = 0; b0 < S; b0 += 4) {
+                float v[4];  // four exchanges in flight (registers are scarce here), then the in-order chain
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    v[j] = b0 + j < S ? __builtin_bit_cast(float, __hip_atomic_exchange(pp + (b0 + j) * seg_stride, 0u,
+                                                                                      __ATOMIC_RELAXED,
+                                                                                      __HIP_MEMORY_SCOPE_AGENT))
+                                      : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    if (b0 + j < S) acc = (b0 + j == 0) ? v[j] : acc + v[j];
+            }
+            y[cm * ld_y + row] = acc;
+        }
+    }
+}
 
 }  // namespace q8k

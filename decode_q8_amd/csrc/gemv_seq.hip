@@ -14,9 +14,14 @@
 // cannot do (the weights do not depend on the activations; the activations
 // do depend on the step before, which the wait models).
 //
-// Step completion is a per-step counter in the workspace, incremented with a
-// device-scope atomic (performed at the device-coherent point) once a unit is
-// done.  The unit that brings it to the step's unit count raises the step's
+// Step completion is counted in the workspace with device-scope atomics
+// (performed at the device-coherent point) once a unit is done: directly in
+// the step's counter when the step has at most SEQ_SUB_MIN_UNITS units, else
+// first in one of SEQ_NSUB sub-counters (unit u in sub-counter u mod SEQ_NSUB)
+// whose last unit then counts the sub-counter in -- hundreds of units
+// incrementing one address queue up behind each other, sixteen do not.  Every
+// counter sits in a 128-byte line of its own and is returned to zero by the
+// unit that completes it.  The unit that completes a step raises the step's
 // flag in FLAG_LINES separate lines with system-scope stores, and a waiting
 // workgroup polls "its" line (workgroup index mod FLAG_LINES, so roughly one
 // line per XCD) with system-scope loads: both bypass the per-XCD L2s, which
@@ -27,8 +32,18 @@
 // grid did not fit on the GPU) records Q8_ERR_LAUNCH in the workspace status
 // word and proceeds -- outputs do not depend on the waits, since every input
 // is ready before the launch.  The unit that completes the last step returns
-// every counter and flag to zero; by then no workgroup is waiting any more,
-// since each wait precedes a unit that the last step transitively depends on.
+// every flag to zero; by then no workgroup is waiting any more, since each
+// wait precedes a unit that the last step transitively depends on.
+//
+// A step whose tiles are split over several workgroups (long rows, few tiles)
+// and that has a successor hands its segment sums over instead of chaining
+// them itself: its workgroups only leave the sums in the workspace (no
+// per-tile counter, no last-workgroup chain), and the successor's units, which
+// wait for the step anyway, chain them and write its outputs (unit u takes
+// tiles u, u + units, ...) while their own activation loads are in flight.
+// Every output is still the same chain of the same segment sums, so it stays
+// bit-identical to its own launch; the step's outputs are complete when its
+// successor is.
 #include "device.hpp"
 #include "gemv_core.hpp"
 #include "launch.hpp"
@@ -39,7 +54,13 @@ constexpr int SEQ_THREADS = 512;
 constexpr uint32_t SEQ_SPIN_LIMIT = 1u << 18;  // polls of roughly 1 us each
 constexpr int FLAG_LINES = 8;
 constexpr int FLAG_LINE_BYTES = 4096;  // one int32 flag per step in each line
+constexpr int SEQ_NSUB = 16;           // sub-counters of a step with many units
+constexpr int SEQ_SUB_MIN_UNITS = 64;  // more units than this: two-level counting
+constexpr int CTR_LINE = 128;          // bytes per counter
+constexpr uint32_t SEQ_PACE_TICKS = 150;  // prefetch stagger per wave, in 10 ns ticks of s_memrealtime
+constexpr int CTR_PER_STEP = SEQ_NSUB + 1;
 static_assert(SEQ_MAX_STEPS * 4 <= FLAG_LINE_BYTES, "a flag line holds every step's flag");
+static_assert((SEQ_NSUB & (SEQ_NSUB - 1)) == 0 && SEQ_NSUB <= SEQ_SUB_MIN_UNITS, "every sub-counter has units");
 
 struct SeqStep {
     const float *x;
@@ -52,7 +73,8 @@ struct SeqStep {
 };
 static_assert(sizeof(SeqStep) == 48, "kernel-argument layout");
 
-// Workspace: [0, 4) status word; step p's done counter at 256 * (p + 1);
+// Workspace: [0, 4) status word; from byte 256 CTR_PER_STEP counters of
+// CTR_LINE bytes per step (the step's counter, then its sub-counters);
 // FLAG_LINES flag lines from flag_off (4 KB aligned); then the split steps'
 // tile counters and segment sums.
 struct SeqArgs {
@@ -62,12 +84,37 @@ struct SeqArgs {
     SeqStep step[SEQ_MAX_STEPS];
 };
 
-__device__ __forceinline__ uint32_t *done_counter(uint8_t *ws, int p) {
-    return reinterpret_cast<uint32_t *>(ws + 256 * (p + 1));
+__device__ __forceinline__ uint32_t *step_counter(uint8_t *ws, int p, int c) {
+    return reinterpret_cast<uint32_t *>(ws + 256 + CTR_LINE * (CTR_PER_STEP * p + c));
 }
 
 __device__ __forceinline__ uint32_t *step_flag(const SeqArgs &a, int line, int p) {
     return reinterpret_cast<uint32_t *>(a.ws + a.flag_off + FLAG_LINE_BYTES * line + 4 * p);
+}
+
+__device__ __forceinline__ uint32_t atomic_inc_old(uint32_t *c) {
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_clear(uint32_t *c) {
+    __hip_atomic_exchange(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts unit u of a step of `units` units in; true for the unit that
+// completes the step (one thread calls this).
+__device__ __forceinline__ bool count_unit(uint8_t *ws, int p, int u, int units) {
+    uint32_t *top = step_counter(ws, p, 0);
+    if (units > SEQ_SUB_MIN_UNITS) {
+        const int c = u & (SEQ_NSUB - 1);
+        uint32_t *sub = step_counter(ws, p, 1 + c);
+        if (atomic_inc_old(sub) != (uint32_t)((units - 1 - c) / SEQ_NSUB)) return false;
+        atomic_clear(sub);
+        if (atomic_inc_old(top) != (uint32_t)(SEQ_NSUB - 1)) return false;
+    } else if (atomic_inc_old(top) != (uint32_t)(units - 1)) {
+        return false;
+    }
+    atomic_clear(top);
+    return true;
 }
 
 // Thread-level wait until *flag != 0 (bounded; see the file comment).
@@ -79,48 +126,98 @@ __device__ __forceinline__ void wait_flag(uint32_t *flag, int32_t *status) {
     __hip_atomic_exchange(status, 6 /* Q8_ERR_LAUNCH */, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ bool hands_over(const SeqArgs &a, int p) { return a.step[p].wgs > 1 && p + 1 < a.count; }
+
+__device__ __forceinline__ uint32_t *split_counters(const SeqArgs &a, int p) {
+    return reinterpret_cast<uint32_t *>(a.ws + 256 * (size_t)a.step[p].ws_off);
+}
+
+__device__ __forceinline__ float *split_sums(const SeqArgs &a, int p) {
+    const int tiles = a.step[p].n >> 6;
+    return reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(split_counters(a, p)) + (tiles * 4 + 255) / 256 * 256);
+}
+
+// Unit u (of `units`) of step p chains its share of step p - 1's handed-over
+// sums: tiles u, u + units, ...
+template <int M>
+__device__ __forceinline__ void finish_previous(const SeqArgs &a, int p, int u, int units) {
+    if (p > 0 && hands_over(a, p - 1)) {
+        const SeqStep &q = a.step[p - 1];
+        finish_split<M>(split_sums(a, p - 1), q.y, q.ld_y, q.n, ((q.k >> 8) + SEG_GROUPS - 1) / SEG_GROUPS, u, units);
+    }
+}
+
+// The per-unit hooks of tile_unit in the sequence: wait for the previous
+// step (first unit of this step on this workgroup only); then, for one
+// activation row, chain this unit's share of the previous step's handed-over
+// sums while the activation loads are in flight.  With more rows the weights
+// and activations held at that point leave no registers for it, and the
+// sequence kernel does it after the unit instead.
+template <int M>
+struct SeqHooks {
+    const SeqArgs &a;
+    int p, wg, u, units;
+    bool ready;
+    bool pace;  // this unit's weights are needed a step or more after the workgroup's previous unit
+    uint64_t t0;  // s_memrealtime when the workgroup took up the unit
+    int32_t *status;
+    __device__ void before() const {
+        if (pace) {  // wave w issues its weight loads w * SEQ_PACE_TICKS after the unit was taken up
+            const uint64_t until = t0 + (uint64_t)SEQ_PACE_TICKS * (threadIdx.x >> 6);
+            for (int i = 0; i < 4096 && __builtin_amdgcn_s_memrealtime() < until; i++) __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __device__ void operator()() const {
+        if (!ready) {
+            if (threadIdx.x == 0) wait_flag(step_flag(a, wg % FLAG_LINES, p - 1), status);
+            __syncthreads();
+        }
+    }
+    __device__ void after() const {
+        if constexpr (M == 1) finish_previous<M>(a, p, u, units);
+    }
+};
+
 template <int M, bool ONE>
 __global__ __launch_bounds__(SEQ_THREADS) void gemv_sequence_kernel(const SeqArgs a) {
     extern __shared__ float lds_u[];  // [groups of a unit][M][64]
     __shared__ int last_wg;
     const int wg = blockIdx.x, nwg = a.nwg;
     int32_t *status = reinterpret_cast<int32_t *>(a.ws);
+    int prev_p = -1;     // step of this workgroup's previous unit
     int start = 0;       // workgroup of step p's first unit: (units of all earlier steps) mod nwg
     for (int p = 0; p < a.count; p++) {
         const SeqStep &st = a.step[p];
         const int tiles = st.n >> 6;
         const int units = tiles * st.wgs;
-        uint32_t *ctr = st.ws_off ? reinterpret_cast<uint32_t *>(a.ws + 256 * (size_t)st.ws_off) : nullptr;
-        float *part = ctr ? reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ctr) + (tiles * 4 + 255) / 256 * 256)
-                          : nullptr;
+        uint32_t *ctr = st.ws_off ? split_counters(a, p) : nullptr;
+        float *part = ctr ? split_sums(a, p) : nullptr;
+        const bool handover = hands_over(a, p);
         // this workgroup's units of step p: u = first, first + nwg, ... (32-bit arithmetic throughout)
         const int first = wg >= start ? wg - start : wg - start + nwg;
         bool ready = p == 0;
         for (int u = first; u < units; u += nwg) {
             const int T = u / st.wgs, wi = u - T * st.wgs;
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // previous unit's LDS reads done
-            auto wait_inputs = [&]() {
-                if (!ready) {
-                    if (threadIdx.x == 0) wait_flag(step_flag(a, wg % FLAG_LINES, p - 1), status);
-                    __syncthreads();
-                }
-            };
             tile_unit<M, 1, float, ONE>(st.x, st.ld_x, nullptr, st.w, st.n, st.k, st.y, st.ld_y, T, wi, st.wgs,
-                                        st.segs, ctr, part, lds_u, &last_wg, wait_inputs);
+                                        st.segs, ctr, part, lds_u, &last_wg, handover,
+                                        SeqHooks<M>{a, p, wg, u, units, ready, prev_p >= 0 && p > prev_p + 1,
+                                                    __builtin_amdgcn_s_memrealtime(), status});
+            prev_p = p;
+            if constexpr (M > 1) finish_previous<M>(a, p, u, units);
             ready = true;
-            // every wave of the unit is done (its LDS work complete); its output
-            // stores may still be in flight: nothing in the launch reads them
+            // every wave of the unit is done (its LDS work complete, handed-over
+            // sums and chained outputs of the previous step written at the
+            // coherent point or stored); its own output stores may still be in
+            // flight: nothing in the launch reads them
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             if (threadIdx.x < 64) {  // wave 0: count the unit in; the last one raises the step's flags
-                uint32_t old = 0;
-                if (threadIdx.x == 0)
-                    old = __hip_atomic_fetch_add(done_counter(a.ws, p), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const bool last = __builtin_amdgcn_readfirstlane(old) == (uint32_t)units - 1;
+                int last = 0;
+                if (threadIdx.x == 0) last = count_unit(a.ws, p, u, units);
+                last = __builtin_amdgcn_readfirstlane(last);
                 if (last && threadIdx.x < FLAG_LINES)
                     __hip_atomic_store(step_flag(a, threadIdx.x, p), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                if (last && p == a.count - 1) {  // the whole sequence is done: clear counters and flags
-                    for (int q = threadIdx.x; q < a.count; q += 64)
-                        __hip_atomic_exchange(done_counter(a.ws, q), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (last && p == a.count - 1) {  // the whole sequence is done: clear the flags
                     for (int i = threadIdx.x; i < FLAG_LINES * a.count; i += 64)
                         __hip_atomic_store(step_flag(a, i / a.count, i % a.count), 0u, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_SYSTEM);
@@ -142,8 +239,9 @@ struct SeqLayout {
 static bool seq_layout(const SeqHostStep *steps, int count, int64_t m, SeqLayout &L) {
     L.one = true;
     L.lds = 0;
-    // status line + one line per done counter, then the flag lines (4 KB aligned)
-    const size_t flag_off = (256 * (size_t)(count + 1) + FLAG_LINE_BYTES - 1) / FLAG_LINE_BYTES * FLAG_LINE_BYTES;
+    // status line + the counters, then the flag lines (4 KB aligned)
+    const size_t ctr_end = 256 + (size_t)CTR_LINE * CTR_PER_STEP * count;
+    const size_t flag_off = (ctr_end + FLAG_LINE_BYTES - 1) / FLAG_LINE_BYTES * FLAG_LINE_BYTES;
     size_t off = flag_off + (size_t)FLAG_LINES * FLAG_LINE_BYTES;
     L.args.count = count;
     L.args.flag_off = (int32_t)flag_off;
