@@ -81,48 +81,82 @@ __device__ __forceinline__ v4h rank1_operand(const uint8_t *p) {
     return __builtin_bit_cast(v4h, v);
 }
 
-// Issue this wave's PER_WAVE direct-to-LDS loads of stage s (blocks 4s..4s+3).
-// Each load writes 64 lanes x size bytes contiguously from the wave-uniform
-// LDS address; the lane decides which global bytes it fetches.  Load i of the
-// stage goes to wave i % WAVES.
+// This wave's PER_WAVE direct-to-LDS loads of a stage (load i of a stage goes
+// to wave i % WAVES).  Each load writes 64 lanes x size bytes contiguously
+// from a wave-uniform LDS offset; the lane decides which global bytes it
+// fetches.  Every address is this lane's stage-0 address plus a wave-uniform
+// offset of the stage, (s >> 1) * p + (s & 1) * q (two stages per 256-value
+// group; the weight records of group s / 2 are RECORD_BYTES apart), so a
+// stage costs one 64-bit add per load instead of the address arithmetic.
 template <int WM, int WN>
-__device__ __forceinline__ void issue_stage(uint8_t *buf, const int8_t *xq, const uint16_t *xs, int64_t M,
-                                            int64_t m_tile, const uint8_t *w_tiles, int64_t tile_stride, int64_t K,
-                                            int64_t nb, int64_t s, int wave, int lane) {
+struct StageLoads {
     using T = Tile<WM, WN>;
-    const int64_t blk0 = s * SB;
-    const int bb0 = (int)(s & 1) * SB;
-    const uint8_t *recs = w_tiles + (s >> 1) * RECORD_BYTES;  // group s/2 of the workgroup's first tile
+    const uint8_t *g[T::PER_WAVE];  // this lane's global address in stage 0
+    int lds[T::PER_WAVE];           // offset in the stage buffer (wave-uniform)
+    int p[T::PER_WAVE], q[T::PER_WAVE];
+    bool wide[T::PER_WAVE];         // 16-byte loads (operands), else 4-byte (scales)
+
+    // Stage 0 of the workgroup at output rows m_tile.. and packed tiles from
+    // w_tiles (tile_stride bytes apart; 0: one tile, reloaded).  Activation
+    // rows past M read row M - 1 (their outputs are not stored).
+    __device__ __forceinline__ void init(const int8_t *xq, const uint16_t *xs, int64_t M, int64_t m_tile,
+                                         const uint8_t *w_tiles, int64_t tile_stride, int64_t K, int64_t nb, int wave,
+                                         int lane) {
 #pragma unroll
-    for (int u = 0; u < T::PER_WAVE; u++) {
-        int i = wave + T::WAVES * u;
-        i = i < T::LOADS ? i : T::LOADS - 1;
-        if (i < T::NA) {  // activations: 8 rows x 128 bytes, row r's chunk c at position c ^ (r & 7)
-            const int r = 8 * i + (lane >> 3);
-            const int c = (lane & 7) ^ (lane >> 3);
-            int64_t row = m_tile + r;
-            row = row < M ? row : M - 1;
-            __builtin_amdgcn_global_load_lds(xq + row * K + blk0 * QK + c * 16, (lds_ptr)(buf + i * 1024), 16, 0, 0);
-        } else if (i < T::NA + T::NB) {  // weights: a tile's 4 block records are 8 KB contiguous
-            const int q = i - T::NA;
-            const uint8_t *rec = recs + (q >> 3) * tile_stride;
-            __builtin_amdgcn_global_load_lds(rec + bb0 * 2048 + (q & 7) * 1024 + lane * 16,
-                                             (lds_ptr)(buf + T::A_BYTES + q * 1024), 16, 0, 0);
-        } else if (i < T::NA + T::NB + T::NSX) {  // activation scales [row][4], 4 bytes per lane
-            const int d = (i - T::NA - T::NB) * 64 + lane;
-            int64_t row = m_tile + (d >> 1);
-            row = row < M ? row : M - 1;
-            __builtin_amdgcn_global_load_lds(xs + row * nb + blk0 + 2 * (d & 1),
-                                             (lds_ptr)(buf + T::SX_OFF + (i - T::NA - T::NB) * 256), 4, 0, 0);
-        } else {  // weight scales [tile][row][4], 4 bytes per lane
-            const int e = i - T::NA - T::NB - T::NSX;
-            const int d = e * 64 + lane;
-            const uint8_t *rec = recs + (d >> 7) * tile_stride;
-            __builtin_amdgcn_global_load_lds(rec + RECORD_Q_BYTES + ((d >> 1) & 63) * 16 + bb0 * 2 + (d & 1) * 4,
-                                             (lds_ptr)(buf + T::SW_OFF + e * 256), 4, 0, 0);
+        for (int u = 0; u < T::PER_WAVE; u++) {
+            int i = wave + T::WAVES * u;
+            i = i < T::LOADS ? i : T::LOADS - 1;  // a wave short of work repeats the last load
+            if (i < T::NA) {  // activations: 8 rows x 128 bytes, row r's chunk c at position c ^ (r & 7)
+                const int r = 8 * i + (lane >> 3);
+                const int c = (lane & 7) ^ (lane >> 3);
+                int64_t row = m_tile + r;
+                row = row < M ? row : M - 1;
+                g[u] = reinterpret_cast<const uint8_t *>(xq + row * K + c * 16);
+                lds[u] = i * 1024;
+                p[u] = 2 * SB * QK;
+                q[u] = SB * QK;
+                wide[u] = true;
+            } else if (i < T::NA + T::NB) {  // weights: a tile's 4 block records are 8 KB contiguous
+                const int e = i - T::NA;
+                g[u] = w_tiles + (e >> 3) * tile_stride + (e & 7) * 1024 + lane * 16;
+                lds[u] = T::A_BYTES + e * 1024;
+                p[u] = RECORD_BYTES;
+                q[u] = SB * 2048;
+                wide[u] = true;
+            } else if (i < T::NA + T::NB + T::NSX) {  // activation scales [row][4], 4 bytes per lane
+                const int e = i - T::NA - T::NB;
+                const int d = e * 64 + lane;
+                int64_t row = m_tile + (d >> 1);
+                row = row < M ? row : M - 1;
+                g[u] = reinterpret_cast<const uint8_t *>(xs + row * nb + 2 * (d & 1));
+                lds[u] = T::SX_OFF + e * 256;
+                p[u] = 2 * SB * 2;
+                q[u] = SB * 2;
+                wide[u] = false;
+            } else {  // weight scales [tile][row][4], 4 bytes per lane
+                const int e = i - T::NA - T::NB - T::NSX;
+                const int d = e * 64 + lane;
+                g[u] = w_tiles + (d >> 7) * tile_stride + RECORD_Q_BYTES + ((d >> 1) & 63) * 16 + (d & 1) * 4;
+                lds[u] = T::SW_OFF + e * 256;
+                p[u] = RECORD_BYTES;
+                q[u] = SB * 2;
+                wide[u] = false;
+            }
         }
     }
-}
+
+    __device__ __forceinline__ void issue(uint8_t *buf, int64_t s) const {
+        const int half = (int)(s >> 1), odd = (int)(s & 1);
+#pragma unroll
+        for (int u = 0; u < T::PER_WAVE; u++) {
+            const uint8_t *src = g[u] + ((int64_t)half * p[u] + odd * q[u]);
+            if (wide[u])
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + lds[u]), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + lds[u]), 4, 0, 0);
+        }
+    }
+};
 
 // Wait until this wave's loads of the stage about to be computed have landed
 // (pending = how many later stages it has issued since), then barrier, so
@@ -145,14 +179,6 @@ struct Lane {
     int sx_off, sw_off;
 };
 
-struct Args {
-    const int8_t *xq;
-    const uint16_t *xs;
-    int64_t M, m_tile;
-    const uint8_t *w_tiles;  // the workgroup's first packed tile
-    int64_t tile_stride;     // bytes between consecutive packed tiles (0: a single tile, reloaded)
-    int64_t K, nb, S;
-};
 
 // Read block bb's operands from the stage buffer and issue its MFMAs: the
 // exact int32 block dots (one i8 MFMA per 32 x 32 tile) and the rank-1 scale
@@ -176,18 +202,16 @@ __device__ __forceinline__ void mfma_block(v16i (&sv)[2], v16f (&sp)[2], const u
 
 // One 256-value group = stages 2g and 2g + 1, resident in buffers 2P and 2P + 1.
 template <int WM, int WN, int P>
-__device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const Lane &ln, const Args &a, int64_t g,
-                                      int wave, int lane) {
+__device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const Lane &ln, const StageLoads<WM, WN> &sl,
+                                      int64_t S, int64_t g) {
     using T = Tile<WM, WN>;
     float ga[2][16];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
         const int64_t s = 2 * g + h;
-        const int64_t last = s + NS - 2 < a.S - 1 ? s + NS - 2 : a.S - 1;  // latest stage issued so far
+        const int64_t last = s + NS - 2 < S - 1 ? s + NS - 2 : S - 1;  // latest stage issued so far
         stage_barrier<T::PER_WAVE>((int)(last - s));
-        if (s + NS - 1 < a.S)
-            issue_stage<WM, WN>(lds + ((2 * P + h + NS - 1) % NS) * T::STAGE_BYTES, a.xq, a.xs, a.M, a.m_tile,
-                                a.w_tiles, a.tile_stride, a.K, a.nb, s + NS - 1, wave, lane);
+        if (s + NS - 1 < S) sl.issue(lds + ((2 * P + h + NS - 1) % NS) * T::STAGE_BYTES, s + NS - 1);
         const uint8_t *buf = lds + (2 * P + h) * T::STAGE_BYTES;
         // Software pipeline over the stage's blocks: the MFMAs of block bb + 1
         // are issued before the VALU epilogue of block bb, so the matrix core
@@ -242,24 +266,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t tiles = N / TILE_ROWS;
     const int64_t T0 = (int64_t)blockIdx.x * WN;  // the workgroup's first packed weight tile
-    const int64_t G = K / GROUP_K;
-    Args a;
-    a.xq = xq;
-    a.xs = xs;
-    a.M = M;
-    a.m_tile = (int64_t)blockIdx.y * T::ROWS;
-    a.w_tiles = w + (T0 * G) * RECORD_BYTES;
-    // tiles past the last one (N not a multiple of the workgroup's columns) reload the last tile
-    a.tile_stride = T0 + WN <= tiles ? G * RECORD_BYTES : 0;
-    a.K = K;
-    a.nb = K / QK;
-    a.S = 2 * G;
+    const int64_t G = K / GROUP_K, S = 2 * G;
+    const int64_t m_tile = (int64_t)blockIdx.y * T::ROWS;
     const bool ragged = T0 + WN > tiles;
-
+    StageLoads<WM, WN> sl;
+    // tiles past the last one (N not a multiple of the workgroup's columns) reload the last tile
+    sl.init(xq, xs, M, m_tile, w + (T0 * G) * RECORD_BYTES, ragged ? 0 : G * RECORD_BYTES, K, K / QK, wave, lane);
     for (int s = 0; s < NS - 1; s++)
-        if (s < a.S)
-            issue_stage<WM, WN>(lds + s * T::STAGE_BYTES, xq, xs, M, a.m_tile, a.w_tiles, a.tile_stride, K, a.nb, s,
-                                wave, lane);
+        if (s < S) sl.issue(lds + s * T::STAGE_BYTES, s);
 
     Lane ln;
     const int row = wm * 32 + l32;
@@ -275,15 +289,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[j][r] = -0.0f;  // -0 + x == x for every x
     for (int64_t g = 0; g < G; g += 2) {
-        group<WM, WN, 0>(acc, lds, ln, a, g, wave, lane);
-        if (g + 1 < G) group<WM, WN, 1>(acc, lds, ln, a, g + 1, wave, lane);
+        group<WM, WN, 0>(acc, lds, ln, sl, S, g);
+        if (g + 1 < G) group<WM, WN, 1>(acc, lds, ln, sl, S, g + 1);
     }
     if (ragged && T0 + wn >= tiles) return;
     const int64_t n_wave = (T0 + wn) * TILE_ROWS;
     // lane holds column l32 of each 32 x 32 tile and rows 8q + 4*half + p
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-        const int64_t orow = a.m_tile + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int64_t orow = m_tile + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (orow >= M) continue;
 #pragma unroll
         for (int j = 0; j < 2; j++) y[orow * ld_y + n_wave + j * 32 + l32] = acc[j][r];
@@ -391,10 +405,9 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(const int8_t *__restric
     }
 }
 
-// Kernel by problem size: 128 x 128 tiles while they give every CU a
-// workgroup, else 32 x 64 strips with k split across the waves.  Each
+// Kernel by problem size: 128 x 128 tiles when there are at least 256 of them
+// (one per CU), else 32 x 64 strips with k split across the waves.  Each
 // output's arithmetic is the same in both, so rows stay bit-identical across m.
-// 128 x 128 tiles when there are at least 256 of them (one per CU), else strips.
 static bool gemm_tiled(int64_t m, int64_t n) { return ((m + 127) / 128) * ((n + 127) / 128) >= 256; }
 
 hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int64_t k, float *y, int64_t ld_y,
