@@ -270,16 +270,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
         }
 #pragma unroll
         for (int g = 0; g < G; g++) {
-            float a = 0.0f;
+            float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four independent chains (value i in chain i % 4)
 #pragma unroll
             for (int i = 0; i < 32; i += 4) {
                 const float4 qv = *reinterpret_cast<const float4 *>(qg + g * HD + 32 * b + i);
-                a = __builtin_fmaf(qv.x, kf[i], a);
-                a = __builtin_fmaf(qv.y, kf[i + 1], a);
-                a = __builtin_fmaf(qv.z, kf[i + 2], a);
-                a = __builtin_fmaf(qv.w, kf[i + 3], a);
+                a[0] = __builtin_fmaf(qv.x, kf[i], a[0]);
+                a[1] = __builtin_fmaf(qv.y, kf[i + 1], a[1]);
+                a[2] = __builtin_fmaf(qv.z, kf[i + 2], a[2]);
+                a[3] = __builtin_fmaf(qv.w, kf[i + 3], a[3]);
             }
-            sc[g] = __builtin_fmaf(a, ks[b], sc[g]);
+            sc[g] = __builtin_fmaf((a[0] + a[1]) + (a[2] + a[3]), ks[b], sc[g]);
         }
     }
 #pragma unroll
@@ -305,24 +305,35 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     __builtin_amdgcn_wave_barrier();
 
     // weighted sum of V over this wave's 64 keys: lanes are dimensions now
-    float acc[DPL][G];
+    // two independent chains over the keys (even and odd), added at the end
+    float acc[DPL][G], acc2[DPL][G];
 #pragma unroll
     for (int e = 0; e < DPL; e++)
 #pragma unroll
-        for (int g = 0; g < G; g++) acc[e][g] = 0.0f;
-#pragma unroll 4
-    for (int jj = 0; jj < 64; jj++) {
-        float pj[G];
+        for (int g = 0; g < G; g++) acc[e][g] = acc2[e][g] = 0.0f;
+#pragma unroll 2
+    for (int jj = 0; jj < 64; jj += 2) {
+        float pj[2][G];
 #pragma unroll
-        for (int g = 0; g < G; g++) pj[g] = pl_w[jj][g];
+        for (int k = 0; k < 2; k++)
+#pragma unroll
+            for (int g = 0; g < G; g++) pj[k][g] = pl_w[jj + k][g];
 #pragma unroll
         for (int e = 0; e < DPL; e++) {
             const int d = lane + 64 * e;
-            const float vv = (float)vt[w][jj][d] * vss[w][d >> 5][jj];
+            const float v0 = (float)vt[w][jj][d] * vss[w][d >> 5][jj];
+            const float v1 = (float)vt[w][jj + 1][d] * vss[w][d >> 5][jj + 1];
 #pragma unroll
-            for (int g = 0; g < G; g++) acc[e][g] = __builtin_fmaf(pj[g], vv, acc[e][g]);
+            for (int g = 0; g < G; g++) {
+                acc[e][g] = __builtin_fmaf(pj[0][g], v0, acc[e][g]);
+                acc2[e][g] = __builtin_fmaf(pj[1][g], v1, acc2[e][g]);
+            }
         }
     }
+#pragma unroll
+    for (int e = 0; e < DPL; e++)
+#pragma unroll
+        for (int g = 0; g < G; g++) acc[e][g] += acc2[e][g];
     // the wave's sums go where its V tile was (read by no one else, and its
     // own reads of it are done: LDS operations of a wave complete in order)
     asm volatile("" ::: "memory");
