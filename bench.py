@@ -158,6 +158,27 @@ def per_launch_ms(run, count, stream, g_filler, reps):
     return total / reps
 
 
+def profiled_field(profile: str, source, key: str):
+    """Field `key` of profiles/<profile> if that summary was taken from the
+    current kernel source (sha256 of the source file, or of the listed files
+    concatenated, matches); otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, val = line.split(":", 1)
+            fields[k.strip()] = val.strip()
+    h = hashlib.sha256()
+    for src in ([source] if isinstance(source, str) else list(source)):
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest() or key not in fields:
+        return None
+    return float(fields[key])
+
+
 def profiled_traffic(profile: str, source: str):
     """HBM bytes per launch recorded in profiles/<profile> by the rocprofv3
     FETCH_SIZE / WRITE_SIZE runs, if that summary was taken from the current
@@ -218,8 +239,9 @@ def oracle_rows(w: np.ndarray, threads: int) -> np.ndarray:
     return out
 
 
-def timed_repeat(fn, min_seconds=2.0, max_reps=50):
-    """Run fn until min_seconds have passed; returns seconds per call."""
+def timed_repeat(fn, min_seconds=10.0, max_reps=100000):
+    """Run fn until min_seconds have passed (the CPU baseline's bounded sample:
+    about 10 s of oracle work); returns (seconds per call, calls)."""
     reps, t0 = 0, time.time()
     while True:
         fn()
@@ -472,13 +494,15 @@ def bench_prefill(args):
         for c in cases:
             xa = oracle.quantize_rows(c["x"], oracle.LAYOUT_ACT)
             pts.append((c, xa, rng.integers(0, c["m"], 2048), rng.integers(0, c["n"], 2048)))
-        t0 = time.time()
-        for c, xa, mi, ni in pts:
-            oracle.matmul_points(xa, c["m"], c["rows"], c["n"], c["k"], mi, ni)
-        dt = time.time() - t0
+        def sample():
+            for c, xa, mi, ni in pts:
+                oracle.matmul_points(xa, c["m"], c["rows"], c["n"], c["k"], mi, ni)
+
+        dt, reps = timed_repeat(sample)
         cpu_ops = sum(2.0 * 2048 * c["k"] for c in cases)
         cpu = {"value": round(cpu_ops / dt / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
-               "sample": f"2048 outputs of each of the 9 prefill cases, single-threaded, {dt:.2f} s"}
+               "sample": f"2048 outputs of each of the 9 prefill cases, single-threaded, {reps} repetitions, "
+                         f"{dt * reps:.1f} s"}
     config = {
         "workload": "prefill GEMM: M in {188, 752, 2048} x (N, K) in {(2048, 2048), (8192, 2048), (2048, 8192)}, "
                     "Q8_0 packed weights, activations with 1% outlier channels x20",
@@ -490,7 +514,9 @@ def bench_prefill(args):
     roof = {"kernel": "q8k::gemm_kernel", "bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
             "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
             "traffic": profiled_traffic("gemm_prefill.txt", "decode_q8_amd/csrc/gemm.hip"),
-            "avg_launch_us": round(float(ms.mean()) * 1e3, 3), "algorithmic_ops_per_launch": int(ops.mean())}
+            "avg_launch_us": round(float(ms.mean()) * 1e3, 3), "algorithmic_ops_per_launch": int(ops.mean()),
+            "mfma_busy_pct": profiled_field("gemm_prefill_counters.txt", "decode_q8_amd/csrc/gemm.hip",
+                                            "mfma_busy_pct")}
     return base_record(args, "Q8_0 prefill GEMM int8 TOPS (%MFMA peak)", value, "TOPS", ms_per_step,
                        "int8xint8->int32 (MFMA), fp32 scale/sum", config, roof, cpu)
 
@@ -588,7 +614,7 @@ def bench_moe(args):
                 hq1 = oracle.swiglu_quantize(yg[:, :F], yg[:, F:])
                 oracle.matmul(hq1, 1, rows_d, H, F, threads=args.threads)
 
-        sec, reps = timed_repeat(oracle_sample, min_seconds=5.0, max_reps=10000)
+        sec, reps = timed_repeat(oracle_sample)
         nb = len(sample) * (s_gu + s_d)
         cpu = {"value": round(nb / sec / 1e9, 3), "unit": "GB/s", "cores": args.threads, "kind": "oracle",
                "sample": f"gate||up, SwiGLU and down of the {len(sample)} pairs routed to 2 experts, "
@@ -689,10 +715,10 @@ def bench_norm(args):
     cpu = None
     if not args.no_cpu_baseline:
         c = timed[big]
-        sec, reps = timed_repeat(lambda: oracle.rmsnorm_quantize(c["x"], c["res"], c["gain"], wl.NORM_EPS),
-                                 min_seconds=3.0)
+        sec, reps = timed_repeat(lambda: oracle.rmsnorm_quantize(c["x"], c["res"], c["gain"], wl.NORM_EPS))
         cpu = {"value": round(norm_bytes(c["rows"], k) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "sample": f"the {c['rows']}-row launch, {reps} repetitions, single-threaded"}
+               "kind": "oracle",
+               "sample": f"the {c['rows']}-row launch, {reps} repetitions, single-threaded, {sec * reps:.1f} s"}
     config = {
         "workload": f"fused residual + RMSNorm + Q8_0 quantize: rows in {{188, 752, 2048}} x hidden {k} "
                     "(Llama-3.2-1B prefill tokens), residual stream with 1% outlier channels x20",
@@ -807,9 +833,10 @@ def bench_kv(args):
     if not args.no_cpu_baseline:
         q1 = q_ref[:1]
         sec, reps = timed_repeat(lambda: oracle.attention_decode(q1, kc, ks, vc, vs, np.zeros(1, np.int32),
-                                                                 np.full(1, L, np.int32), scale), min_seconds=3.0)
+                                                                 np.full(1, L, np.int32), scale))
         cpu = {"value": round(abytes / S / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"attention of one sequence (32 heads x 4096 positions) of one layer, {reps} repetitions"}
+               "sample": f"attention of one sequence (32 heads x 4096 positions) of one layer, {reps} repetitions, "
+                         f"{sec * reps:.1f} s"}
     config = {
         "workload": "Llama-3.2-1B decode-step attention over a Q8 KV cache: 16 layers, 16 sequences x 4096 cached "
                     "positions, 32 query / 8 KV heads of 64; per layer the new tokens' fused norm + rope + cache "
