@@ -226,25 +226,21 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     const int last = nv > 0 ? nv - 1 : 0;
     const bool valid = lane < nv;
     // coalesced direct-to-LDS loads: each instruction moves 1 KB of whole rows
-    // (rows past the valid ones repeat the last valid row: in bounds, masked)
+    // (rows past the valid ones repeat the last valid row: in bounds, masked).
+    // K and its scales first; V and its scales are issued once the lanes hold
+    // their K rows, so they arrive while the scores are computed.
 #pragma unroll
     for (int t = 0; t < W16; t++) {
         const int p16 = 64 * t + lane;                 // 16-byte position in the tile
         const int r = p16 / W16, slot = p16 % W16;
-        const int rc = min(r, last);
         const int chunk = slot ^ (r & (W16 - 1));      // the K row chunk stored at this slot
-        __builtin_amdgcn_global_load_lds(k_cache + (r0 + rc) * HD + chunk * 16, (lds_ptr)(&kt[w][0] + 1024 * t), 16,
-                                         0, 0);
-        __builtin_amdgcn_global_load_lds(v_cache + (r0 + rc) * HD + slot * 16, (lds_ptr)(&vt[w][0][0] + 1024 * t),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(k_cache + (r0 + min(r, last)) * HD + chunk * 16,
+                                         (lds_ptr)(&kt[w][0] + 1024 * t), 16, 0, 0);
     }
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-        const int rc = min(lane, last);
-        __builtin_amdgcn_global_load_lds(k_scale + (r0 + rc) * NB + b, (lds_ptr)(&kss[w][b][0]), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(v_scale + (r0 + rc) * NB + b, (lds_ptr)(&vss[w][b][0]), 4, 0, 0);
-    }
-    // the wave's own loads have landed in LDS (nothing else touches its tiles)
+    for (int b = 0; b < NB; b++)
+        __builtin_amdgcn_global_load_lds(k_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&kss[w][b][0]), 4, 0, 0);
+    // the wave's own K loads have landed in LDS (nothing else touches its tiles)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
     uint4 kr[W16];
@@ -254,6 +250,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
         kr[i] = *reinterpret_cast<const uint4 *>(&kt[w][0] + lane * HD + 16 * (i ^ (lane & (W16 - 1))));
 #pragma unroll
     for (int b = 0; b < NB; b++) ks[b] = kss[w][b][lane];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the K reads are done before the V tile is written
+#pragma unroll
+    for (int t = 0; t < W16; t++) {
+        const int p16 = 64 * t + lane;
+        const int r = p16 / W16, slot = p16 % W16;
+        __builtin_amdgcn_global_load_lds(v_cache + (r0 + min(r, last)) * HD + slot * 16,
+                                         (lds_ptr)(&vt[w][0][0] + 1024 * t), 16, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+        __builtin_amdgcn_global_load_lds(v_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&vss[w][b][0]), 4, 0, 0);
 
     // scores of this lane's key for the G heads, per 32-value block then scaled
     float sc[G];
@@ -300,8 +307,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
         pl_w[lane][g] = p[g];
         lw[g] = wave_sum_f32(p[g]);
     }
-    // the wave reads back its own V rows from LDS: keep the writes above the reads
-    asm volatile("" ::: "memory");
+    // the wave reads back its own V rows from LDS: keep the writes above the
+    // reads, and wait for the V loads
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
 
     // weighted sum of V over this wave's 64 keys: lanes are dimensions now
