@@ -84,6 +84,22 @@ def test_general_path_many_groups_per_wave():
         assert bits_equal(down(s["y"]), _single(s, 2)), f"step {i}"
 
 
+@pytest.mark.parametrize("m", [1, 3])
+def test_split_steps_back_to_back_and_last(m):
+    """Steps whose tiles are split over several workgroups (long rows, few
+    tiles): two in a row (the second chains the first's segment sums while
+    handing over its own), one followed by a single-unit step (that unit
+    chains every tile of it), and one as the last step (chained inside the
+    step itself).  Every step equals its own launch; the workspace returns to
+    zero."""
+    shapes = [(2048, 8192), (1024, 16384), (64, 256), (2048, 8192), (512, 2048), (1024, 8192)]
+    steps = _chain(shapes, m, seed=700 + m)
+    ws = _run(steps, m)
+    assert int(down(ws).astype(np.uint8).any()) == 0, "workspace not returned to zero"
+    for i, s in enumerate(steps):
+        assert bits_equal(down(s["y"]), _single(s, m)), f"step {i} ({s['n']}x{s['k']}) differs from its own launch"
+
+
 def test_maximum_length_and_repeat():
     """Q8_SEQUENCE_MAX_STEPS small steps (the longest argument block), called
     twice on one workspace: identical results, workspace zero after each."""
