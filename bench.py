@@ -23,11 +23,16 @@ routed GEMVs, SwiGLU, weighted combine), ``norm`` (the fused residual + RMSNorm 
 Q8_0 quantize producer at the prefill row counts, hidden 2048), ``kv`` (a
 decode step's attention over a Q8 KV cache: 16 layers, 16 sequences x 4096
 positions), ``copy`` (a device copy of 1 GiB, used to calibrate rocprofv3's
-byte counters).
+byte counters), ``read`` (the streaming-read ceiling, q8_stream_read over
+1 GiB and over the decode step's, the LM head's and single matrices' sizes).
 
 The JSON line carries the metric, the roofline of the dominant kernel (its
-average launch duration measured with HIP events on the stream it runs on)
-and the CPU oracle timed on the host on a bounded sample of the same workload.
+average launch duration measured with HIP events on the stream it runs on),
+the 10th/50th/90th percentile of the per-replay times, and the CPU oracle
+timed on the host on a bounded sample of the same workload.  The decode step's
+line also carries the streaming-read ceiling measured in the same run on a
+buffer of the step's weight bytes, and the step's fraction of it (the pages'
+own yardstick for weight-streaming decode).
 """
 from __future__ import annotations
 
@@ -53,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "single", "batched", "prefill", "moe", "norm", "kv", "copy"])
+                    choices=["decode", "single", "batched", "prefill", "moe", "norm", "kv", "copy", "read"])
     ap.add_argument("--m", type=int, default=1, help="rows per GEMV for --workload batched")
     ap.add_argument("--unfused", action="store_true", help="decode: separate quantize and GEMV launches")
     ap.add_argument("--per-matrix", action="store_true",
@@ -92,6 +97,7 @@ def base_record(args, metric, value, unit, ms_per_step, dtype, config, roofline,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_p10_p50_p90": [STEP_SPREAD.get(k) for k in ("p10", "p50", "p90")],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -118,9 +124,16 @@ def hbm_roofline(kernel, bytes_per_launch, avg_ms):
     }
 
 
+# Spread of the per-replay times of the most recent graph_time call (ms at the
+# 10th, 50th and 90th percentile), reported beside the mean in every record.
+STEP_SPREAD = {}
+
+
 def graph_time(run, stream, steps, warmup):
     """Capture run(stream) into a graph, replay warmup + steps times; returns
-    (ms per replay, graph)."""
+    (ms per replay, graph).  The mean comes from one event pair around the
+    `steps` timed replays; an event between consecutive replays gives the
+    per-replay times whose percentiles go to STEP_SPREAD."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -129,14 +142,39 @@ def graph_time(run, stream, steps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    t = Timer(torch.cuda.current_stream())
-    t.start()
-    for _ in range(steps):
+    cur = torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(cur)
+    for i in range(steps):
         g.replay()
-    t.stop()
-    ms = t.ms() / steps
+        marks[i + 1].record(cur)
+    marks[-1].synchronize()
+    ms = marks[0].elapsed_time(marks[-1]) / steps
+    each = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+    STEP_SPREAD.clear()
+    STEP_SPREAD.update({f"p{q}": round(float(np.percentile(each, q)), 5) for q in (10, 50, 90)})
     torch.cuda.synchronize()
     return ms, g
+
+
+def read_ceiling_gbs(nbytes, steps=20, warmup=3):
+    """The streaming-read ceiling: q8_stream_read over a fresh device buffer of
+    nbytes (rounded down to 16), graph-replayed; GB/s by the mean replay."""
+    import torch
+
+    from decode_q8_amd import q8
+    n = nbytes // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    saved = dict(STEP_SPREAD)
+    ms, _ = graph_time(lambda s: q8.q8_stream_read(buf, n, sink, s.cuda_stream), stream, steps, warmup)
+    STEP_SPREAD.clear()
+    STEP_SPREAD.update(saved)
+    del buf
+    torch.cuda.synchronize()
+    return n / (ms * 1e-3) / 1e9
 
 
 def per_launch_ms(run, count, stream, g_filler, reps):
@@ -409,6 +447,11 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
                                  if mt.layer == 0 or mt.name == "lm_head"},
         "prep_seconds": round(prep_s, 1),
     }
+    if len(mats) > 1:
+        # the pages' yardstick: a pure streaming read of the same number of bytes
+        ceiling = read_ceiling_gbs(step.weight_bytes)
+        config["stream_read_ceiling_GBs"] = round(ceiling, 1)
+        config["frac_of_stream_read_ceiling"] = round(value / ceiling, 4)
     metric = ("Q8_0 matmul weight GB/s (%HBM peak) at M=1" if m == 1 else f"Q8_0 matmul weight GB/s at M={m}")
     if mode == "sequence":
         kname = "q8k::gemv_sequence_kernel<%d>" % m
@@ -869,6 +912,33 @@ def bench_copy(args):
                        {"workload": "copy 1 GiB", "bytes_read": n, "bytes_written": n}, None, None)
 
 
+def bench_read(args):
+    """The streaming-read ceiling (q8_stream_read) at 1 GiB, with the sizes of
+    the decode step's weights, the LM head and one gate||up matrix beside it."""
+    from decode_q8_amd import q8
+    import torch
+    n = 1 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    ms_per_step, _ = graph_time(lambda s: q8.q8_stream_read(buf, n, sink, s.cuda_stream), stream, args.steps,
+                                args.warmup)
+    spread = dict(STEP_SPREAD)
+    del buf
+    torch.cuda.synchronize()
+    value = n / (ms_per_step * 1e-3) / 1e9
+    sizes = {"decode_step_weights_1313MB": 1312980992, "lm_head_279MB": 128256 * 64 * 34,
+             "gate_up_35.7MB": 16384 * 64 * 34, "qkv_6.7MB": 3072 * 64 * 34}
+    others = {k: round(read_ceiling_gbs(b), 1) for k, b in sizes.items()}
+    STEP_SPREAD.clear()
+    STEP_SPREAD.update(spread)
+    roof = hbm_roofline("q8k::stream_read_kernel", float(n), ms_per_step)
+    return base_record(args, "streaming-read GB/s", value, "GB/s", ms_per_step, "u8",
+                       {"workload": "plain streaming read of 1 GiB (each byte once, 16-byte loads)",
+                        "bytes_read": n, "other_sizes_GBs": others}, roof, None)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -880,7 +950,8 @@ def main():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
     fn = {"decode": bench_decode, "batched": bench_decode, "single": bench_single, "prefill": bench_prefill,
-          "moe": bench_moe, "norm": bench_norm, "kv": bench_kv, "copy": bench_copy}[args.workload]
+          "moe": bench_moe, "norm": bench_norm, "kv": bench_kv, "copy": bench_copy,
+          "read": bench_read}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
 

@@ -24,7 +24,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libq8.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["quantize.hip", "repack.hip", "gemv.hip", "gemv_seq.hip", "gemm.hip", "norm.hip", "moe.hip", "kv.hip"]
+HIP_SOURCES = ["quantize.hip", "repack.hip", "gemv.hip", "gemv_seq.hip", "gemm.hip", "norm.hip", "moe.hip", "kv.hip", "measure.hip"]
 HOST_SOURCES = ["api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",

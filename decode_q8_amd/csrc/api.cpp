@@ -333,4 +333,15 @@ int q8_grouped_matmul(const void *x_q, int64_t x_rows, int x_per_pair, const int
                                         expert_stride_bytes, n, k, y, workspace, stream));
 }
 
+int q8_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    if (!buf || !sink) return Q8_ERR_ARG;
+    if (bytes % 16) return Q8_ERR_SHAPE;
+    if (!aligned16(buf) || ((uintptr_t)sink & 3u)) return Q8_ERR_ALIGN;
+    if (bytes == 0) return Q8_OK;
+    if (overlap(sink, 4, buf, bytes)) return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_stream_read(buf, bytes, sink, stream));
+}
+
 }  // extern "C"

@@ -82,4 +82,8 @@ hipError_t launch_grouped(const void *x_q, int64_t x_rows, int x_per_pair, const
                           int topk, const void *w, int64_t n_experts, int64_t expert_stride, int64_t n, int64_t k,
                           float *y, void *workspace, hipStream_t s);
 
+// Measurement only: a plain streaming read of `bytes` (a multiple of 16)
+// that XORs the XOR of all its 32-bit words into *sink.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
+
 }  // namespace q8k

@@ -22,7 +22,7 @@ Q8_BLOCK_BYTES = 34
 Q8_TILE_ROWS = 64
 Q8_GEMV_MAX_ROWS = 8
 Q8_SEQUENCE_MAX_STEPS = 72
-Q8_ABI_VERSION = 3
+Q8_ABI_VERSION = 4
 Q8_NORM_MAX_K = 16384
 Q8_ROUTE_MAX_EXPERTS = 1024
 Q8_ROUTE_MAX_TOPK = 32
@@ -57,6 +57,7 @@ SIGNATURES = {
                              _P], _I),
     "q8_grouped_workspace_bytes": ([_I64, _I, _I64, _I64, _I64], _SZ),
     "q8_grouped_matmul": ([_P, _I64, _I, _P, _I64, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P], _I),
+    "q8_stream_read": ([_P, _SZ, _P, _P], _I),
 }
 
 
@@ -226,6 +227,10 @@ def q8_grouped_matmul(x_q, x_rows: int, x_per_pair: int, topk_ids, tokens: int, 
 
 
 # --- torch conveniences (allocation + one call each) -------------------------
+
+def q8_stream_read(buf, nbytes: int, sink, stream=None) -> int:
+    return _check(lib().q8_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "q8_stream_read")
+
 
 def quantize(x, layout: int = Q8_LAYOUT_ACT, stream=None):
     """fp32 [rows][k] CUDA tensor (unit column stride) -> new uint8 tensor."""

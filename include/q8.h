@@ -71,8 +71,9 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 3u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize, the
-                              MoE router, SwiGLU and combine, and the Q8 KV cache entry points */
+#define Q8_ABI_VERSION 4u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize, the
+                              MoE router, SwiGLU and combine, and the Q8 KV cache entry points;
+                              4: q8_stream_read */
 #define Q8_BLOCK 32          /* values per block */
 #define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
 #define Q8_TILE_ROWS 64      /* rows per packed record */
@@ -387,6 +388,19 @@ int q8_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int
                         const float *k_scale, const int8_t *v_cache, const float *v_scale, int64_t n_slots,
                         const int32_t *base, const int32_t *len, int64_t max_len, float scale, float *out,
                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Measurement: the streaming-read ceiling ("ferro" README, "Using LFM2.5
+ * language models": decode weight streaming is reported as a fraction of what
+ * a pure streaming-read kernel reaches on the same device). ---- */
+
+/* Reads every byte of buf once, in coalesced 16-byte loads, and XORs the XOR
+ * of all its 32-bit words into *sink (so *sink = 0 before the call leaves the
+ * buffer's XOR checksum there).  Its only purpose is to time the device's
+ * streaming-read bandwidth; it computes nothing the matmuls use.
+ *  buf   device, 16-byte aligned, bytes a multiple of 16 (0: no-op).
+ *  sink  device uint32, 4-byte aligned, outside buf.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     m = re.search(r"#define Q8_ABI_VERSION (\d+)u", open(HEADER).read())
-    assert int(m.group(1)) == q8.Q8_ABI_VERSION == q8.q8_abi_version() == 3
+    assert int(m.group(1)) == q8.Q8_ABI_VERSION == q8.q8_abi_version() == 4
     for s in range(7):
         assert q8.status_str(s).startswith("Q8_")
     assert q8.status_str(99) == "Q8_ERR_UNKNOWN"
@@ -337,3 +337,14 @@ def test_valid_request_without_device_reports_device_error():
     need = q8.q8_attention_workspace_bytes(4, 8, 2, 64, 512)
     assert _raw("q8_attention_decode", A, 4, 8, 2, 64, B, C, D, 0x7F0000400000, 1024, 0x7F0000500000,
                 0x7F0000500040, 512, 0.125, 0x7F0000600000, 0x7F0000700000, need, None) == q8.Q8_ERR_DEVICE
+
+
+def test_stream_read_validation():
+    f = "q8_stream_read"
+    assert _raw(f, None, 1024, B, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 1024, None, None) == q8.Q8_ERR_ARG
+    assert _raw(f, A, 1000, B, None) == q8.Q8_ERR_SHAPE           # not a multiple of 16
+    assert _raw(f, A + 4, 1024, B, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 1024, B + 2, None) == q8.Q8_ERR_ALIGN
+    assert _raw(f, A, 1024, A + 512, None) == q8.Q8_ERR_ARG      # sink inside the buffer
+    assert _raw(f, A, 0, B, None) == q8.Q8_OK                    # nothing to read: no-op, no launch
