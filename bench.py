@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="decode: separate quantize and GEMV launches")
     ap.add_argument("--per-matrix", action="store_true",
                     help="decode: one fused quantize+GEMV launch per matrix instead of one launch per step")
+    ap.add_argument("--layout", choices=["packed", "rows"], default="packed",
+                    help="decode/batched: weight layout; rows (row-contiguous Q8_0) implies one launch per matrix")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     return ap.parse_args()
@@ -299,7 +301,7 @@ class DecodeStep:
     q8_quantize_matmul launch per matrix) and "unfused" (q8_quantize_rows then
     q8_matmul per matrix)."""
 
-    def __init__(self, mats, workload, m, threads, keep_host_rows, mode):
+    def __init__(self, mats, workload, m, threads, keep_host_rows, mode, rows_layout=False):
         import torch
 
         import workloads as wl
@@ -307,6 +309,7 @@ class DecodeStep:
 
         self.q8, self.m, self.mats, self.mode = q8, m, mats, mode
         self.fused = mode != "unfused"
+        self.layout = q8.Q8_LAYOUT_ROWS if rows_layout else q8.Q8_LAYOUT_PACKED
         dev = torch.device("cuda", 0)
         self.w_packed, self.host_rows = [], []
         chunk = 8
@@ -317,7 +320,7 @@ class DecodeStep:
             for mt, w in zip(group, ws):
                 wt = torch.from_numpy(w).to(dev)
                 wr = q8.quantize(wt, q8.Q8_LAYOUT_ROWS)
-                self.w_packed.append(q8.repack(wr, mt.n, mt.k))
+                self.w_packed.append(wr if rows_layout else q8.repack(wr, mt.n, mt.k))
                 del wt, wr
                 if keep_host_rows:
                     self.host_rows.append(oracle_rows(w, threads))
@@ -357,10 +360,10 @@ class DecodeStep:
             if gemv_timers is not None:
                 gemv_timers[i].start()
             if self.fused:
-                q8.q8_quantize_matmul(xt, mt.k, self.m, self.w_packed[i], q8.Q8_LAYOUT_PACKED, mt.n, mt.k,
+                q8.q8_quantize_matmul(xt, mt.k, self.m, self.w_packed[i], self.layout, mt.n, mt.k,
                                       self.y[i], mt.n, self.ws, self.ws.numel(), s)
             else:
-                q8.q8_matmul(qb, self.m, self.w_packed[i], q8.Q8_LAYOUT_PACKED, mt.n, mt.k, self.y[i], mt.n,
+                q8.q8_matmul(qb, self.m, self.w_packed[i], self.layout, mt.n, mt.k, self.y[i], mt.n,
                              self.ws, self.ws.numel(), s)
             if gemv_timers is not None:
                 gemv_timers[i].stop()
@@ -383,8 +386,11 @@ class DecodeStep:
 def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
     import torch
     t0 = time.time()
-    mode = "unfused" if args.unfused else ("fused" if args.per_matrix or not allow_sequence else "sequence")
-    step = DecodeStep(mats, workload, m, args.threads, keep_host_rows=not args.no_cpu_baseline, mode=mode)
+    rows = args.layout == "rows"
+    mode = ("unfused" if args.unfused else
+            ("fused" if args.per_matrix or rows or not allow_sequence else "sequence"))
+    step = DecodeStep(mats, workload, m, args.threads, keep_host_rows=not args.no_cpu_baseline, mode=mode,
+                      rows_layout=rows)
     prep_s = time.time() - t0
     stream = torch.cuda.Stream()
 
@@ -436,8 +442,9 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
                 "fused": f"{len(mats)} fused quantize+GEMV",
                 "unfused": f"{len(mats)} quantize + {len(mats)} GEMV"}[mode]
     config = {
-        "workload": label,
+        "workload": label if not rows else label.replace("Q8_0 packed", "Q8_0 row-contiguous"),
         "m": m,
+        "layout": args.layout,
         "weight_bytes": step.weight_bytes,
         "launches_per_step": launches,
         "hip_graph": True,
@@ -461,12 +468,12 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
             roof["traffic"] = profiled_traffic("gemv_sequence_decode_step_llama1b.txt",
                                                ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
     else:
-        kname = "q8k::gemv_kernel<%d, packed, %s>" % (m, "fp32 in" if step.fused else "int8 in")
+        kname = "q8k::gemv_kernel<%d, %s, %s>" % (m, args.layout, "fp32 in" if step.fused else "int8 in")
         avg_ms = seq_ms if seq_ms is not None else float(gemv_ms.mean())
         roof = hbm_roofline(kname, float(gemv_bytes.mean()), avg_ms)
         roof["timing"] = ("one event pair around all launches of the step, queued ahead; per launch = total / "
                           "launches" if seq_ms is not None else "one event pair per launch, queued ahead")
-        if step.fused and m == 1 and len(mats) == 65:
+        if step.fused and m == 1 and len(mats) == 65 and not rows:
             roof["traffic"] = profiled_traffic("gemv_decode_step_llama1b.txt",
                                                ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
     return base_record(args, metric, value, "GB/s", ms_per_step, "int8xint8->int32, fp32 scale/sum", config,
