@@ -196,15 +196,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     constexpr int NB = HD / 32;
     constexpr int W16 = HD / 16;  // 16-byte words per cached row
     constexpr int DPL = HD / 64;  // dimensions per lane in the weighted sum
-    // per wave: its 64 keys' K rows (XOR-swizzled 16-byte chunks) and V rows
-    // (later its G x HD weighted sums, G <= 16), their block scales ([block]
-    // [key]) and the softmax weights
-    __shared__ __align__(16) int8_t kt[4][64 * HD];
-    __shared__ __align__(16) int8_t vt[4][64][HD];
-    static_assert(G * HD * 4 <= 64 * HD, "the weighted sums fit in the wave's V tile");
-    __shared__ float kss[4][NB][64], vss[4][NB][64];
+    // per wave one tile: its 64 keys' K rows (XOR-swizzled 16-byte chunks),
+    // then, once the lanes hold their K rows, its V rows, then its G x HD
+    // weighted sums (G <= 16); likewise one array for the block scales
+    // ([block][key]: K's, then V's); and the softmax weights [key][G].  Sharing
+    // the tiles keeps a workgroup at 22 KB of LDS for HD = 64 (7 workgroups
+    // per CU instead of 4 with separate K and V tiles).
+    __shared__ __align__(16) int8_t kv[4][64 * HD];
+    static_assert(G * HD * 4 <= 64 * HD, "the weighted sums fit in the wave's tile");
+    __shared__ float ksv[4][NB][64];
+    __shared__ float pls[4][64][G];
     __shared__ float redm[4][G], reds[4][G];
-    static_assert(64 * G * 4 <= 64 * HD, "the softmax weights fit in the wave's K tile");
     const int sp = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int splits = gridDim.x;
     if ((sp | kvh | s) == 0 && threadIdx.x == 0)  // the status word of this call starts clear
@@ -235,11 +237,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
         const int r = p16 / W16, slot = p16 % W16;
         const int chunk = slot ^ (r & (W16 - 1));      // the K row chunk stored at this slot
         __builtin_amdgcn_global_load_lds(k_cache + (r0 + min(r, last)) * HD + chunk * 16,
-                                         (lds_ptr)(&kt[w][0] + 1024 * t), 16, 0, 0);
+                                         (lds_ptr)(&kv[w][0] + 1024 * t), 16, 0, 0);
     }
 #pragma unroll
     for (int b = 0; b < NB; b++)
-        __builtin_amdgcn_global_load_lds(k_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&kss[w][b][0]), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(k_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&ksv[w][b][0]), 4, 0, 0);
     // the wave's own K loads have landed in LDS (nothing else touches its tiles)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
@@ -247,20 +249,21 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     float ks[NB];
 #pragma unroll
     for (int i = 0; i < W16; i++)
-        kr[i] = *reinterpret_cast<const uint4 *>(&kt[w][0] + lane * HD + 16 * (i ^ (lane & (W16 - 1))));
+        kr[i] = *reinterpret_cast<const uint4 *>(&kv[w][0] + lane * HD + 16 * (i ^ (lane & (W16 - 1))));
 #pragma unroll
-    for (int b = 0; b < NB; b++) ks[b] = kss[w][b][lane];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the K reads are done before the V tile is written
+    for (int b = 0; b < NB; b++) ks[b] = ksv[w][b][lane];
+    // the K rows and scales are in registers before V overwrites them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int t = 0; t < W16; t++) {
         const int p16 = 64 * t + lane;
         const int r = p16 / W16, slot = p16 % W16;
         __builtin_amdgcn_global_load_lds(v_cache + (r0 + min(r, last)) * HD + slot * 16,
-                                         (lds_ptr)(&vt[w][0][0] + 1024 * t), 16, 0, 0);
+                                         (lds_ptr)(&kv[w][0] + 1024 * t), 16, 0, 0);
     }
 #pragma unroll
     for (int b = 0; b < NB; b++)
-        __builtin_amdgcn_global_load_lds(v_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&vss[w][b][0]), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(v_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&ksv[w][b][0]), 4, 0, 0);
 
     // scores of this lane's key for the G heads, per 32-value block then scaled
     float sc[G];
@@ -294,11 +297,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
 
     // this wave's softmax over its 64 keys (exp2 domain); waves run on
     // independently until the one barrier that combines them
-    // the softmax weights [key][G] go where the wave's K rows were: every
-    // lane has read its row (LDS operations of a wave complete in order)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
-    float(*pl_w)[G] = reinterpret_cast<float(*)[G]>(&kt[w][0]);
+    float(*pl_w)[G] = pls[w];
     float mw[G], lw[G], p[G];
 #pragma unroll
     for (int g = 0; g < G; g++) {
@@ -329,8 +328,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
 #pragma unroll
         for (int e = 0; e < DPL; e++) {
             const int d = lane + 64 * e;
-            const float v0 = (float)vt[w][jj][d] * vss[w][d >> 5][jj];
-            const float v1 = (float)vt[w][jj + 1][d] * vss[w][d >> 5][jj + 1];
+            const float v0 = (float)kv[w][jj * HD + d] * ksv[w][d >> 5][jj];
+            const float v1 = (float)kv[w][(jj + 1) * HD + d] * ksv[w][d >> 5][jj + 1];
 #pragma unroll
             for (int g = 0; g < G; g++) {
                 acc[e][g] = __builtin_fmaf(pj[0][g], v0, acc[e][g]);
@@ -346,7 +345,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     // own reads of it are done: LDS operations of a wave complete in order)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_wave_barrier();
-    float(*accw_w)[HD] = reinterpret_cast<float(*)[HD]>(&vt[w][0][0]);
+    float(*accw_w)[HD] = reinterpret_cast<float(*)[HD]>(&kv[w][0]);
 #pragma unroll
     for (int e = 0; e < DPL; e++)
 #pragma unroll
@@ -374,7 +373,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
 #pragma unroll
         for (int ww = 0; ww < 4; ww++) {
             const float f = redm[ww][g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(redm[ww][g] - m);
-            a = __builtin_fmaf(f, reinterpret_cast<const float(*)[HD]>(&vt[ww][0][0])[g][d], a);
+            a = __builtin_fmaf(f, reinterpret_cast<const float(*)[HD]>(&kv[ww][0])[g][d], a);
         }
         o[g * (HD + 2) + 2 + d] = a;
     }
