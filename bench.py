@@ -56,7 +56,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "single", "batched", "prefill", "moe", "norm", "kv", "copy", "read"])
     ap.add_argument("--m", type=int, default=1, help="rows per GEMV for --workload batched")
@@ -134,8 +134,10 @@ STEP_SPREAD = {}
 def graph_time(run, stream, steps, warmup):
     """Capture run(stream) into a graph, replay warmup + steps times; returns
     (ms per replay, graph).  The mean comes from one event pair around the
-    `steps` timed replays; an event between consecutive replays gives the
-    per-replay times whose percentiles go to STEP_SPREAD."""
+    `steps` timed replays.  A second pass of `steps` replays, with an event
+    between consecutive replays, gives the per-replay times whose percentiles
+    go to STEP_SPREAD (the events themselves add a little time, so that pass
+    is not the mean)."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -144,6 +146,13 @@ def graph_time(run, stream, steps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    t = Timer(torch.cuda.current_stream())
+    t.start()
+    for _ in range(steps):
+        g.replay()
+    t.stop()
+    ms = t.ms() / steps
+    torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     marks[0].record(cur)
@@ -151,12 +160,26 @@ def graph_time(run, stream, steps, warmup):
         g.replay()
         marks[i + 1].record(cur)
     marks[-1].synchronize()
-    ms = marks[0].elapsed_time(marks[-1]) / steps
     each = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
     STEP_SPREAD.clear()
     STEP_SPREAD.update({f"p{q}": round(float(np.percentile(each, q)), 5) for q in (10, 50, 90)})
     torch.cuda.synchronize()
     return ms, g
+
+
+def replay_ms(graph, steps):
+    """Mean ms per replay of an already captured graph over `steps` replays
+    (one event pair on the current stream): an identical-control repeat of a
+    timed configuration, taken later in the same run."""
+    import torch
+    t = Timer(torch.cuda.current_stream())
+    t.start()
+    for _ in range(steps):
+        graph.replay()
+    t.stop()
+    ms = t.ms() / steps
+    torch.cuda.synchronize()
+    return ms
 
 
 def read_ceiling_gbs(nbytes, steps=20, warmup=3):
@@ -415,6 +438,7 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
     gemv_ms = per_launch_ms(step.run_per_matrix, len(step.mats), stream, g_filler=graph,
                             reps=max(1, min(args.steps, 10)))
     gemv_bytes = np.array([step.gemv_bytes(i) for i in range(len(step.mats))], dtype=np.float64)
+    ctrl_ms = replay_ms(graph, args.steps)
     # the dominant kernel's average launch duration: one event pair around the
     # queued-ahead launches of one step, divided by the number of launches
     seq_ms = None
@@ -459,6 +483,14 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
         ceiling = read_ceiling_gbs(step.weight_bytes)
         config["stream_read_ceiling_GBs"] = round(ceiling, 1)
         config["frac_of_stream_read_ceiling"] = round(value / ceiling, 4)
+    # identical-control repeats of the timed step, after the other measurements
+    # of this run (per-launch breakdown, oracle, read ceiling) ran in between;
+    # a spread above 2% flags the run as unstable
+    controls = [ms_per_step, ctrl_ms, replay_ms(graph, args.steps)]
+    spread = 100.0 * (max(controls) - min(controls)) / min(controls)
+    config["control_ms_per_step"] = [round(c, 5) for c in controls]
+    config["control_spread_pct"] = round(spread, 2)
+    config["control_spread_over_2pct"] = bool(spread > 2.0)
     metric = ("Q8_0 matmul weight GB/s (%HBM peak) at M=1" if m == 1 else f"Q8_0 matmul weight GB/s at M={m}")
     if mode == "sequence":
         kname = "q8k::gemv_sequence_kernel<%d>" % m
