@@ -130,6 +130,44 @@ def test_fused_quantization_bit_identical(m, n, k):
         assert bits_equal(down(y), ref), f"layout {layout}"
 
 
+def _half_integer_activations(m, k, seed):
+    """Rows whose quotients x / d sit on or next to half-integers: per 32-value
+    block a scale d0, the block maximum 127 * d0, and values (j + 0.5) * d0,
+    (j + 0.5 +- 1e-4) * d0 and (j + 0.5 +- 3e-4) * d0 mixed with random ones --
+    the cases where a fast reciprocal could round differently from the
+    correctly rounded quotient."""
+    rng = np.random.default_rng(seed)
+    x = np.empty((m, k), np.float32)
+    offs = np.array([0.0, 1e-4, -1e-4, 3e-4, -3e-4, 2.44140625e-4, -2.44140625e-4], np.float64)
+    for r in range(m):
+        for b in range(k // 32):
+            d0 = float(rng.uniform(1e-3, 4.0))
+            j = rng.integers(-127, 127, size=32)
+            o = offs[rng.integers(0, len(offs), size=32)]
+            v = (j + 0.5 + o) * d0
+            v[rng.random(32) < 0.25] = rng.uniform(-127, 127, size=1) * d0
+            v[rng.integers(0, 32)] = 127.0 * d0 * (1 if rng.random() < 0.5 else -1)
+            x[r, 32 * b:32 * b + 32] = v.astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_fused_quantization_half_integer_quotients(m):
+    """The fused quantization equals the standalone quantizer bitwise where the
+    quotients are exact or near half-integers (ties away from zero)."""
+    n, k = 512, 2048
+    x = _half_integer_activations(m, k, seed=77 + m)
+    _, w = _case(m, n, k, seed=5 * m)
+    _, wp = weights_packed(w)
+    ref = _gemv(quantize(x, q8.Q8_LAYOUT_ACT), m, wp, 1, n, k)
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    ws = q8.workspace(m, n, k)
+    q8.q8_quantize_matmul(up(x), k, m, wp, q8.Q8_LAYOUT_PACKED, n, k, y, n, ws, 0 if ws is None else ws.numel())
+    assert bits_equal(down(y), ref)
+    # and the standalone codes are the oracle's (ties away from zero)
+    assert np.array_equal(down(quantize(x, q8.Q8_LAYOUT_ACT)), ref_quantize(x, q8.Q8_LAYOUT_ACT))
+
+
 def test_ld_y_and_workspace_reuse():
     """Output row stride larger than n; one zeroed workspace reused by calls of
     different shapes and m leaves its tile counters at zero and gives the same
