@@ -24,7 +24,9 @@ Q8_0 quantize producer at the prefill row counts, hidden 2048), ``kv`` (a
 decode step's attention over a Q8 KV cache: 16 layers, 16 sequences x 4096
 positions), ``copy`` (a device copy of 1 GiB, used to calibrate rocprofv3's
 byte counters), ``read`` (the streaming-read ceiling, q8_stream_read over
-1 GiB and over the decode step's, the LM head's and single matrices' sizes).
+1 GiB and over the decode step's, the LM head's and single matrices' sizes),
+``quantize`` (weight quantization and repack of the LM head matrix, activation
+quantization of 2048 prefill rows).
 
 The JSON line carries the metric, the roofline of the dominant kernel (its
 average launch duration measured with HIP events on the stream it runs on),
@@ -58,7 +60,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "single", "batched", "prefill", "moe", "norm", "kv", "copy", "read"])
+                    choices=["decode", "single", "batched", "prefill", "moe", "norm", "kv", "copy", "read",
+                             "quantize"])
     ap.add_argument("--m", type=int, default=1, help="rows per GEMV for --workload batched")
     ap.add_argument("--unfused", action="store_true", help="decode: separate quantize and GEMV launches")
     ap.add_argument("--per-matrix", action="store_true",
@@ -937,6 +940,79 @@ def bench_kv(args):
 
 # --------------------------------------------------------------------------
 
+def bench_quantize(args):
+    """The preparation rows on their own: weight quantization (q8_quantize_rows
+    to the row-contiguous layout) and repack (q8_repack_weights) of the LM head
+    matrix 128256x2048 (1.05 GB of fp32 in), and activation quantization (the
+    ACT layout) of 2048 prefill rows of 2048.  Checked against the oracle on
+    the first and last 64 rows before timing."""
+    import torch
+
+    import oracle
+    import workloads as wl
+    from decode_q8_amd import q8
+    dev = torch.device("cuda", 0)
+    n, k = wl.LLAMA_VOCAB, wl.LLAMA_HIDDEN
+    w = wl.weight(wl.DECODE, 0, n, k, group=wl.LLAMA_LAYERS)  # the decode step's LM head weights
+    wt = torch.from_numpy(w).to(dev)
+    qb = q8.q8_quantized_bytes(n, k)
+    wr = torch.empty(qb, dtype=torch.uint8, device=dev)
+    wp = torch.empty(qb, dtype=torch.uint8, device=dev)
+    xm = 2048
+    x = wl.activation(wl.PREFILL, xm, xm, k, outliers=True)
+    xt = torch.from_numpy(x).to(dev)
+    xq = torch.empty(q8.q8_quantized_bytes(xm, k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    run_q = lambda s: q8.q8_quantize_rows(wt, k, n, k, q8.Q8_LAYOUT_ROWS, wr, s.cuda_stream)
+    run_r = lambda s: q8.q8_repack_weights(wr, n, k, wp, s.cuda_stream)
+    run_a = lambda s: q8.q8_quantize_rows(xt, k, xm, k, q8.Q8_LAYOUT_ACT, xq, s.cuda_stream)
+    for f in (run_q, run_r, run_a):
+        with torch.cuda.stream(stream):
+            f(stream)
+    torch.cuda.synchronize()
+    row_b = (k // 32) * 34
+    wr_h = wr.cpu().numpy()
+    for r0 in (0, n - 64):
+        ref = oracle.quantize_rows(w[r0:r0 + 64], oracle.LAYOUT_ROWS)
+        if not np.array_equal(wr_h[r0 * row_b:(r0 + 64) * row_b], ref):
+            raise RuntimeError(f"weight quantization differs from the oracle at rows {r0}..{r0 + 63}")
+        if not np.array_equal(wp[r0 * row_b:(r0 + 64) * row_b].cpu().numpy(), oracle.pack(ref, 64, k)):
+            raise RuntimeError(f"repacked tile at rows {r0}..{r0 + 63} differs from the oracle's packing")
+    if not np.array_equal(xq.cpu().numpy(), oracle.quantize_rows(x, oracle.LAYOUT_ACT)):
+        raise RuntimeError("activation quantization differs from the oracle")
+
+    ms_q, _ = graph_time(run_q, stream, args.steps, args.warmup)
+    spread = dict(STEP_SPREAD)
+    ms_r, _ = graph_time(run_r, stream, args.steps, args.warmup)
+    ms_a, _ = graph_time(run_a, stream, args.steps, args.warmup)
+    STEP_SPREAD.clear()
+    STEP_SPREAD.update(spread)
+    bytes_q = 4 * n * k + qb       # fp32 in, Q8_0 out
+    bytes_r = 2 * qb               # Q8_0 in, the same bytes reordered out
+    bytes_a = 4 * xm * k + q8.q8_quantized_bytes(xm, k)
+    value = bytes_q / (ms_q * 1e-3) / 1e9
+    roof = hbm_roofline("q8k::quantize_kernel (row-contiguous weights)", float(bytes_q), ms_q)
+    roof["timing"] = "one event pair around the graph replays of the single launch"
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = 4096
+        sec, reps_c = timed_repeat(lambda: oracle.quantize_rows(w[:rows], oracle.LAYOUT_ROWS))
+        cpu = {"value": round((4 * rows * k + rows * row_b) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"weight quantization of the first {rows} of the {n} rows, {reps_c} runs, {sec:.3f} s each"}
+    config = {"workload": "Q8_0 weight quantization of the LM head matrix 128256x2048 (fp32 in, row-contiguous "
+                          "Q8_0 out), then repack to the packed layout; activation quantization of 2048 prefill "
+                          "rows of 2048",
+              "weight_quantize_GBs": round(value, 1), "weight_quantize_us": round(ms_q * 1e3, 2),
+              "repack_GBs": round(bytes_r / (ms_r * 1e-3) / 1e9, 1), "repack_us": round(ms_r * 1e3, 2),
+              "activation_quantize_GBs": round(bytes_a / (ms_a * 1e-3) / 1e9, 1),
+              "activation_quantize_us": round(ms_a * 1e3, 2),
+              "activation_note": "per graph replay of one short launch, so host replay overhead dominates; the "
+                                 "2048-row activation (16.8 MB) stays in the Infinity Cache between replays (warm)"}
+    return base_record(args, "Q8_0 weight quantization GB/s (fp32 in + Q8_0 out)", value, "GB/s", ms_q, "f32->q8_0",
+                       config, roof, cpu)
+
+
 def bench_copy(args):
     """1 GiB device-to-device copy: known bytes for calibrating byte counters."""
     import torch
@@ -990,7 +1066,7 @@ def main():
         sys.exit(1)
     fn = {"decode": bench_decode, "batched": bench_decode, "single": bench_single, "prefill": bench_prefill,
           "moe": bench_moe, "norm": bench_norm, "kv": bench_kv, "copy": bench_copy,
-          "read": bench_read}[args.workload]
+          "read": bench_read, "quantize": bench_quantize}[args.workload]
     print(json.dumps(fn(args)), flush=True)
 
 
