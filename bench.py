@@ -993,6 +993,8 @@ def bench_quantize(args):
     value = bytes_q / (ms_q * 1e-3) / 1e9
     roof = hbm_roofline("q8k::quantize_kernel (row-contiguous weights)", float(bytes_q), ms_q)
     roof["timing"] = "one event pair around the graph replays of the single launch"
+    roof["traffic"] = profiled_traffic("quantize_repack_lm_head.txt",
+                                       ["decode_q8_amd/csrc/quantize.hip", "decode_q8_amd/csrc/repack.hip"])
     cpu = None
     if not args.no_cpu_baseline:
         rows = 4096
@@ -1049,6 +1051,7 @@ def bench_read(args):
     STEP_SPREAD.clear()
     STEP_SPREAD.update(spread)
     roof = hbm_roofline("q8k::stream_read_kernel", float(n), ms_per_step)
+    roof["traffic"] = profiled_traffic("stream_read_ceiling.txt", "decode_q8_amd/csrc/measure.hip")
     return base_record(args, "streaming-read GB/s", value, "GB/s", ms_per_step, "u8",
                        {"workload": "plain streaming read of 1 GiB (each byte once, 16-byte loads)",
                         "bytes_read": n, "other_sizes_GBs": others}, roof, None)
