@@ -178,8 +178,12 @@ struct SeqHooks {
     }
 };
 
+// ONE (at most one group per wave): at most 128 VGPRs, so that two 512-thread
+// workgroups fit on a CU for every m (m >= 4 then spills a few registers,
+// which costs less than halving the workgroups that stream and compute).
 template <int M, bool ONE>
-__global__ __launch_bounds__(SEQ_THREADS) void gemv_sequence_kernel(const SeqArgs a) {
+__global__ __launch_bounds__(SEQ_THREADS) __attribute__((amdgpu_waves_per_eu(ONE ? 4 : 1, 8))) void
+gemv_sequence_kernel(const SeqArgs a) {
     extern __shared__ float lds_u[];  // [groups of a unit][M][64]
     __shared__ int last_wg;
     const int wg = blockIdx.x, nwg = a.nwg;
