@@ -213,13 +213,17 @@ int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m,
  * producer emitting the next matmul's int8 input).  The pages name the fusion
  * but not the norm; this is Llama's RMSNorm, per row:
  *   h_j = fp32(residual_in_j + x_j)   (h_j = x_j when residual_in is NULL)
- *   ss  = sum_j (double)h_j^2 in a fixed order: partial p_t (t = 0..511)
- *         sums the j with floor(j / 4) == t mod 512 in increasing j, then
- *         p_t += p_{t+s} for t < s, s = 256, 128, ..., 1; ss = p_0
+ *   ss  = sum_j (double)h_j^2 (each square exact in fp64), the exact sum
+ *         rounded to fp64; the library sums the squares in fp64 in one fixed
+ *         order (512 partials over 4-value chunks, then a halving tree),
+ *         which is within k * 2^-52 (relative) of that exactly rounded sum
+ *   r   = fp32(1 / sqrt(ss / k + eps)), each fp64 operation correctly rounded
  *   r   = fp32(1 / sqrt(ss / k + eps)), each fp64 operation correctly rounded
  *   n_j = fp32(fp32(h_j * r) * weight_j)
  * then n is quantized per 32-value block exactly as q8_quantize_rows does.
- * Codes, scales and h are deterministic (bit-identical for any rows count).
+ * Codes, scales and h are deterministic (bit-identical for any rows count);
+ * they equal the exactly rounded definition's unless 1 / sqrt(ss / k + eps)
+ * lies within that fp64 margin of an fp32 rounding boundary.
  *  x            device fp32 [rows][k] (row stride k), 16-byte aligned.
  *  residual_in  device fp32 [rows][k] or NULL (a norm without residual add).
  *  residual_out device fp32 [rows][k] receiving h, or NULL; may be the same
@@ -290,10 +294,15 @@ int q8_grouped_matmul(const void *x_q, int64_t x_rows, int x_per_pair, const int
  *  weights  device fp32 [tokens][topk]: with m the largest logit and
  *           e_i = exp((double)l_i - m):
  *             normalize != 0: w_j = fp32(e_j / D), D = sum of the selected
- *               e in slot order (softmax over the selected experts);
- *             normalize == 0: D = sum over all experts, as 64 partials (experts
- *               l, l + 64, ... ascending, l = 0..63) folded P_l += P_{l+s},
- *               s = 32..1 (softmax over all experts, selected ones kept).
+ *               e (softmax over the selected experts);
+ *             normalize == 0: D = sum over all experts (softmax over all
+ *               experts, selected ones kept).
+ *           D is defined as the exact sum rounded to fp64.  The library adds
+ *           the selected e in slot order, and all experts as 64 partials
+ *           (experts l, l + 64, ... ascending) folded P_l += P_{l+s},
+ *           s = 32..1: within a few fp64 ulps of the exact sum, so w_j equals
+ *           the definition's unless e_j / D lies that close to an fp32
+ *           rounding boundary.
  *  1 <= topk <= min(n_experts, 32), n_experts <= 1024, tokens >= 0.
  *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int topk, int normalize, int32_t *ids,
@@ -341,10 +350,12 @@ int q8_moe_combine(const float *y, int64_t ld_y, const float *weights, int64_t t
  *  positions  device int32 [tokens], each in [0, max_pos).
  *  cos_tab, sin_tab  device fp32 [max_pos][head_dim / 2] (model constants).
  *  q_gain, k_gain    device fp32 [head_dim] or NULL: per-head RMSNorm of the
- *             query / key heads before the rotation (ss = sum of x^2 in fp64
- *             as head_dim/4 partials of 4 consecutive values, folded
- *             p_c += p_{c+s} for s = head_dim/8 .. 1; r = fp32(1 / sqrt(ss /
- *             head_dim + eps)); x = fp32(fp32(x * r) * gain)).
+ *             query / key heads before the rotation (ss = sum of the exact
+ *             fp64 squares x^2 rounded to fp64 -- the library adds them as
+ *             head_dim/4 partials of 4 consecutive values folded
+ *             p_c += p_{c+s} for s = head_dim/8 .. 1, within a few fp64 ulps
+ *             of that; r = fp32(1 / sqrt(ss / head_dim + eps));
+ *             x = fp32(fp32(x * r) * gain)).
  *  rotation   half-split: for i < head_dim/2 with c, s = tables[pos][i]:
  *             x_i <- fp32(fp32(x_i c) - fp32(x_{i+h} s)),
  *             x_{i+h} <- fp32(fp32(x_{i+h} c) + fp32(x_i s)),  h = head_dim/2.

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.q8ref_matmul_points.argtypes = [P, I64, P, I64, I64, P, P, I64, P, P]
         L.q8ref_grouped_matmul.argtypes = [P, I64, I, P, I64, I, P, I64, I64, I64, I64, P, P, I]
         L.q8ref_rmsnorm_quantize.argtypes = [P, P, P, I64, I64, ctypes.c_float, P, P]
+        L.q8ref_exact_sum.argtypes = [P, I64]
+        L.q8ref_exact_sum.restype = ctypes.c_double
         L.q8ref_exp_nonpos.argtypes = [ctypes.c_double]
         L.q8ref_exp_nonpos.restype = ctypes.c_double
         L.q8ref_moe_route.argtypes = [P, I64, I64, I, I, P, P]
@@ -146,6 +148,12 @@ def rmsnorm_quantize(x: np.ndarray, res_in: np.ndarray, w: np.ndarray, eps: floa
                                         _p(res_out), _p(q)),
            "rmsnorm_quantize")
     return res_out, q
+
+
+def exact_sum(v) -> float:
+    """Sum of non-negative finite doubles rounded once to fp64 (q8ref_exact_sum)."""
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    return float(lib().q8ref_exact_sum(_p(a), a.size))
 
 
 def exp_nonpos(x: float) -> float:

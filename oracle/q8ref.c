@@ -133,6 +133,77 @@ int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* exactly rounded fp64 sum of non-negative terms                            */
+/* ------------------------------------------------------------------------ */
+
+/* Bit p of the accumulator stands for 2^(p - 1074), the fp64 subnormal unit;
+ * the largest finite fp64 has its top bit at p = 2097, and 34 limbs of 64 bits
+ * (2176 positions) leave 78 bits of headroom for carries. */
+#define XS_LIMBS 34
+#define XS_BIAS 1074
+
+static void xs_add_bits(uint64_t *acc, uint64_t v, int pos) {
+    /* acc += v * 2^pos (v < 2^53), carrying upwards */
+    int li = pos / 64, sh = pos % 64;
+    uint64_t lo = v << sh;
+    uint64_t hi = sh ? (v >> (64 - sh)) : 0;
+    uint64_t old = acc[li];
+    acc[li] = old + lo;
+    uint64_t carry = (acc[li] < old) ? 1 : 0;
+    for (int i = li + 1; i < XS_LIMBS && (hi || carry); i++) {
+        old = acc[i];
+        uint64_t add = hi + carry; /* hi < 2^53, no wrap */
+        acc[i] = old + add;
+        carry = (acc[i] < old) ? 1 : 0;
+        hi = 0;
+    }
+}
+
+static int xs_bit(const uint64_t *acc, int p) { return (int)((acc[p / 64] >> (p % 64)) & 1u); }
+
+double q8ref_exact_sum(const double *v, int64_t n) {
+    uint64_t acc[XS_LIMBS];
+    memset(acc, 0, sizeof(acc));
+    for (int64_t i = 0; i < n; i++) {
+        const double x = v[i];
+        if (!(x >= 0.0) || x > 1.7976931348623157e308) return NAN; /* outside the contract */
+        uint64_t u;
+        memcpy(&u, &x, 8);
+        const int eb = (int)((u >> 52) & 0x7ffu);
+        uint64_t mant = u & 0xfffffffffffffull;
+        int pos; /* bit position of mant's least significant bit */
+        if (eb == 0) {
+            pos = 0; /* subnormal (or zero): mant * 2^-1074 */
+        } else {
+            mant |= 1ull << 52;
+            pos = eb - 1; /* value = mant * 2^(eb - 1075) = mant * 2^(pos - 1074) */
+        }
+        if (mant) xs_add_bits(acc, mant, pos);
+    }
+    int top = -1;
+    for (int p = XS_LIMBS * 64 - 1; p >= 0; p--)
+        if (xs_bit(acc, p)) {
+            top = p;
+            break;
+        }
+    if (top < 0) return 0.0;
+    if (top < 53) { /* at most 53 bits: exactly representable */
+        uint64_t m = 0;
+        for (int p = top; p >= 0; p--) m = (m << 1) | (uint64_t)xs_bit(acc, p);
+        return ldexp((double)m, -XS_BIAS);
+    }
+    /* keep the top 53 bits, round to nearest with ties to even */
+    uint64_t m = 0;
+    for (int p = top; p > top - 53; p--) m = (m << 1) | (uint64_t)xs_bit(acc, p);
+    const int lsb = top - 52;
+    const int round = xs_bit(acc, lsb - 1);
+    int sticky = 0;
+    for (int p = lsb - 2; p >= 0 && !sticky; p--) sticky = xs_bit(acc, p);
+    if (round && (sticky || (m & 1u))) m += 1; /* 2^53 after the carry is still exact */
+    return ldexp((double)m, lsb - XS_BIAS);
+}
+
+/* ------------------------------------------------------------------------ */
 /* fused residual + RMSNorm + quantization ("ferro" README, item 3)          */
 /* ------------------------------------------------------------------------ */
 
@@ -143,23 +214,19 @@ int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, 
     int64_t nb = k / QK;
     float *h = malloc(sizeof(float) * (size_t)k);
     float *n = malloc(sizeof(float) * (size_t)k);
-    if (!h || !n) {
+    double *sq = malloc(sizeof(double) * (size_t)k);
+    if (!h || !n || !sq) {
         free(h);
         free(n);
+        free(sq);
         return Q8REF_EARG;
     }
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t j = 0; j < k; j++) h[j] = res_in ? res_in[r * k + j] + x[r * k + j] : x[r * k + j];
-        /* the defined fp64 summation order: 512 partials over 4-value chunks, then the halving tree */
-        double p[512];
-        for (int t = 0; t < 512; t++) {
-            p[t] = 0.0;
-            for (int64_t j0 = 4 * (int64_t)t; j0 < k; j0 += 2048)
-                for (int c = 0; c < 4; c++) p[t] += (double)h[j0 + c] * (double)h[j0 + c];
-        }
-        for (int stride = 256; stride >= 1; stride /= 2)
-            for (int t = 0; t < stride; t++) p[t] += p[t + stride];
-        const double mean = p[0] / (double)k;
+        /* ss: the exactly rounded sum of the squares (each square of an fp32 is exact in fp64) */
+        for (int64_t j = 0; j < k; j++) sq[j] = (double)h[j] * (double)h[j];
+        const double ss = q8ref_exact_sum(sq, k);
+        const double mean = ss / (double)k;
         const float rs = (float)(1.0 / sqrt(mean + (double)eps));
         for (int64_t j = 0; j < k; j++) {
             const float hr = h[j] * rs;
@@ -176,6 +243,7 @@ int q8ref_rmsnorm_quantize(const float *x, const float *res_in, const float *w, 
     }
     free(h);
     free(n);
+    free(sq);
     return Q8REF_OK;
 }
 
@@ -384,7 +452,12 @@ int q8ref_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int 
     if (!logits || !ids || !weights || tokens < 0 || n_experts <= 0 || topk < 1 || topk > n_experts)
         return Q8REF_EARG;
     char *taken = malloc((size_t)n_experts);
-    if (!taken) return Q8REF_EARG;
+    double *e = malloc(sizeof(double) * (size_t)n_experts);
+    if (!taken || !e) {
+        free(taken);
+        free(e);
+        return Q8REF_EARG;
+    }
     for (int64_t t = 0; t < tokens; t++) {
         const float *l = logits + t * n_experts;
         memset(taken, 0, (size_t)n_experts);
@@ -397,23 +470,19 @@ int q8ref_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int 
             ids[t * topk + j] = (int32_t)best;
         }
         const double m = (double)l[ids[t * topk]];
-        double D = 0.0;
+        /* D: the exactly rounded sum of the e's (selected experts, or all of them) */
+        int64_t ne = 0;
         if (normalize) {
-            for (int j = 0; j < topk; j++) D += q8ref_exp_nonpos((double)l[ids[t * topk + j]] - m);
+            for (int j = 0; j < topk; j++) e[ne++] = q8ref_exp_nonpos((double)l[ids[t * topk + j]] - m);
         } else {
-            double P[64];
-            for (int i = 0; i < 64; i++) {
-                P[i] = 0.0;
-                for (int64_t e = i; e < n_experts; e += 64) P[i] += q8ref_exp_nonpos((double)l[e] - m);
-            }
-            for (int s = 32; s >= 1; s /= 2)
-                for (int i = 0; i < s; i++) P[i] += P[i + s];
-            D = P[0];
+            for (int64_t x = 0; x < n_experts; x++) e[ne++] = q8ref_exp_nonpos((double)l[x] - m);
         }
+        const double D = q8ref_exact_sum(e, ne);
         for (int j = 0; j < topk; j++)
             weights[t * topk + j] = (float)(q8ref_exp_nonpos((double)l[ids[t * topk + j]] - m) / D);
     }
     free(taken);
+    free(e);
     return Q8REF_OK;
 }
 
@@ -475,15 +544,10 @@ static float kv_quantize_block(const float *x, int8_t *q) {
 }
 
 static void head_norm(float *x, int hd, const float *g, float eps) {
-    double p[64];
-    const int nc = hd / 4;
-    for (int c = 0; c < nc; c++) {
-        p[c] = 0.0;
-        for (int i = 0; i < 4; i++) p[c] += (double)x[4 * c + i] * (double)x[4 * c + i];
-    }
-    for (int st = nc / 2; st >= 1; st /= 2)
-        for (int c = 0; c < st; c++) p[c] += p[c + st];
-    const float r = (float)(1.0 / sqrt(p[0] / (double)hd + (double)eps));
+    double sq[256];
+    for (int i = 0; i < hd; i++) sq[i] = (double)x[i] * (double)x[i];
+    const double ss = q8ref_exact_sum(sq, hd); /* exactly rounded sum of the exact squares */
+    const float r = (float)(1.0 / sqrt(ss / (double)hd + (double)eps));
     for (int i = 0; i < hd; i++) {
         const float xr = x[i] * r;
         x[i] = xr * g[i];
@@ -584,7 +648,7 @@ int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, 
                     const double vv = (double)v_cache[row * hd + d] * (double)v_scale[row * nb + d / QK];
                     o += sc[j] * vv;
                     ob += sc[j] * fabs(vv) *
-                          ((double)scale * Sj[j] * 2.0 * (hd + 2) * u + (96.0 + (double)L / 256.0) * u);
+                          ((double)scale * Sj[j] * 2.0 * (hd + 2) * u + ((double)L + 8.0) * u);
                 }
                 const double r = o / l;
                 out[(sq * n_heads + h) * hd + d] = (float)r;

@@ -65,6 +65,13 @@ void q8ref_f16_to_f32_n(const uint16_t *in, float *out, int64_t n);
  * (if d_out) the fp32 scale d used for the division. */
 uint16_t q8ref_quantize_block(const float *x, int8_t *q, float *d_out);
 
+/* The sum of n non-negative finite doubles, rounded once to fp64 (to nearest,
+ * ties to even).  Every term is added exactly into a fixed-point integer that
+ * holds every fp64 bit position, and that integer is rounded at the end, so
+ * the result does not depend on the order of the terms.  A negative,
+ * infinite or NaN term returns NaN. */
+double q8ref_exact_sum(const double *v, int64_t n);
+
 /* rows x k fp32 (row stride ld_x elements) -> layout 0 (ROWS) or 2 (ACT). */
 int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, int layout, uint8_t *out);
 
@@ -76,12 +83,9 @@ int q8ref_quantize_rows(const float *x, int64_t ld_x, int64_t rows, int64_t k, i
  *   h_j   = fp32(res_in_j + x_j), or x_j when res_in is NULL (a norm with
  *           no residual add, as before a model's first layer); written to
  *           res_out unless res_out is NULL
- *   ss    = sum_j (double)h_j^2 in a fixed order: partial p_t = sum of the
- *           j whose 4-value chunk index floor(j / 4) is t mod 512, in
- *           increasing j, for t = 0..511; then for stride 256, 128, ..., 1:
- *           p_t += p_{t+stride} for t < stride; ss = p_0 (every h_j^2 is
- *           exact in fp64; the order only fixes the fp64 roundings of the
- *           sum)
+ *   ss    = sum_j (double)h_j^2, rounded once to fp64 (every square of an
+ *           fp32 is exact in fp64; the sum is q8ref_exact_sum's, so no
+ *           summation order enters the definition)
  *   r     = fp32(1.0 / sqrt(ss / k + eps)), all in correctly rounded fp64
  *   n_j   = fp32(fp32(h_j * r) * w_j)
  * and n is quantized per 32-value block as q8ref_quantize_block does, into
@@ -141,10 +145,9 @@ double q8ref_exp_nonpos(double x);
 /* Router: logits fp32 [tokens][n_experts] -> ids int32 [tokens][topk] and
  * weights fp32 [tokens][topk].  With m = the largest logit of the token and
  * e_i = q8ref_exp_nonpos((double)l_i - (double)m):
- *   normalize = 1: D = sum of e over the selected experts in slot order
- *   normalize = 0: D = sum of e over all experts in a fixed order: partial
- *                  P_l = sum of e_i over i = l, l + 64, ... ascending, for
- *                  l = 0..63, then P_l += P_{l+s} for l < s, s = 32..1
+ *   normalize = 1: D = sum of e over the selected experts
+ *   normalize = 0: D = sum of e over all experts
+ * each sum rounded once to fp64 (q8ref_exact_sum: no summation order enters)
  *   w_j = fp32(e_{id_j} / D).
  * Returns Q8REF_OK or Q8REF_EARG (sizes, topk outside 1..n_experts). */
 int q8ref_moe_route(const float *logits, int64_t tokens, int64_t n_experts, int topk, int normalize, int32_t *ids,
@@ -171,9 +174,9 @@ int q8ref_moe_combine(const float *y, int64_t ld_y, const float *w, int64_t toke
  *  - qkv rows hold n_heads query heads, then n_kv key heads, then n_kv value
  *    heads, each head_dim values (one fused QKV projection per token);
  *  - optional per-head RMSNorm of q and k (gains of head_dim values, NULL for
- *    none): ss = sum of x^2 in fp64 as head_dim/4 partials of 4 consecutive
- *    values (in order), folded p_c += p_{c+s} for s = head_dim/8, ..., 1;
- *    r = fp32(1 / sqrt(ss / head_dim + eps)); n = fp32(fp32(x * r) * g);
+ *    none): ss = sum of the exact fp64 squares x^2 rounded once to fp64
+ *    (q8ref_exact_sum); r = fp32(1 / sqrt(ss / head_dim + eps));
+ *    n = fp32(fp32(x * r) * g);
  *  - rotary embedding of q and k (after the norm) in the half-split layout:
  *    for i < head_dim/2, with c = cos_tab[pos][i], s = sin_tab[pos][i]:
  *      y_i        = fp32(fp32(x_i * c) - fp32(x_{i+h} * s))
@@ -198,12 +201,14 @@ int q8ref_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_kv, int 
  *   v = q * d (exact in fp64):
  *   s_j = scale * sum_d q_d k_jd;  p_j = exp(s_j - max);  out = sum p_j v_j / sum p_j
  * all in fp64, out rounded once to fp32.  bound (may be NULL) receives, per
- * output, an fp64 error budget for an fp32 evaluation whose dot products are
- * sums of head_dim + 2 rounded terms, whose softmax sums and weighted sums run
- * over at most 96 rounded steps inside a chunk of 256 keys plus one step per
- * chunk (an error common to every p_j, such as that of the maximum, cancels
- * in the normalization):
- *   (sum_j p_j |v_jd| * (scale * S_j * 2 (head_dim + 2) u + (96 + len/256) u))
+ * output, an fp64 error budget for any fp32 evaluation, whatever its
+ * summation order: each dot product is a sum of head_dim + 2 rounded terms,
+ * each softmax sum and weighted sum a sum of len terms in any order (at most
+ * len - 1 roundings, Higham's bound for recursive summation in any order),
+ * plus a few roundings for the exponential, the maximum and the division (an
+ * error common to every p_j, such as that of the maximum, cancels in the
+ * normalization):
+ *   (sum_j p_j |v_jd| * (scale * S_j * 2 (head_dim + 2) u + (len + 8) u))
  *   / sum_j p_j + 2 u |out|,  S_j = sum_d |q_d k_jd|,  u = 2^-24. */
 int q8ref_attention_decode(const float *q, int64_t seqs, int n_heads, int n_kv, int head_dim, const int8_t *k_cache,
                            const float *k_scale, const int8_t *v_cache, const float *v_scale, int64_t n_slots,
