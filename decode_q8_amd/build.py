@@ -25,13 +25,31 @@ LIB = os.path.join(HERE, "libq8.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["quantize.hip", "repack.hip", "gemv.hip", "gemv_seq.hip", "gemm.hip", "norm.hip", "moe.hip", "kv.hip", "measure.hip"]
-HOST_SOURCES = ["api.cpp"]
+HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+
+
+def source_digest() -> str:
+    """sha256 over every file the library is built from (the kernel and host
+    sources, their headers, include/q8.h) and the compile flags, without
+    absolute paths, so the same tree gives the same digest on any machine.
+    build() compiles it into the library (q8_build_digest), and the binding
+    refuses a library whose digest differs from the tree's."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".cpp", ".h")))
+    for name in files:
+        h.update(name.encode() + b"\0")
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    h.update(b"include/q8.h\0")
+    h.update(open(os.path.join(ROOT, "include", "q8.h"), "rb").read())
+    h.update(" ".join(a for a in COMMON + DEVICE if not os.path.isabs(a) and a != "-I").encode())
+    return h.hexdigest()
 
 
 def hipcc() -> str:
@@ -54,6 +72,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link libq8.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
+    digest = source_digest()
     cmds, objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
@@ -62,8 +81,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         rocm_inc = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(cc))), "include")
-        cmds.append([cc, *COMMON, "-D__HIP_PLATFORM_AMD__", "-I", rocm_inc, "-x", "c++", "-c",
-                     os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMMON, "-D__HIP_PLATFORM_AMD__", f'-DQ8_BUILD_DIGEST="{digest}"', "-I", rocm_inc,
+                     "-x", "c++", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         logs = list(ex.map(_run, cmds))

@@ -13,10 +13,19 @@
 #include "../../include/q8.h"
 #include "launch.hpp"
 
+#ifndef Q8_BUILD_DIGEST
+#define Q8_BUILD_DIGEST "unknown"
+#endif
+
 static_assert(Q8_SEQUENCE_MAX_STEPS == q8k::SEQ_MAX_STEPS, "sequence length limit");
 static_assert(Q8_ROUTE_MAX_EXPERTS == q8k::ROUTE_MAX_EXPERTS && Q8_ROUTE_MAX_TOPK == q8k::ROUTE_MAX_TOPK,
               "router limits");
 static_assert(Q8_ATTENTION_MAX_LEN == q8k::ATT_MAX_LEN, "attention context limit");
+
+namespace q8k {
+static std::atomic<uint32_t> g_device_queries{0};
+void note_device_query() { g_device_queries.fetch_add(1, std::memory_order_relaxed); }
+}  // namespace q8k
 
 namespace {
 
@@ -41,6 +50,7 @@ int check_device() {
         if (known == -1) return Q8_ERR_DEVICE;
     }
     hipDeviceProp_t prop;
+    q8k::note_device_query();
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return Q8_ERR_DEVICE;
     const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
@@ -54,6 +64,10 @@ int launched(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH; }
 extern "C" {
 
 uint32_t q8_abi_version(void) { return Q8_ABI_VERSION; }
+
+const char *q8_build_digest(void) { return Q8_BUILD_DIGEST; }
+
+uint32_t q8_device_queries(void) { return q8k::g_device_queries.load(std::memory_order_relaxed); }
 
 const char *q8_status_str(int status) {
     switch (status) {
@@ -170,6 +184,19 @@ int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m,
     const size_t need = q8k::gemv_sequence_workspace_bytes(hs, count, m);
     if (!workspace || workspace_bytes < need) return Q8_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q8_ERR_ALIGN;
+    // every x must be ready before the call: no y may overlap any x (the
+    // chaining y_i == x_(i+1) included), the y's must be disjoint, and the
+    // workspace must overlap neither
+    for (int i = 0; i < count; i++) {
+        const size_t yb = (size_t)((m - 1) * hs[i].ld_y + hs[i].n) * 4;
+        if (overlap(workspace, need, hs[i].y, yb)) return Q8_ERR_ARG;
+        if (overlap(workspace, need, hs[i].x, (size_t)((m - 1) * hs[i].ld_x + hs[i].k) * 4)) return Q8_ERR_ARG;
+        for (int j = 0; j < count; j++) {
+            if (overlap(hs[i].y, yb, hs[j].x, (size_t)((m - 1) * hs[j].ld_x + hs[j].k) * 4)) return Q8_ERR_ARG;
+            if (j != i && overlap(hs[i].y, yb, hs[j].y, (size_t)((m - 1) * hs[j].ld_y + hs[j].n) * 4))
+                return Q8_ERR_ARG;
+        }
+    }
     const int dev = check_device();
     if (dev != Q8_OK) return dev;
     return launched(q8k::launch_gemv_sequence(hs, count, m, workspace, stream));

@@ -4,17 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "layout.hpp"
+
 namespace q8k {
 
-constexpr int QK = 32;            // values per block
-constexpr int BLOCK_BYTES = 34;   // fp16 scale + 32 int8
-constexpr int TILE_ROWS = 64;     // rows per packed record = lanes per wave
-constexpr int GROUP_BLOCKS = 8;   // blocks per packed record and per summation group
-constexpr int GROUP_K = GROUP_BLOCKS * QK;              // 256 values
-constexpr int RECORD_BYTES = TILE_ROWS * GROUP_BLOCKS * BLOCK_BYTES;  // 17408
-constexpr int RECORD_Q_BYTES = TILE_ROWS * GROUP_K;     // 16384
-constexpr int ROW_GROUP_BYTES = GROUP_BLOCKS * BLOCK_BYTES;           // 272
-constexpr int SEG_GROUPS = 8;     // groups per summation segment (2048 values)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

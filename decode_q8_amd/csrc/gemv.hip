@@ -42,44 +42,6 @@ __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, i
                                    (int)gridDim.x, segs_per_wg, ctr, part, lds_u, &last_wg, false, NoWait());
 }
 
-constexpr int GEMV_MAX_WAVES = 8;
-constexpr int64_t GEMV_LDS_LIMIT = 64 * 1024;
-
-// Execution plan of a GEMV.  Only speed depends on it; every plan produces
-// the same bits.  Up to 8 waves per workgroup (one or more groups each);
-// tiles of narrow matrices are spread over one workgroup per segment so that
-// at least ~256 workgroups run; the group sums a workgroup keeps in LDS must
-// fit in 64 KB.
-GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k) {
-    GemvPlan p;
-    p.tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
-    p.groups = k / GROUP_K;
-    const int64_t S = (p.groups + SEG_GROUPS - 1) / SEG_GROUPS;
-    int64_t wgs = 1;
-    if (p.tiles < 256) wgs = (256 + p.tiles - 1) / p.tiles;
-    if (wgs > S) wgs = S;
-    for (;;) {  // LDS bound: groups per workgroup x m x 64 rows x 4 bytes
-        const int64_t sp = (S + wgs - 1) / wgs;
-        const int64_t gpw = sp * SEG_GROUPS < p.groups ? sp * SEG_GROUPS : p.groups;
-        if (gpw * m * TILE_ROWS * (int64_t)sizeof(float) <= GEMV_LDS_LIMIT || wgs >= S) break;
-        wgs++;
-    }
-    const int64_t sp = (S + wgs - 1) / wgs;
-    wgs = (S + sp - 1) / sp;  // no workgroup without a segment
-    const int64_t gpw = sp * SEG_GROUPS < p.groups ? sp * SEG_GROUPS : p.groups;
-    p.wgs_per_tile = (int)wgs;
-    p.segs_per_wg = (int)sp;
-    // one chain thread per (row, activation row) after the barrier: at least m waves
-    int64_t waves = gpw < GEMV_MAX_WAVES ? gpw : GEMV_MAX_WAVES;
-    if (waves < m) waves = m;
-    p.waves = (int)waves;
-    p.lds = (size_t)(gpw * m * TILE_ROWS) * sizeof(float);
-    p.workspace = 0;
-    if (wgs > 1) p.workspace = (size_t)((p.tiles * 4 + 255) / 256 * 256) + (size_t)(S * m * n) * sizeof(float);
-    return p;
-}
-
-size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k) { return gemv_plan(m, n, k).workspace; }
 
 template <int LAYOUT, typename ACT>
 static void launch_gemv_m(int64_t m, const GemvPlan &p, hipStream_t s, const ACT *x, int64_t ld_x,
@@ -307,10 +269,6 @@ __global__ __launch_bounds__(256) void grouped_gemv_kernel(const int8_t *__restr
             default: expert_pass<8>(xq, xs, k, x_per_pair, topk, pl, wbase, G, row, n, y); break;
         }
     }
-}
-
-size_t grouped_workspace_bytes(int64_t tokens, int topk, int64_t n_experts) {
-    return (size_t)(16 + 2 * n_experts + 1 + tokens * topk) * sizeof(int32_t);
 }
 
 hipError_t launch_grouped(const void *x_q, int64_t x_rows, int x_per_pair, const int32_t *ids, int64_t tokens,

@@ -30,8 +30,10 @@
 // counter itself with read-modify-writes made the step 2x slower).  The poll
 // is bounded: a wait that does not end within the limit (only possible if the
 // grid did not fit on the GPU) records Q8_ERR_LAUNCH in the workspace status
-// word and proceeds -- outputs do not depend on the waits, since every input
-// is ready before the launch.  The unit that completes the last step returns
+// word and proceeds, so the launch always ends.  The call's outputs are then
+// undefined (a successor may chain handed-over segment sums that are not all
+// written yet) and a late unit may leave a flag raised, so the caller must
+// zero the workspace again.  The unit that completes the last step returns
 // every flag to zero; by then no workgroup is waiting any more, since each
 // wait precedes a unit that the last step transitively depends on.
 //
@@ -44,21 +46,21 @@
 // Every output is still the same chain of the same segment sums, so it stays
 // bit-identical to its own launch; the step's outputs are complete when its
 // successor is.
+#include <atomic>
+
 #include "device.hpp"
 #include "gemv_core.hpp"
 #include "launch.hpp"
 
 namespace q8k {
 
-constexpr int SEQ_THREADS = 512;
 constexpr uint32_t SEQ_SPIN_LIMIT = 1u << 18;  // polls of roughly 1 us each
-constexpr int FLAG_LINES = 8;
-constexpr int FLAG_LINE_BYTES = 4096;  // one int32 flag per step in each line
-constexpr int SEQ_NSUB = 16;           // sub-counters of a step with many units
 constexpr int SEQ_SUB_MIN_UNITS = 64;  // more units than this: two-level counting
-constexpr int CTR_LINE = 128;          // bytes per counter
 constexpr uint32_t SEQ_PACE_TICKS = 150;  // prefetch stagger per wave, in 10 ns ticks of s_memrealtime
-constexpr int CTR_PER_STEP = SEQ_NSUB + 1;
+constexpr int FLAG_LINES = SEQ_FLAG_LINES;
+constexpr int FLAG_LINE_BYTES = SEQ_FLAG_LINE_BYTES;
+constexpr int CTR_LINE = SEQ_CTR_LINE;
+constexpr int CTR_PER_STEP = SEQ_CTR_PER_STEP;
 static_assert(SEQ_MAX_STEPS * 4 <= FLAG_LINE_BYTES, "a flag line holds every step's flag");
 static_assert((SEQ_NSUB & (SEQ_NSUB - 1)) == 0 && SEQ_NSUB <= SEQ_SUB_MIN_UNITS, "every sub-counter has units");
 
@@ -73,10 +75,7 @@ struct SeqStep {
 };
 static_assert(sizeof(SeqStep) == 48, "kernel-argument layout");
 
-// Workspace: [0, 4) status word; from byte 256 CTR_PER_STEP counters of
-// CTR_LINE bytes per step (the step's counter, then its sub-counters);
-// FLAG_LINES flag lines from flag_off (4 KB aligned); then the split steps'
-// tile counters and segment sums.
+// Workspace layout: see SeqPlan (plan.cpp).
 struct SeqArgs {
     uint8_t *ws;
     int32_t count, nwg;
@@ -241,21 +240,15 @@ struct SeqLayout {
 };
 
 static bool seq_layout(const SeqHostStep *steps, int count, int64_t m, SeqLayout &L) {
-    L.one = true;
-    L.lds = 0;
-    // status line + the counters, then the flag lines (4 KB aligned)
-    const size_t ctr_end = 256 + (size_t)CTR_LINE * CTR_PER_STEP * count;
-    const size_t flag_off = (ctr_end + FLAG_LINE_BYTES - 1) / FLAG_LINE_BYTES * FLAG_LINE_BYTES;
-    size_t off = flag_off + (size_t)FLAG_LINES * FLAG_LINE_BYTES;
+    SeqPlan P;
+    seq_plan(steps, count, m, P);
+    L.one = P.one;
+    L.lds = P.lds;
+    L.workspace = P.workspace;
     L.args.count = count;
-    L.args.flag_off = (int32_t)flag_off;
+    L.args.flag_off = P.flag_off;
     for (int i = 0; i < count; i++) {
         const SeqHostStep &h = steps[i];
-        const GemvPlan p = gemv_plan(m, h.n, h.k);
-        const int64_t gpw = (int64_t)p.segs_per_wg * SEG_GROUPS < p.groups ? (int64_t)p.segs_per_wg * SEG_GROUPS
-                                                                           : p.groups;
-        if (gpw > SEQ_THREADS / 64) L.one = false;
-        if (p.lds > L.lds) L.lds = p.lds;
         SeqStep &s = L.args.step[i];
         s.x = h.x;
         s.w = (const uint8_t *)h.w;
@@ -264,36 +257,49 @@ static bool seq_layout(const SeqHostStep *steps, int count, int64_t m, SeqLayout
         s.ld_y = (int32_t)h.ld_y;
         s.n = (int32_t)h.n;
         s.k = (int32_t)h.k;
-        s.wgs = (uint16_t)p.wgs_per_tile;
-        s.segs = (uint16_t)p.segs_per_wg;
-        s.ws_off = 0;
-        if (p.workspace) {
-            s.ws_off = (uint32_t)(off / 256);
-            off += (p.workspace + 255) / 256 * 256;
-        }
+        s.wgs = P.wgs[i];
+        s.segs = P.segs[i];
+        s.ws_off = P.ws_off[i];
     }
-    L.workspace = off;
     return true;
 }
 
-size_t gemv_sequence_workspace_bytes(const SeqHostStep *steps, int count, int64_t m) {
-    SeqLayout L;
-    seq_layout(steps, count, m, L);
-    return L.workspace;
-}
+// Resident workgroups per CU of each kernel variant, per device and dynamic
+// LDS size (whole KB, at most 64), and the CU count per device: discovered on
+// the first launch that needs them and kept, so later calls on the token path
+// query nothing about the device.
+constexpr int SEQ_MAX_DEVICES = 64;
+constexpr int SEQ_LDS_KB_MAX = 64;
+static std::atomic<int16_t> g_seq_per_cu[SEQ_MAX_DEVICES][8][2][SEQ_LDS_KB_MAX + 1];  // 0: not yet known
+static std::atomic<int32_t> g_seq_cus[SEQ_MAX_DEVICES];
 
 template <int M, bool ONE>
 static hipError_t launch_seq(SeqLayout &L, void *ws, hipStream_t s) {
     // The grid is as many workgroups as the GPU holds at once: the waits need
     // every workgroup resident.
-    int dev = 0, per_cu = 0, cus = 0;
+    int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_sequence_kernel<M, ONE>, SEQ_THREADS, L.lds);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+    const int lds_kb = (int)((L.lds + 1023) / 1024);
+    if (dev < 0 || dev >= SEQ_MAX_DEVICES || lds_kb > SEQ_LDS_KB_MAX) return hipErrorInvalidConfiguration;
+    std::atomic<int16_t> &slot = g_seq_per_cu[dev][M - 1][ONE ? 1 : 0][lds_kb];
+    int per_cu = slot.load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        note_device_query();
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_sequence_kernel<M, ONE>, SEQ_THREADS,
+                                                         (size_t)lds_kb * 1024);
+        if (e != hipSuccess) return e;
+        if (per_cu < 1) return hipErrorInvalidConfiguration;
+        slot.store((int16_t)per_cu, std::memory_order_relaxed);
+    }
+    int cus = g_seq_cus[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        note_device_query();
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (cus < 1) return hipErrorInvalidConfiguration;
+        g_seq_cus[dev].store(cus, std::memory_order_relaxed);
+    }
     L.args.ws = (uint8_t *)ws;
     L.args.nwg = per_cu * cus;
     hipLaunchKernelGGL((gemv_sequence_kernel<M, ONE>), dim3((unsigned)L.args.nwg), dim3(SEQ_THREADS), L.lds, s,

@@ -145,7 +145,6 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const float *__restrict__
 // Decode attention
 // ---------------------------------------------------------------------------
 
-constexpr int ATT_CHUNK = 256;  // cached positions per workgroup (4 waves x 64)
 
 // Wave-wide max / sum through DPP lane moves (quad swaps, half-row and row
 // mirrors, row broadcasts 15 and 31; lane 63 ends with the result, read back
@@ -469,11 +468,6 @@ hipError_t launch_kv_write(const float *qkv, int64_t tokens, int n_heads, int n_
     }
 #undef Q8_KVW
     return hipGetLastError();
-}
-
-size_t attention_workspace_bytes(int64_t seqs, int n_heads, int n_kv, int head_dim, int64_t max_len) {
-    const int64_t splits = (max_len + ATT_CHUNK - 1) / ATT_CHUNK;
-    return 256 + (size_t)seqs * n_kv * splits * (n_heads / n_kv) * (head_dim + 2) * 4;
 }
 
 template <int HD, int G>

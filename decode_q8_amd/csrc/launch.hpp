@@ -8,6 +8,11 @@
 
 namespace q8k {
 
+// Counts the library's queries of device properties (architecture, CU count,
+// occupancy).  Each is made once per device and kernel variant and then
+// cached, so the count stops growing after the first calls.
+void note_device_query();
+
 hipError_t launch_quantize(const float *x, int64_t ld_x, int64_t rows, int64_t k, int layout, void *out,
                            hipStream_t s);
 
@@ -43,6 +48,19 @@ struct SeqHostStep {
     float *y;
     int64_t ld_x, ld_y, n, k;
 };
+// Host plan of a sequence launch: kernel variant, dynamic LDS, workspace size
+// and layout (flag lines, each split step's counters and sums), and each
+// step's split of its tiles over workgroups.
+struct SeqPlan {
+    bool one;          // every unit has at most one group per wave
+    size_t lds;        // dynamic LDS bytes per workgroup
+    size_t workspace;  // bytes
+    int32_t flag_off;  // byte offset of the flag lines
+    uint32_t ws_off[SEQ_MAX_STEPS];  // split step's counters and sums at 256 * ws_off (0: none)
+    uint16_t wgs[SEQ_MAX_STEPS];     // workgroups per tile
+    uint16_t segs[SEQ_MAX_STEPS];    // segments per workgroup
+};
+void seq_plan(const SeqHostStep *steps, int count, int64_t m, SeqPlan &plan);
 size_t gemv_sequence_workspace_bytes(const SeqHostStep *steps, int count, int64_t m);
 hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, void *workspace, hipStream_t s);
 

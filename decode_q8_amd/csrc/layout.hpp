@@ -1,0 +1,40 @@
+// Sizes of the byte formats and of the work decomposition, shared by the
+// kernels and the host-side planning (plain constants: this header compiles
+// with any C++17 host compiler as well as hipcc).
+#pragma once
+
+#include <stdint.h>
+
+namespace q8k {
+
+// Q8_0 blocks and the packed layout
+constexpr int QK = 32;            // values per block
+constexpr int BLOCK_BYTES = 34;   // fp16 scale + 32 int8
+constexpr int TILE_ROWS = 64;     // rows per packed record = lanes per wave
+constexpr int GROUP_BLOCKS = 8;   // blocks per packed record and per summation group
+constexpr int GROUP_K = GROUP_BLOCKS * QK;              // 256 values
+constexpr int RECORD_BYTES = TILE_ROWS * GROUP_BLOCKS * BLOCK_BYTES;  // 17408
+constexpr int RECORD_Q_BYTES = TILE_ROWS * GROUP_K;     // 16384
+constexpr int ROW_GROUP_BYTES = GROUP_BLOCKS * BLOCK_BYTES;           // 272
+constexpr int SEG_GROUPS = 8;     // groups per summation segment (2048 values)
+
+// GEMV plan: up to 8 waves per workgroup; the group sums a workgroup keeps in
+// LDS must fit in 64 KB
+constexpr int GEMV_MAX_WAVES = 8;
+constexpr int64_t GEMV_LDS_LIMIT = 64 * 1024;
+
+// Sequence workspace: [0, 4) status word; from byte 256 SEQ_CTR_PER_STEP
+// counters of SEQ_CTR_LINE bytes per step (the step's counter, then its
+// sub-counters); SEQ_FLAG_LINES flag lines of SEQ_FLAG_LINE_BYTES from a
+// 4 KB-aligned offset; then the split steps' tile counters and segment sums.
+constexpr int SEQ_FLAG_LINES = 8;
+constexpr int SEQ_FLAG_LINE_BYTES = 4096;  // one int32 flag per step in each line
+constexpr int SEQ_NSUB = 16;               // sub-counters of a step with many units
+constexpr int SEQ_CTR_LINE = 128;          // bytes per counter
+constexpr int SEQ_CTR_PER_STEP = SEQ_NSUB + 1;
+constexpr int SEQ_THREADS = 512;
+
+// Decode attention: cached positions per workgroup
+constexpr int ATT_CHUNK = 256;
+
+}  // namespace q8k

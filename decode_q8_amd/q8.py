@@ -13,7 +13,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libq8.so")
+# Q8_LIB names another build of the same sources (the host-only sanitizer
+# build of the test suite); the digest check below applies to it as well.
+LIB_PATH = os.environ.get("Q8_LIB") or os.path.join(HERE, "libq8.so")
 
 Q8_OK, Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE, Q8_ERR_DEVICE, Q8_ERR_LAUNCH = range(7)
 Q8_LAYOUT_ROWS, Q8_LAYOUT_PACKED, Q8_LAYOUT_ACT = 0, 1, 2
@@ -22,7 +24,7 @@ Q8_BLOCK_BYTES = 34
 Q8_TILE_ROWS = 64
 Q8_GEMV_MAX_ROWS = 8
 Q8_SEQUENCE_MAX_STEPS = 72
-Q8_ABI_VERSION = 4
+Q8_ABI_VERSION = 5
 Q8_NORM_MAX_K = 16384
 Q8_ROUTE_MAX_EXPERTS = 1024
 Q8_ROUTE_MAX_TOPK = 32
@@ -37,6 +39,8 @@ class q8_gemv_step(ctypes.Structure):
 _P, _I64, _I, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32
 SIGNATURES = {
     "q8_abi_version": ([], _U32),
+    "q8_device_queries": ([], _U32),
+    "q8_build_digest": ([], ctypes.c_char_p),
     "q8_status_str": ([_I], ctypes.c_char_p),
     "q8_quantized_bytes": ([_I64, _I64], _SZ),
     "q8_quantize_rows": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
@@ -70,18 +74,28 @@ class Q8Error(RuntimeError):
 _lib = None
 
 
+class StaleLibraryError(RuntimeError):
+    """libq8.so was built from other sources than the ones in this tree."""
+
+
 def lib() -> ctypes.CDLL:
-    """Load libq8.so (building it first if no build exists)."""
+    """Load libq8.so (building it first if no build exists).  A build whose
+    recorded source digest differs from this tree's sources is refused: its
+    kernels are not the ones the sources describe."""
     global _lib
     if _lib is None:
+        from . import build as _build
         if not os.path.exists(LIB_PATH):
-            from . import build as _build
             _build.build()
         L = ctypes.CDLL(LIB_PATH)
         for name, (args, res) in SIGNATURES.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = res
+        built, tree = L.q8_build_digest().decode(), _build.source_digest()
+        if built != tree:
+            raise StaleLibraryError(f"{LIB_PATH} was built from sources with digest {built}, but the tree's sources "
+                                    f"have digest {tree}: rebuild it (__graft_entry__.build())")
         _lib = L
     return _lib
 
@@ -115,6 +129,14 @@ def status_str(status: int) -> str:
 
 def q8_abi_version() -> int:
     return lib().q8_abi_version()
+
+
+def q8_device_queries() -> int:
+    return lib().q8_device_queries()
+
+
+def q8_build_digest() -> str:
+    return lib().q8_build_digest().decode()
 
 
 def q8_status_str(status: int) -> str:

@@ -71,9 +71,9 @@
 extern "C" {
 #endif
 
-#define Q8_ABI_VERSION 4u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize, the
+#define Q8_ABI_VERSION 5u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize, the
                               MoE router, SwiGLU and combine, and the Q8 KV cache entry points;
-                              4: q8_stream_read */
+                              4: q8_stream_read; 5: q8_device_queries, q8_build_digest */
 #define Q8_BLOCK 32          /* values per block */
 #define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
 #define Q8_TILE_ROWS 64      /* rows per packed record */
@@ -95,6 +95,18 @@ typedef enum { Q8_LAYOUT_ROWS = 0, Q8_LAYOUT_PACKED = 1, Q8_LAYOUT_ACT = 2 } q8_
 
 /* Version of this ABI (Q8_ABI_VERSION). */
 uint32_t q8_abi_version(void);
+
+/* Number of device-property queries (architecture, CU count, kernel
+ * occupancy) the library has made in this process.  Each is made once per
+ * device and kernel variant, at its first use, and cached; a caller can check
+ * that repeated calls on the token path query nothing ("Ferrule" README,
+ * "Core features": the token hot path performs no architecture discovery). */
+uint32_t q8_device_queries(void);
+
+/* sha256 (hex) of the sources and compile flags this library was built from
+ * (static string, never NULL); the Python binding compares it with the tree
+ * it is loaded from and refuses a stale build. */
+const char *q8_build_digest(void);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *q8_status_str(int status);
@@ -196,12 +208,18 @@ size_t q8_sequence_workspace_bytes(const q8_gemv_step *steps, int count, int64_t
  *            k % 256 == 0; 1 <= m <= 8 for all steps.
  *  workspace device, >= q8_sequence_workspace_bytes(steps, count, m) bytes,
  *            zero-filled before its first use; every completed call leaves
- *            it zero except the int32 status word at byte 0, which a call
- *            sets to Q8_ERR_LAUNCH if one of its internal waits timed out
- *            (possible only when other work occupies the GPU and not all of
- *            the call's workgroups can be resident; outputs are still
- *            correct) -- clear it to reuse the flag.  Calls that run
- *            concurrently need separate workspaces.
+ *            it zero, so one workspace serves any sequence of calls on one
+ *            stream (graph replays included).  Calls that run concurrently
+ *            need separate workspaces.  Its int32 word at byte 0 is the
+ *            call's status: 0, or Q8_ERR_LAUNCH if one of the internal waits
+ *            timed out (possible only when other work occupies the GPU so
+ *            that not all of the call's workgroups are resident at once).
+ *            After a non-zero status the outputs of that call are undefined
+ *            and the workspace must be zero-filled again before reuse.
+ *  Aliasing: no y may overlap any step's x (so step i + 1 cannot read step
+ *  i's y in place: copy it, or give each step its own input), the y's must
+ *  be disjoint, and the workspace must overlap no x or y; violations return
+ *  Q8_ERR_ARG.
  *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
  *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m, void *workspace,

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     m = re.search(r"#define Q8_ABI_VERSION (\d+)u", open(HEADER).read())
-    assert int(m.group(1)) == q8.Q8_ABI_VERSION == q8.q8_abi_version() == 4
+    assert int(m.group(1)) == q8.Q8_ABI_VERSION == q8.q8_abi_version() == 5
     for s in range(7):
         assert q8.status_str(s).startswith("Q8_")
     assert q8.status_str(99) == "Q8_ERR_UNKNOWN"
@@ -189,6 +189,51 @@ def test_sequence_workspace_and_validation():
     assert _seq([o], 1, ws=None) == q8.Q8_ERR_WORKSPACE
     assert _seq([down], 1, wsb=1024) == q8.Q8_ERR_WORKSPACE
     assert _seq([o], 1, ws=D + 8) == q8.Q8_ERR_ALIGN
+
+
+def test_sequence_aliasing_is_rejected():
+    """Every x must be ready before the call: a y over any x (the in-place
+    chaining y_i == x_(i+1) among them), two y's sharing bytes, or the
+    workspace over an x or y is refused before any HIP call."""
+    E, F, G = 0x7F0000500000, 0x7F0000600000, 0x7F0000700000
+    s0 = (A, 2048, B, 2048, 2048, C, 2048)
+    s1 = (E, 2048, B, 2048, 2048, F, 2048)
+    ws = q8.q8_sequence_workspace_bytes([s0, s1], 1)
+    assert _seq([s0, s1], 1, ws=G, wsb=ws) == q8.Q8_ERR_DEVICE           # valid: reaches the device check
+    assert _seq([s0, (C, 2048, B, 2048, 2048, F, 2048)], 1, ws=G, wsb=ws) == q8.Q8_ERR_ARG    # y_0 == x_1
+    assert _seq([s0, (E, 2048, B, 2048, 2048, A, 2048)], 1, ws=G, wsb=ws) == q8.Q8_ERR_ARG    # y_1 over x_0
+    assert _seq([s0, (E, 2048, B, 2048, 2048, C + 4096, 2048)], 1, ws=G, wsb=ws) == q8.Q8_ERR_ARG  # y's overlap
+    assert _seq([s0, (E, 2048, B, 2048, 2048, C + 8192, 2048)], 1, ws=G, wsb=ws) == q8.Q8_ERR_DEVICE  # adjacent
+    assert _seq([s0, (A + 8176, 2048, B, 2048, 2048, F, 2048)], 1, ws=G, wsb=ws) == q8.Q8_ERR_DEVICE  # x's may share
+    assert _seq([s0, s1], 1, ws=E, wsb=ws) == q8.Q8_ERR_ARG              # workspace over an x
+    assert _seq([s0, s1], 1, ws=F - 4096, wsb=ws) == q8.Q8_ERR_ARG       # workspace over a y
+    # with m rows the extents are (m - 1) * ld + n (or k)
+    s1m = (E, 4096, B, 2048, 2048, F, 4096)
+    ws2 = q8.q8_sequence_workspace_bytes([s0, s1m], 2)
+    assert _seq([(A, 4096, B, 2048, 2048, C, 4096), s1m], 2, ws=G, wsb=ws2) == q8.Q8_ERR_DEVICE
+    assert _seq([(A, 4096, B, 2048, 2048, E + 4 * 6144, 4096), s1m], 2, ws=G, wsb=ws2) == q8.Q8_ERR_DEVICE  # adjacent
+    assert _seq([(A, 4096, B, 2048, 2048, E + 4 * 6144 - 16, 4096), s1m], 2, ws=G, wsb=ws2) == q8.Q8_ERR_ARG
+
+
+def test_stale_library_is_refused(monkeypatch):
+    """A libq8.so built from other sources than the tree's is not loaded."""
+    from decode_q8_amd import build
+    assert q8.q8_build_digest() == build.source_digest()
+    saved = q8._lib
+    try:
+        q8._lib = None
+        monkeypatch.setattr(build, "source_digest", lambda: "0" * 64)
+        with pytest.raises(q8.StaleLibraryError):
+            q8.lib()
+    finally:
+        q8._lib = saved
+
+
+def test_device_queries_need_a_device():
+    """Without a GPU no call gets as far as a device query."""
+    before = q8.q8_device_queries()
+    assert _seq([(A, 2048, B, 2048, 2048, C, 2048)], 1) == q8.Q8_ERR_DEVICE
+    assert q8.q8_device_queries() == before
 
 
 def test_rmsnorm_quantize_validation():

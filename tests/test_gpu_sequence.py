@@ -53,7 +53,7 @@ def _single(s, m):
 LAYER = [(3072, 2048), (2048, 2048), (16384, 2048), (2048, 8192)]  # fused QKV, O, gate||up, down
 
 
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 4, 6, 8])
 def test_decode_layers_bit_identical_to_single_launches(m):
     """Two decode layers plus a head: every step equals its own launch bit for
     bit, sampled outputs meet the oracle bound, the workspace returns to zero."""
@@ -84,7 +84,7 @@ def test_general_path_many_groups_per_wave():
         assert bits_equal(down(s["y"]), _single(s, 2)), f"step {i}"
 
 
-@pytest.mark.parametrize("m", [1, 3])
+@pytest.mark.parametrize("m", [1, 3, 8])
 def test_split_steps_back_to_back_and_last(m):
     """Steps whose tiles are split over several workgroups (long rows, few
     tiles): two in a row (the second chains the first's segment sums while
@@ -139,3 +139,19 @@ def test_graph_replay():
         assert int(down(ws).astype(np.uint8).any()) == 0, f"replay {r}: workspace"
         for i, s in enumerate(steps):
             assert bits_equal(down(s["y"]), eager[i]), f"replay {r} step {i}"
+
+
+def test_no_device_queries_after_the_first_call():
+    """The grid size (resident workgroups per CU, CU count) is discovered once
+    per device and kernel variant and cached: repeated calls make no further
+    device queries."""
+    steps = _chain(LAYER, 1, seed=650)
+    ws = _run(steps, 1)
+    torch.cuda.synchronize()
+    after_first = q8.q8_device_queries()
+    assert after_first >= 1
+    for _ in range(5):
+        _run(steps, 1, ws)
+    torch.cuda.synchronize()
+    assert q8.q8_device_queries() == after_first
+    assert int(down(ws).astype(np.uint8).any()) == 0
