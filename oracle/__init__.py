@@ -15,7 +15,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "q8ref.c")
-LIB = os.path.join(HERE, "libq8ref.so")
+# Q8REF_LIB names another build of q8ref.c (the sanitizer build of the tests).
+LIB = os.environ.get("Q8REF_LIB") or os.path.join(HERE, "libq8ref.so")
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 LAYOUT_ROWS = 0
