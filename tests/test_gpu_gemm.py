@@ -1,5 +1,7 @@
 """Prefill GEMM (q8_matmul with m > 8, int8 MFMA) against the oracle, and its
 row invariance: a row's output does not depend on m or on the row order."""
+import os
+
 import numpy as np
 import pytest
 
@@ -57,21 +59,41 @@ def test_row_invariance_across_tile_shapes():
     assert bits_equal(y_small, y_big[900:1000])
 
 
+THREADS = min(16, os.cpu_count() or 1)
+
+
 @pytest.mark.parametrize("m", wl.PREFILL_M)
 @pytest.mark.parametrize("n,k", wl.PREFILL_NK)
-def test_prefill_full_size_sampled(m, n, k):
-    """Every prefill configuration at full size: 1024 sampled outputs against
-    the oracle (which computes them one by one)."""
+def test_prefill_full_size_whole_output(m, n, k):
+    """Every prefill configuration at full size, every output against the
+    oracle.  m = 2048 and 752 x 8192 run the 128 x 128 tiled kernel, the rest
+    the k-split strip kernel."""
     x = wl.activation(wl.PREFILL, m, m, k, outliers=True)
     w = wl.weight(wl.PREFILL, n + k, n, k)
     xq = quantize(x, q8.Q8_LAYOUT_ACT)
     wr, wp = weights_packed(w)
     y = _gemm(xq, m, wp, n, k)
-    rng = np.random.default_rng(m * n + k)
-    mi = rng.integers(0, m, 1024)
-    ni = rng.integers(0, n, 1024)
-    mi[:4] = [0, m - 1, 0, m - 1]
-    ni[:4] = [0, n - 1, n - 1, 0]
-    y_ref, S = oracle.matmul_points(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
-                                    mi, ni)
-    check_tol(y[mi, ni], y_ref, S, f"prefill m={m} n={n} k={k}")
+    y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                             threads=THREADS)
+    check_tol(y, y_ref, S, f"prefill m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(2048, 2112, 2048), (1100, 4160, 512)])
+def test_tiled_ragged_n_whole_output(m, n, k):
+    """Tiled kernel with an odd number of 64-row weight tiles (n / 64 = 33 and
+    65): the last workgroup column holds one real tile and reloads it for its
+    second; every output against the oracle, and the columns past n are never
+    written (checked through a wider output stride)."""
+    import torch
+    x = wl.activation(wl.PREFILL, 70 + m, m, k, outliers=True)
+    w = wl.weight(wl.PREFILL, 70 + n, n, k)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    _, wp = weights_packed(w)
+    ld = n + 64
+    yt = torch.full((m, ld), 7.0, dtype=torch.float32, device="cuda")
+    q8.q8_matmul(xq, m, wp, q8.Q8_LAYOUT_PACKED, n, k, yt, ld)
+    yfull = down(yt)
+    assert np.all(yfull[:, n:] == 7.0), "columns past n were written"
+    y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                             threads=THREADS)
+    check_tol(yfull[:, :n], y_ref, S, f"ragged tiled m={m} n={n} k={k}")

@@ -204,23 +204,22 @@ def test_single_gemv_full_size():
 
 
 @pytest.mark.parametrize("name,n,k", [m[:3] for m in wl.LLAMA_LAYER_MATS] + [wl.LLAMA_HEAD])
-def test_decode_shapes_full_size_sampled(name, n, k):
+def test_decode_shapes_full_size_whole_output(name, n, k):
     """Full decode-step shapes (fused QKV, O, gate||up, down, LM head) at m = 1
-    and m = 8: 512 sampled outputs per m against the oracle; every row of the
-    m = 8 batch bit-identical to its m = 1 run; both layouts bit-identical."""
+    and m = 8: every output against the oracle; every row of the m = 8 batch
+    bit-identical to its m = 1 run; both layouts bit-identical."""
+    import os
     w = wl.weight(wl.BATCHED, 1000 + n + k, n, k)
     x = wl.activation(wl.BATCHED, 1000 + n + k, 8, k)
     wr, wp = weights_packed(w)
     wr_h = ref_quantize(w, oracle.LAYOUT_ROWS)
-    rng = np.random.default_rng(n + k)
     y1 = None
     for m in (1, 8):
         xq = quantize(x[:m], q8.Q8_LAYOUT_ACT)
         y = _gemv(xq, m, wp, 1, n, k)
-        mi = rng.integers(0, m, 512)
-        ni = rng.integers(0, n, 512)
-        y_ref, S = oracle.matmul_points(ref_quantize(x[:m], oracle.LAYOUT_ACT), m, wr_h, n, k, mi, ni)
-        check_tol(y[mi, ni], y_ref, S, f"{name} m={m}")
+        y_ref, S = oracle.matmul(ref_quantize(x[:m], oracle.LAYOUT_ACT), m, wr_h, n, k,
+                                 threads=min(16, os.cpu_count() or 1))
+        check_tol(y, y_ref, S, f"{name} m={m}")
         if m == 1:
             y1 = y
             assert bits_equal(y, _gemv(xq, 1, wr, 0, n, k)), f"{name}: layouts differ"
