@@ -69,6 +69,11 @@ def parse():
     ap.add_argument("--layout", choices=["packed", "rows"], default="packed",
                     help="decode/batched: weight layout; rows (row-contiguous Q8_0) implies one launch per matrix")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ramp-seconds", type=float, default=0.3,
+                    help="replays of each captured step before timing, by wall time, on top of --warmup: "
+                         "the clocks ramp up over the first ~0.2 s of work")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode: leave out the prefill GEMM half of the metric")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     return ap.parse_args()
 
@@ -111,6 +116,7 @@ def base_record(args, metric, value, unit, ms_per_step, dtype, config, roofline,
         "config": config,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "clock_ramp": {"seconds": RAMP["seconds"], "replays": RAMP["replays"]},
     }
 
 
@@ -132,6 +138,9 @@ def hbm_roofline(kernel, bytes_per_launch, avg_ms):
 # Spread of the per-replay times of the most recent graph_time call (ms at the
 # 10th, 50th and 90th percentile), reported beside the mean in every record.
 STEP_SPREAD = {}
+# Wall time of replays every graph_time call runs after its warm-up and before
+# timing (set from --ramp-seconds), and how many replays that took last time.
+RAMP = {"seconds": 0.3, "replays": 0}
 
 
 def graph_time(run, stream, steps, warmup):
@@ -149,6 +158,15 @@ def graph_time(run, stream, steps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    # clock ramp: keep replaying for RAMP["seconds"] of wall time, whatever
+    # --warmup asked for, so the timed pass does not start on rising clocks
+    t_ramp, ramp = time.time(), 0
+    while time.time() - t_ramp < RAMP["seconds"]:
+        for _ in range(16):
+            g.replay()
+        ramp += 16
+        torch.cuda.synchronize()
+    RAMP["replays"] = ramp
     t = Timer(torch.cuda.current_stream())
     t.start()
     for _ in range(steps):
@@ -305,6 +323,17 @@ def oracle_rows(w: np.ndarray, threads: int) -> np.ndarray:
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the CPU baseline."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def timed_repeat(fn, min_seconds=10.0, max_reps=100000):
     """Run fn until min_seconds have passed (the CPU baseline's bounded sample:
     about 10 s of oracle work); returns (seconds per call, calls)."""
@@ -429,6 +458,10 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
         if not torch.equal(y.view(torch.int32), eager[i].view(torch.int32)):
             raise RuntimeError(f"graph replay output {i} differs from the eager step")
     if mode == "sequence":
+        # a non-zero status word means a wait timed out: the outputs are undefined
+        status = int(step.seq_ws[:4].view(torch.int32).cpu()[0])
+        if status != 0:
+            raise RuntimeError(f"sequence status word {status}: a wait timed out, outputs undefined")
         # the one-launch step must equal the per-matrix launches bit for bit
         step.run_per_matrix(stream)
         torch.cuda.synchronize()
@@ -459,11 +492,15 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
 
     cpu = None
     if not args.no_cpu_baseline:
-        sec, reps_c = timed_repeat(lambda: step.oracle_step(args.threads))
+        sec, reps_c = timed_repeat(lambda: step.oracle_step(args.threads), min_seconds=8.0)
+        sec1, reps_1 = timed_repeat(lambda: step.oracle_step(1), min_seconds=6.0)
         cpu = {"value": round(step.weight_bytes / sec / 1e9, 3), "unit": "GB/s", "cores": args.threads,
                "kind": "oracle",
                "sample": f"the whole {label} ({len(mats)} matrices, quantize + matmul), {reps_c} runs, "
-                         f"{sec:.3f} s each"}
+                         f"{sec:.3f} s each",
+               "value_1_core": round(step.weight_bytes / sec1 / 1e9, 3),
+               "sample_1_core": f"the same step on one thread, {reps_1} runs, {sec1:.3f} s each",
+               "cpu_model": cpu_model()}
 
     launches = {"sequence": f"1 (q8_quantize_matmul_sequence over {len(mats)} fused quantize+GEMV steps)",
                 "fused": f"{len(mats)} fused quantize+GEMV",
@@ -515,12 +552,33 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
                        roof, cpu)
 
 
+HEADLINE_METRIC = "Q8_0 matmul weight GB/s (%HBM peak) at M=1; int8 TOPS (%MFMA peak) prefill"
+
+
 def bench_decode(args):
     import workloads as wl
     m = args.m if args.workload == "batched" else 1
     label = (f"Llama-3.2-1B-shaped decode step, batch {m}: 16 x (QKV 3072x2048, O 2048x2048, "
              "gate||up 16384x2048, down 2048x8192) + LM head 128256x2048, Q8_0 packed")
-    return bench_gemv_workload(args, wl.decode_matrices(), wl.BATCHED if m > 1 else wl.DECODE, m, label)
+    rec = bench_gemv_workload(args, wl.decode_matrices(), wl.BATCHED if m > 1 else wl.DECODE, m, label)
+    if args.workload == "decode" and not args.no_prefill and not args.per_matrix and not args.unfused \
+            and args.layout == "packed":
+        # the metric's second half: the prefill GEMM, measured in the same run
+        p = prefill_measure(args)
+        rec["metric"] = HEADLINE_METRIC
+        rec["prefill"] = p
+        c = rec["config"]
+        c["prefill_int8_TOPS"] = p["value"]
+        c["prefill_frac_of_int8_peak"] = p["frac_of_int8_peak"]
+        c["prefill_ms_per_step"] = p["ms_per_step"]
+        for kname, r in p["rooflines"].items():
+            key = "tiled" if kname.startswith("gemm_kernel") else "strip"
+            c[f"prefill_{key}_kernel_TOPS"] = r["achieved"]
+            c[f"prefill_{key}_kernel_frac"] = r["frac"]
+        c["prefill_mfma_busy_pct"] = p["mfma_busy_pct"]
+        if p["cpu_baseline"]:
+            c["prefill_cpu_baseline_TOPS"] = p["cpu_baseline"]["value"]
+    return rec
 
 
 def bench_single(args):
@@ -534,7 +592,22 @@ def bench_single(args):
 # prefill GEMM
 # --------------------------------------------------------------------------
 
-def bench_prefill(args):
+def gemm_kernel_for(m: int, n: int) -> str:
+    """The GEMM kernel libq8 runs for an m x n output (its rule: 128 x 128
+    workgroup tiles when there are at least 256 of them, else 32 x 64 strips
+    with k split across the waves)."""
+    return "gemm_kernel<4, 2>" if ((m + 127) // 128) * ((n + 127) // 128) >= 256 else "gemm_strip_kernel"
+
+
+PREFILL_ORDER_SEED = 20261202
+
+
+def prefill_measure(args):
+    """The nine prefill GEMM shapes (M in {188, 752, 2048} x (N, K) in
+    {(2048, 2048), (8192, 2048), (2048, 8192)}): 256 sampled outputs of every
+    shape checked against the oracle first, then the shapes captured in one
+    graph in a seeded shuffled order and timed; per-launch durations by HIP
+    events on the launch stream give the two kernels' rooflines."""
     import torch
 
     import oracle
@@ -547,12 +620,14 @@ def bench_prefill(args):
         w = wl.weight(wl.PREFILL, n + k, n, k)
         wr = q8.quantize(torch.from_numpy(w).to(dev), q8.Q8_LAYOUT_ROWS)
         wp = q8.repack(wr, n, k)
-        host_rows = None if args.no_cpu_baseline else oracle_rows(w, args.threads)
+        host_rows = oracle_rows(w, args.threads)
         for m in wl.PREFILL_M:
             x = wl.activation(wl.PREFILL, m, m, k, outliers=True)
             xq = q8.quantize(torch.from_numpy(x).to(dev), q8.Q8_LAYOUT_ACT)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
             cases.append(dict(m=m, n=n, k=k, xq=xq, wp=wp, y=y, x=x, rows=host_rows))
+    order = np.random.default_rng(PREFILL_ORDER_SEED).permutation(len(cases))
+    cases = [cases[i] for i in order]
     torch.cuda.synchronize()
 
     def run(s, timers=None):
@@ -564,46 +639,81 @@ def bench_prefill(args):
             if timers is not None:
                 timers[i].stop()
 
+    # parity first: sampled outputs of every shape against the oracle
+    with torch.cuda.stream(stream):
+        run(stream)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    pts = []
+    for c in cases:
+        xa = oracle.quantize_rows(c["x"], oracle.LAYOUT_ACT)
+        mi, ni = rng.integers(0, c["m"], 256), rng.integers(0, c["n"], 256)
+        y_ref, S = oracle.matmul_points(xa, c["m"], c["rows"], c["n"], c["k"], mi, ni)
+        got = c["y"].cpu().numpy()[mi, ni].astype(np.float64)
+        if np.any(np.abs(got - y_ref) > 1e-5 * S):
+            raise RuntimeError(f"prefill M={c['m']} N={c['n']} K={c['k']}: outputs outside 1e-5*S of the oracle")
+        pts.append((c, xa))
+
     ms_per_step, graph = graph_time(run, stream, args.steps, args.warmup)
     ms = per_launch_ms(run, len(cases), stream, graph, reps=max(1, min(args.steps, 10)))
     ops = np.array([2.0 * c["m"] * c["n"] * c["k"] for c in cases])
     value = ops.sum() / (ms_per_step * 1e-3) / 1e12
-    per_case = {f"M{c['m']}_N{c['n']}_K{c['k']}": round(ops[i] / (ms[i] * 1e-3) / 1e12, 1)
-                for i, c in enumerate(cases)}
-    achieved = float(ops.mean() / (ms.mean() * 1e-3) / 1e12)
+    tops_by_case = {f"M{c['m']}_N{c['n']}_K{c['k']}": round(ops[i] / (ms[i] * 1e-3) / 1e12, 1)
+                    for i, c in enumerate(cases)}
+    kernels = {}
+    for i, c in enumerate(cases):
+        kname = gemm_kernel_for(c["m"], c["n"])
+        o, t, names = kernels.get(kname, (0.0, 0.0, []))
+        kernels[kname] = (o + ops[i], t + ms[i], names + [f"M{c['m']}_N{c['n']}_K{c['k']}"])
+    mfma_busy = profiled_field("gemm_prefill_counters.txt", "decode_q8_amd/csrc/gemm.hip", "mfma_busy_pct")
+    rooflines = {}
+    for kname, (o, t, names) in kernels.items():
+        achieved = o / (t * 1e-3) / 1e12
+        rooflines[kname] = {"kernel": "q8k::" + kname, "bound": "mfma", "achieved": round(achieved, 1),
+                            "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                            "traffic": None, "avg_launch_us": round(t / len(names) * 1e3, 3),
+                            "algorithmic_ops_per_launch": int(o / len(names)), "shapes": names,
+                            "timing": "one event pair per launch on the launch stream, queued ahead; "
+                                      "achieved = total ops / total duration over its shapes"}
     cpu = None
     if not args.no_cpu_baseline:
         # bounded sample: 2048 outputs of every case, computed one by one
         rng = np.random.default_rng(0)
-        pts = []
-        for c in cases:
-            xa = oracle.quantize_rows(c["x"], oracle.LAYOUT_ACT)
-            pts.append((c, xa, rng.integers(0, c["m"], 2048), rng.integers(0, c["n"], 2048)))
-        def sample():
-            for c, xa, mi, ni in pts:
+        sample = [(c, xa, rng.integers(0, c["m"], 2048), rng.integers(0, c["n"], 2048)) for c, xa in pts]
+
+        def one_pass():
+            for c, xa, mi, ni in sample:
                 oracle.matmul_points(xa, c["m"], c["rows"], c["n"], c["k"], mi, ni)
 
-        dt, reps = timed_repeat(sample)
+        dt, reps = timed_repeat(one_pass, min_seconds=6.0)
         cpu_ops = sum(2.0 * 2048 * c["k"] for c in cases)
         cpu = {"value": round(cpu_ops / dt / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
-               "sample": f"2048 outputs of each of the 9 prefill cases, single-threaded, {reps} repetitions, "
-                         f"{dt * reps:.1f} s"}
-    config = {
+               "sample": f"2048 outputs of each of the 9 prefill shapes, single-threaded, {reps} repetitions, "
+                         f"{dt * reps:.1f} s", "cpu_model": cpu_model()}
+    return {
+        "metric": "Q8_0 prefill GEMM int8 TOPS (%MFMA peak)",
+        "value": round(value, 3), "unit": "TOPS", "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
+        "ms_per_step": round(ms_per_step, 5), "ops_per_step": int(ops.sum()),
         "workload": "prefill GEMM: M in {188, 752, 2048} x (N, K) in {(2048, 2048), (8192, 2048), (2048, 8192)}, "
                     "Q8_0 packed weights, activations with 1% outlier channels x20",
-        "ops_per_step": int(ops.sum()),
-        "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
-        "tops_by_case": per_case,
-        "hip_graph": True,
+        "oracle_check": "256 sampled outputs per shape within 1e-5 * sum|block terms|",
+        "order": [f"M{c['m']}_N{c['n']}_K{c['k']}" for c in cases], "order_seed": PREFILL_ORDER_SEED,
+        "tops_by_case": tops_by_case, "rooflines": rooflines, "mfma_busy_pct": mfma_busy,
+        "cpu_baseline": cpu, "step_spread_ms_p10_p50_p90": [STEP_SPREAD.get(q) for q in ("p10", "p50", "p90")],
     }
-    roof = {"kernel": "q8k::gemm_kernel", "bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
-            "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
-            "traffic": profiled_traffic("gemm_prefill.txt", "decode_q8_amd/csrc/gemm.hip"),
-            "avg_launch_us": round(float(ms.mean()) * 1e3, 3), "algorithmic_ops_per_launch": int(ops.mean()),
-            "mfma_busy_pct": profiled_field("gemm_prefill_counters.txt", "decode_q8_amd/csrc/gemm.hip",
-                                            "mfma_busy_pct")}
-    return base_record(args, "Q8_0 prefill GEMM int8 TOPS (%MFMA peak)", value, "TOPS", ms_per_step,
-                       "int8xint8->int32 (MFMA), fp32 scale/sum", config, roof, cpu)
+
+
+def bench_prefill(args):
+    p = prefill_measure(args)
+    tiled = p["rooflines"].get("gemm_kernel<4, 2>")
+    roof = dict(tiled) if tiled else dict(next(iter(p["rooflines"].values())))
+    roof["traffic"] = profiled_traffic("gemm_prefill.txt", "decode_q8_amd/csrc/gemm.hip")
+    roof["mfma_busy_pct"] = p["mfma_busy_pct"]
+    config = {"workload": p["workload"], "ops_per_step": p["ops_per_step"],
+              "frac_of_int8_peak": p["frac_of_int8_peak"], "tops_by_case": p["tops_by_case"],
+              "rooflines_by_kernel": p["rooflines"], "order": p["order"], "hip_graph": True}
+    return base_record(args, p["metric"], p["value"], "TOPS", p["ms_per_step"],
+                       "int8xint8->int32 (MFMA), fp32 scale/sum", config, roof, p["cpu_baseline"])
 
 
 # --------------------------------------------------------------------------
@@ -1067,6 +1177,7 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
+    RAMP["seconds"] = args.ramp_seconds
     fn = {"decode": bench_decode, "batched": bench_decode, "single": bench_single, "prefill": bench_prefill,
           "moe": bench_moe, "norm": bench_norm, "kv": bench_kv, "copy": bench_copy,
           "read": bench_read, "quantize": bench_quantize}[args.workload]
