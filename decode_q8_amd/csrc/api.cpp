@@ -18,6 +18,7 @@
 #endif
 
 static_assert(Q8_SEQUENCE_MAX_STEPS == q8k::SEQ_MAX_STEPS, "sequence length limit");
+static_assert(Q8_SEQUENCE_SCRATCH_BYTES == q8k::SEQ_SCRATCH_BYTES, "sequence scratch size");
 static_assert(Q8_ROUTE_MAX_EXPERTS == q8k::ROUTE_MAX_EXPERTS && Q8_ROUTE_MAX_TOPK == q8k::ROUTE_MAX_TOPK,
               "router limits");
 static_assert(Q8_ATTENTION_MAX_LEN == q8k::ATT_MAX_LEN, "attention context limit");
@@ -168,6 +169,23 @@ int sequence_steps(const q8_gemv_step *steps, int count, int64_t m, q8k::SeqHost
     return Q8_OK;
 }
 
+// Every x must be ready before the call: no y may overlap any x (the
+// chaining y_i == x_(i+1) included), the y's must be disjoint, and the
+// workspace (if any) must overlap neither.
+int sequence_aliasing(const q8k::SeqHostStep *hs, int count, int64_t m, const void *workspace, size_t need) {
+    for (int i = 0; i < count; i++) {
+        const size_t yb = (size_t)((m - 1) * hs[i].ld_y + hs[i].n) * 4;
+        if (overlap(workspace, need, hs[i].y, yb)) return Q8_ERR_ARG;
+        if (overlap(workspace, need, hs[i].x, (size_t)((m - 1) * hs[i].ld_x + hs[i].k) * 4)) return Q8_ERR_ARG;
+        for (int j = 0; j < count; j++) {
+            if (overlap(hs[i].y, yb, hs[j].x, (size_t)((m - 1) * hs[j].ld_x + hs[j].k) * 4)) return Q8_ERR_ARG;
+            if (j != i && overlap(hs[i].y, yb, hs[j].y, (size_t)((m - 1) * hs[j].ld_y + hs[j].n) * 4))
+                return Q8_ERR_ARG;
+        }
+    }
+    return Q8_OK;
+}
+
 }  // namespace
 
 size_t q8_sequence_workspace_bytes(const q8_gemv_step *steps, int count, int64_t m) {
@@ -184,22 +202,29 @@ int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m,
     const size_t need = q8k::gemv_sequence_workspace_bytes(hs, count, m);
     if (!workspace || workspace_bytes < need) return Q8_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q8_ERR_ALIGN;
-    // every x must be ready before the call: no y may overlap any x (the
-    // chaining y_i == x_(i+1) included), the y's must be disjoint, and the
-    // workspace must overlap neither
-    for (int i = 0; i < count; i++) {
-        const size_t yb = (size_t)((m - 1) * hs[i].ld_y + hs[i].n) * 4;
-        if (overlap(workspace, need, hs[i].y, yb)) return Q8_ERR_ARG;
-        if (overlap(workspace, need, hs[i].x, (size_t)((m - 1) * hs[i].ld_x + hs[i].k) * 4)) return Q8_ERR_ARG;
-        for (int j = 0; j < count; j++) {
-            if (overlap(hs[i].y, yb, hs[j].x, (size_t)((m - 1) * hs[j].ld_x + hs[j].k) * 4)) return Q8_ERR_ARG;
-            if (j != i && overlap(hs[i].y, yb, hs[j].y, (size_t)((m - 1) * hs[j].ld_y + hs[j].n) * 4))
-                return Q8_ERR_ARG;
-        }
-    }
+    const int alias = sequence_aliasing(hs, count, m, workspace, need);
+    if (alias != Q8_OK) return alias;
     const int dev = check_device();
     if (dev != Q8_OK) return dev;
     return launched(q8k::launch_gemv_sequence(hs, count, m, workspace, stream));
+}
+
+int q8_quantize_matmul_sequence_noalloc(const q8_gemv_step *steps, int count, int64_t m, int32_t *status,
+                                        hipStream_t stream) {
+    q8k::SeqHostStep hs[Q8_SEQUENCE_MAX_STEPS];
+    const int st = sequence_steps(steps, count, m, hs);
+    if (st != Q8_OK) return st;
+    if (q8k::gemv_sequence_workspace_bytes(hs, count, m) > (size_t)Q8_SEQUENCE_SCRATCH_BYTES) return Q8_ERR_WORKSPACE;
+    if ((uintptr_t)status & 3u) return Q8_ERR_ALIGN;
+    const int alias = sequence_aliasing(hs, count, m, nullptr, 0);
+    if (alias != Q8_OK) return alias;
+    for (int i = 0; i < count; i++)
+        if (overlap(status, 4, hs[i].y, (size_t)((m - 1) * hs[i].ld_y + hs[i].n) * 4) ||
+            overlap(status, 4, hs[i].x, (size_t)((m - 1) * hs[i].ld_x + hs[i].k) * 4))
+            return Q8_ERR_ARG;
+    const int dev = check_device();
+    if (dev != Q8_OK) return dev;
+    return launched(q8k::launch_gemv_sequence_scratch(hs, count, m, status, stream));
 }
 
 int q8_rmsnorm_quantize(const float *x, const float *residual_in, float *residual_out, const float *weight,

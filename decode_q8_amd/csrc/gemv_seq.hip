@@ -307,9 +307,7 @@ static hipError_t launch_seq(SeqLayout &L, void *ws, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, void *ws, hipStream_t s) {
-    SeqLayout L;
-    seq_layout(steps, count, m, L);
+static hipError_t launch_layout(SeqLayout &L, int64_t m, void *ws, hipStream_t s) {
 #define Q8_SEQ_CASE(MM) \
     case MM:            \
         return L.one ? launch_seq<MM, true>(L, ws, s) : launch_seq<MM, false>(L, ws, s);
@@ -319,6 +317,74 @@ hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, 
         default: return hipErrorInvalidValue;
     }
 #undef Q8_SEQ_CASE
+}
+
+hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, void *ws, hipStream_t s) {
+    SeqLayout L;
+    seq_layout(steps, count, m, L);
+    return launch_layout(L, m, ws, s);
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free variant: the workspace is this library's own device
+// array, one per GPU, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): its device address is looked up once per device with
+// hipGetSymbolAddress and kept, and that address is what the kernels get.
+// Calls on one GPU share the array, so calls that overlap in time on one GPU
+// race; the part a call uses is zeroed at the start of every call (by a fill
+// kernel, so the call can be captured in a graph).
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) uint8_t scratch[SEQ_SCRATCH_BYTES];
+
+static std::atomic<void *> g_scratch_ptr[SEQ_MAX_DEVICES];
+
+// Device address of this GPU's scratch array (the current device), looked up
+// on the first call on that device.
+static hipError_t scratch_address(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SEQ_MAX_DEVICES) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        note_device_query();
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
+// Zero `words` 16-byte words from p (a grid-stride fill).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4 *__restrict__ p, int64_t words) {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) p[i] = z;
+}
+
+// *out = the sequence's status word (one thread).
+__global__ void copy_status_kernel(const int32_t *__restrict__ ws, int32_t *__restrict__ out) { *out = ws[0]; }
+
+hipError_t launch_gemv_sequence_scratch(const SeqHostStep *steps, int count, int64_t m, int32_t *status,
+                                        hipStream_t s) {
+    SeqLayout L;
+    seq_layout(steps, count, m, L);
+    if (L.workspace > SEQ_SCRATCH_BYTES) return hipErrorInvalidValue;  // the caller checked this already
+    void *ws = nullptr;
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    const int64_t words = (int64_t)((L.workspace + 15) / 16);
+    const int64_t blocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4 *)ws, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_layout(L, m, ws, s);
+    if (e != hipSuccess || !status) return e;
+    hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(1), 0, s, (const int32_t *)ws, status);
+    return hipGetLastError();
 }
 
 }  // namespace q8k

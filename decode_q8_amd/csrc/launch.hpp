@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "layout.hpp"
+
 namespace q8k {
 
 // Counts the library's queries of device properties (architecture, CU count,
@@ -63,6 +65,11 @@ struct SeqPlan {
 void seq_plan(const SeqHostStep *steps, int count, int64_t m, SeqPlan &plan);
 size_t gemv_sequence_workspace_bytes(const SeqHostStep *steps, int count, int64_t m);
 hipError_t launch_gemv_sequence(const SeqHostStep *steps, int count, int64_t m, void *workspace, hipStream_t s);
+// The same with the library's own per-GPU scratch array as the workspace
+// (zeroed at the start of the call); copies the status word to *status when
+// status is not NULL.
+hipError_t launch_gemv_sequence_scratch(const SeqHostStep *steps, int count, int64_t m, int32_t *status,
+                                        hipStream_t s);
 
 // Residual add + RMSNorm + quantization to Q8_LAYOUT_ACT (k <= 16384).
 constexpr int64_t NORM_MAX_K = 16384;

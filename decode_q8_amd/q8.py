@@ -24,6 +24,7 @@ Q8_BLOCK_BYTES = 34
 Q8_TILE_ROWS = 64
 Q8_GEMV_MAX_ROWS = 8
 Q8_SEQUENCE_MAX_STEPS = 72
+Q8_SEQUENCE_SCRATCH_BYTES = 8 << 20
 Q8_ABI_VERSION = 5
 Q8_NORM_MAX_K = 16384
 Q8_ROUTE_MAX_EXPERTS = 1024
@@ -50,6 +51,7 @@ SIGNATURES = {
     "q8_quantize_matmul": ([_P, _I64, _I64, _P, _I, _I64, _I64, _P, _I64, _P, _SZ, _P], _I),
     "q8_sequence_workspace_bytes": ([_P, _I, _I64], _SZ),
     "q8_quantize_matmul_sequence": ([_P, _I, _I64, _P, _SZ, _P], _I),
+    "q8_quantize_matmul_sequence_noalloc": ([_P, _I, _I64, _P, _P], _I),
     "q8_rmsnorm_quantize": ([_P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P], _I),
     "q8_moe_route": ([_P, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "q8_swiglu_quantize": ([_P, _I64, _P, _I64, _I64, _I64, _P, _P], _I),
@@ -170,6 +172,14 @@ def q8_quantize_matmul_sequence(steps, m: int, workspace, workspace_bytes: int, 
     arr, count = _steps(steps)
     return _check(lib().q8_quantize_matmul_sequence(arr, count, m, _ptr(workspace), workspace_bytes,
                                                     _stream(stream)), "q8_quantize_matmul_sequence")
+
+
+def q8_quantize_matmul_sequence_noalloc(steps, m: int, status=None, stream=None) -> int:
+    """steps: sequence of (x, ld_x, w, n, k, y, ld_y); the library's own
+    per-GPU workspace; status: optional device int32 receiving the status word."""
+    arr, count = _steps(steps)
+    return _check(lib().q8_quantize_matmul_sequence_noalloc(arr, count, m, _ptr(status), _stream(stream)),
+                  "q8_quantize_matmul_sequence_noalloc")
 
 
 def q8_grouped_workspace_bytes(tokens: int, topk: int, n_experts: int, n: int, k: int) -> int:

@@ -73,7 +73,8 @@ extern "C" {
 
 #define Q8_ABI_VERSION 5u  /* 2: q8_gemv_step and the sequence entry points; 3: q8_rmsnorm_quantize, the
                               MoE router, SwiGLU and combine, and the Q8 KV cache entry points;
-                              4: q8_stream_read; 5: q8_device_queries, q8_build_digest */
+                              4: q8_stream_read; 5: q8_device_queries, q8_build_digest,
+                              q8_quantize_matmul_sequence_noalloc */
 #define Q8_BLOCK 32          /* values per block */
 #define Q8_BLOCK_BYTES 34    /* fp16 scale + 32 int8 */
 #define Q8_TILE_ROWS 64      /* rows per packed record */
@@ -224,6 +225,32 @@ size_t q8_sequence_workspace_bytes(const q8_gemv_step *steps, int count, int64_t
  *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
 int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+#define Q8_SEQUENCE_SCRATCH_BYTES (8ll << 20)  /* the allocation-free variant's workspace per GPU */
+
+/* q8_quantize_matmul_sequence without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the workspace is the library's
+ * own device array of Q8_SEQUENCE_SCRATCH_BYTES per GPU, held until the
+ * process ends; no call allocates or frees memory.  Outputs are bit-identical
+ * to q8_quantize_matmul_sequence with the same steps.
+ *  steps, count, m  as for q8_quantize_matmul_sequence, and the same aliasing
+ *            rules; q8_sequence_workspace_bytes(steps, count, m) must not
+ *            exceed Q8_SEQUENCE_SCRATCH_BYTES (else Q8_ERR_WORKSPACE, before
+ *            any HIP call).  The Llama-3.2-1B-shaped decode step needs about
+ *            0.7 MB at m = 1 and 4.4 MB at m = 8.
+ *  status    device int32 or NULL: receives the call's status word (0, or
+ *            Q8_ERR_LAUNCH if an internal wait timed out, which leaves the
+ *            outputs undefined) when the call completes.  4-byte aligned,
+ *            outside every x and y.
+ * The part of the array a call uses is zeroed at the start of every call (by
+ * a kernel, so the call can be captured in a graph).  Every call on one GPU
+ * uses that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialized by the caller.
+ *  Errors: Q8_ERR_ARG, Q8_ERR_SHAPE, Q8_ERR_ALIGN, Q8_ERR_WORKSPACE,
+ *  Q8_ERR_DEVICE, Q8_ERR_LAUNCH. */
+int q8_quantize_matmul_sequence_noalloc(const q8_gemv_step *steps, int count, int64_t m, int32_t *status,
+                                        hipStream_t stream);
 
 /* Fused producer of a GEMM input: residual add + RMSNorm + quantization of
  * each row to Q8_LAYOUT_ACT in one pass ("ferro" README, "How the iGPU path

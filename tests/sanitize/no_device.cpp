@@ -29,6 +29,9 @@ hipError_t launch_gemv_f32(const float *, int64_t, int64_t, const void *, int, i
     return hipErrorNoDevice;
 }
 hipError_t launch_gemv_sequence(const SeqHostStep *, int, int64_t, void *, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_gemv_sequence_scratch(const SeqHostStep *, int, int64_t, int32_t *, hipStream_t) {
+    return hipErrorNoDevice;
+}
 hipError_t launch_rmsnorm_quantize(const float *, const float *, float *, const float *, int64_t, int64_t, float,
                                    void *, hipStream_t) {
     return hipErrorNoDevice;

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     assert sorted(q8.SIGNATURES) == names
     L = ctypes.CDLL(q8.LIB_PATH)
     for n in names:
@@ -213,6 +213,36 @@ def test_sequence_aliasing_is_rejected():
     assert _seq([(A, 4096, B, 2048, 2048, C, 4096), s1m], 2, ws=G, wsb=ws2) == q8.Q8_ERR_DEVICE
     assert _seq([(A, 4096, B, 2048, 2048, E + 4 * 6144, 4096), s1m], 2, ws=G, wsb=ws2) == q8.Q8_ERR_DEVICE  # adjacent
     assert _seq([(A, 4096, B, 2048, 2048, E + 4 * 6144 - 16, 4096), s1m], 2, ws=G, wsb=ws2) == q8.Q8_ERR_ARG
+
+
+def test_sequence_noalloc_validation():
+    """The allocation-free sequence: the same step checks, its workspace limit
+    (Q8_SEQUENCE_SCRATCH_BYTES) and the status pointer are checked on the host."""
+    f = "q8_quantize_matmul_sequence_noalloc"
+
+    def call(steps, m, status=None):
+        arr, count = q8._steps(steps)
+        return _raw(f, arr, count, m, status, None)
+
+    E = 0x7F0000500000
+    o = (A, 2048, B, 2048, 2048, C, 2048)
+    assert call([o], 1) == q8.Q8_ERR_DEVICE                                   # valid: reaches the device check
+    assert call([o], 1, status=E) == q8.Q8_ERR_DEVICE
+    assert call([o], 1, status=E + 2) == q8.Q8_ERR_ALIGN
+    assert call([o], 1, status=C + 64) == q8.Q8_ERR_ARG                       # status inside a y
+    assert call([o, (C, 2048, B, 2048, 2048, E, 2048)], 1) == q8.Q8_ERR_ARG   # y_0 == x_1
+    assert call([], 1) == q8.Q8_ERR_ARG
+    assert call([o], 9) == q8.Q8_ERR_SHAPE
+    # 72 down-shaped steps at m = 8 need ~18.9 MB of workspace: beyond the limit
+    big = [(A + i * 0x100000, 8192, B, 2048, 8192, 0x7F1000000000 + i * 0x100000, 2048) for i in range(72)]
+    assert q8.q8_sequence_workspace_bytes(big, 8) > q8.Q8_SEQUENCE_SCRATCH_BYTES
+    assert call(big, 8) == q8.Q8_ERR_WORKSPACE
+    # the Llama-3.2-1B-shaped decode step fits at every m <= 8
+    layer = [(A, 2048, B, 3072, 2048, C, 3072), (A, 2048, B, 2048, 2048, C, 2048),
+             (A, 2048, B, 16384, 2048, C, 16384), (A, 8192, B, 2048, 8192, C, 2048)]
+    step = layer * 16 + [(A, 2048, B, 128256, 2048, C, 128256)]
+    for m in range(1, 9):
+        assert q8.q8_sequence_workspace_bytes(step, m) <= q8.Q8_SEQUENCE_SCRATCH_BYTES
 
 
 def test_stale_library_is_refused(monkeypatch):
