@@ -38,7 +38,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(const ACT *__restrict__ xq, i
                                                    float *__restrict__ part) {
     extern __shared__ float lds_u[];  // [groups of this workgroup][M][64]
     __shared__ int last_wg;
-    tile_unit<M, LAYOUT, ACT, ONE>(xq, ld_x, xs, w, n, k, y, ld_y, (int64_t)blockIdx.y, (int)blockIdx.x,
+    tile_unit<M, LAYOUT, ACT, ONE, GEMV_MF_MIN_ROWS>(xq, ld_x, xs, w, n, k, y, ld_y, (int64_t)blockIdx.y, (int)blockIdx.x,
                                    (int)gridDim.x, segs_per_wg, ctr, part, lds_u, &last_wg, false, NoWait());
 }
 

@@ -217,6 +217,233 @@ __device__ __forceinline__ void row_groups(const uint8_t *wbase, int64_t gstride
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA form of a group, for 2..8 activation rows and packed weights.  The
+// block dots of all M activation rows with the tile's 64 weight rows come from
+// v_mfma_i32_32x32x32_i8 (one instruction = one block for 32 weight rows; the
+// activation rows sit on the instruction's other 32-row side, padded), so the
+// VALU no longer broadcasts every activation code to every lane.  Each output
+// keeps exactly the arithmetic of the lane-per-row form -- s exact, t =
+// fp32(s) * (Dw * Dx) with Dw * Dx exact, the tree over the group's 8 blocks
+// -- so its bits do not depend on which form computed it (rows stay
+// bit-identical to m = 1).
+// Register form: lane l holds, for block bb and weight-row half th, the 16
+// values 16 * (l / 32) .. + 15 of block bb of weight row 32 * th + l % 32 (the
+// instruction's B operand), and the scale chunks of rows l % 32 and
+// 32 + l % 32.  Output: lane l holds weight row 32 * th + l % 32 for the
+// activation rows 4 * (l / 32) + p, p = 0..3 (instruction registers 0..3).
+// ---------------------------------------------------------------------------
+struct GroupRegsMF {
+    uint4 c[18];
+};
+
+__device__ __forceinline__ void load_group_mf(GroupRegsMF &g, const uint8_t *rec, int lane) {
+    const uint8_t *p = rec + (lane >> 5) * 1024 + (lane & 31) * 16;
+#pragma unroll
+    for (int bb = 0; bb < GROUP_BLOCKS; bb++)
+#pragma unroll
+        for (int th = 0; th < 2; th++) g.c[2 * bb + th] = *reinterpret_cast<const uint4 *>(p + bb * 2048 + th * 512);
+#pragma unroll
+    for (int th = 0; th < 2; th++)
+        g.c[16 + th] = *reinterpret_cast<const uint4 *>(rec + RECORD_Q_BYTES + (32 * th + (lane & 31)) * 16);
+}
+
+// Per-wave LDS scratch of the MFMA form: the M rows' packed codes as the lanes
+// quantized them ([m][64] dwords) and the activation scales ([block][8]
+// floats, Dx of row m at [bb * 8 + m]).
+template <int M>
+struct MfScratch {
+    static constexpr int DWORDS = M * 64 + GROUP_BLOCKS * 8;
+};
+
+// u[th][p] = the group sum of weight row 32 * th + lane % 32 with activation
+// row 4 * (lane / 32) + p (meaningful for rows < M).  src.a(bb) gives the A
+// operand of block bb (16 activation codes of row lane % 32, values
+// 16 * (lane / 32) ..) and src.dx(bb, d) the activation scales of rows
+// 4 * (lane / 32) + p; they are fetched block by block so that few registers
+// are live.  The tree over the group's blocks is built as the blocks arrive,
+// with the association of tree8.
+template <int M, typename Src>
+__device__ __forceinline__ void group_sums_mf(const GroupRegsMF &g, const Src &src, float (&u)[2][4]) {
+    // Block by block: the block's A operand and activation scales are fetched
+    // one block ahead, its two MFMAs (weight rows 0..31 and 32..63) issued
+    // together, and the epilogue pinned in place, so that few registers are
+    // live (left alone, the compiler issues all 16 MFMAs first and keeps every
+    // result register).  Only the activation rows a lane half can hold are
+    // computed: rows 4 * (lane / 32) + p, p < min(M, 4).
+    constexpr int P = M < 4 ? M : 4;
+    const v16i zi = {0};
+    float x0[2][P], p01[2][P], x2[2][P], q03[2][P], x4[2][P], p45[2][P], x6[2][P];
+    v4i a_cur = src.a(0), a_nxt = a_cur;
+    float dx_cur[4], dx_nxt[4];
+    src.dx(0, dx_cur);
+#pragma unroll
+    for (int bb = 0; bb < GROUP_BLOCKS; bb++) {
+        if (bb + 1 < GROUP_BLOCKS) {
+            a_nxt = src.a(bb + 1);
+            src.dx(bb + 1, dx_nxt);
+        }
+        v16i sv[2];
+#pragma unroll
+        for (int th = 0; th < 2; th++)
+            sv[th] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_cur, __builtin_bit_cast(v4i, g.c[2 * bb + th]), zi, 0, 0, 0);
+#pragma unroll
+        for (int th = 0; th < 2; th++) {
+            const float dw = half_bits_to_float(half_of(g.c[16 + th], bb));
+#pragma unroll
+            for (int p = 0; p < P; p++) {
+                const float t = (float)sv[th][p] * (dw * dx_cur[p]);  // Dw * Dx exact: one rounding
+                float *pin;
+                switch (bb) {  // ((t0 + t1) + (t2 + t3)) + ((t4 + t5) + (t6 + t7))
+                    case 0: x0[th][p] = t; pin = &x0[th][p]; break;
+                    case 1: p01[th][p] = x0[th][p] + t; pin = &p01[th][p]; break;
+                    case 2: x2[th][p] = t; pin = &x2[th][p]; break;
+                    case 3: q03[th][p] = p01[th][p] + (x2[th][p] + t); pin = &q03[th][p]; break;
+                    case 4: x4[th][p] = t; pin = &x4[th][p]; break;
+                    case 5: p45[th][p] = x4[th][p] + t; pin = &p45[th][p]; break;
+                    case 6: x6[th][p] = t; pin = &x6[th][p]; break;
+                    default: u[th][p] = q03[th][p] + (p45[th][p] + (x6[th][p] + t)); pin = &u[th][p]; break;
+                }
+                asm volatile("" : "+v"(*pin) :: "memory");
+            }
+        }
+        a_cur = a_nxt;
+#pragma unroll
+        for (int p = 0; p < 4; p++) dx_cur[p] = dx_nxt[p];
+    }
+}
+
+// Operands of the fp32 path: the wave's scratch, filled by quantize_group.
+template <int M>
+struct ScratchOperands {
+    const uint32_t *scr;
+    int lane;
+    __device__ __forceinline__ v4i a(int bb) const {
+        const int mm = (lane & 31) < M ? (lane & 31) : M - 1;
+        return *reinterpret_cast<const v4i *>(scr + mm * 64 + 8 * bb + 4 * (lane >> 5));
+    }
+    __device__ __forceinline__ void dx(int bb, float (&d)[4]) const {
+        const float4 d4 = *reinterpret_cast<const float4 *>(scr + M * 64 + bb * 8 + 4 * (lane >> 5));
+        d[0] = d4.x;
+        d[1] = d4.y;
+        d[2] = d4.z;
+        d[3] = d4.w;
+    }
+};
+
+// The lanes' quantization of a group of M fp32 activation rows (xv[m]: lane
+// l's values 4l..4l+3, exactly the arithmetic of group_sums_f32) into the
+// wave's scratch: packed codes of row m at [m * 64 + l], the fp32 value of
+// each block's stored fp16 scale at [M * 64 + bb * 8 + m].
+template <int M>
+__device__ __forceinline__ void quantize_group(const float4 (&xv)[M], uint32_t *scr, int lane) {
+    // every lane has read the previous group's operands before they are overwritten
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float *sdx = reinterpret_cast<float *>(scr + M * 64);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const float4 v = xv[m];
+        const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        const float d = amax / 127.0f;
+        int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+        if (d != 0.0f) {
+            q0 = (int)roundf(v.x / d);
+            q1 = (int)roundf(v.y / d);
+            q2 = (int)roundf(v.z / d);
+            q3 = (int)roundf(v.w / d);
+        }
+        scr[m * 64 + lane] = ((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
+                             ((uint32_t)q3 << 24);
+        if ((lane & 7) == 0) sdx[(lane >> 3) * 8 + m] = half_bits_to_float(float_to_half_bits(d));
+    }
+    // the wave's own LDS writes complete before its lanes read each other's
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Operands of the int8 path (Q8_LAYOUT_ACT already quantized): codes of row
+// min(lane % 32, M - 1) straight from memory; the scale chunks of rows
+// 4 * (lane / 32) + p (clamped to M - 1) loaded once per group.
+template <int M>
+struct ActOperands {
+    const int8_t *xr;  // this lane's activation row at the group, + 16 * (lane / 32)
+    uint4 sc[4];
+    __device__ __forceinline__ void init(const int8_t *x0, int64_t ld_x, const uint16_t *s0, int64_t nb, int g,
+                                         int lane) {
+        const int mm = (lane & 31) < M ? (lane & 31) : M - 1;
+        xr = x0 + mm * ld_x + g * GROUP_K + 16 * (lane >> 5);
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            int r = 4 * (lane >> 5) + p;
+            r = r < M ? r : M - 1;
+            sc[p] = *reinterpret_cast<const uint4 *>(s0 + r * nb + g * GROUP_BLOCKS);
+        }
+    }
+    __device__ __forceinline__ v4i a(int bb) const { return *reinterpret_cast<const v4i *>(xr + bb * QK); }
+    __device__ __forceinline__ void dx(int bb, float (&d)[4]) const {
+#pragma unroll
+        for (int p = 0; p < 4; p++) d[p] = half_bits_to_float(half_of(sc[p], bb));
+    }
+};
+
+// row_groups for the MFMA form (packed weights, group sums to LDS): groups
+// g0, g0 + step, ... (< g1) of the tile whose record 0 is at rec0; each
+// group's sums go to lds[((g - g0) * M + m) * 64 + row].  xf (fp32 rows, ACT =
+// float) or xq / xs (int8 rows and scales) give the activations; scr is the
+// wave's MfScratch.  Hooks as in row_groups.
+template <int M, typename ACT, bool ONE, typename Wait>
+__device__ __forceinline__ void row_groups_mf(const uint8_t *rec0, int g0, int g1, int step, const ACT *x0,
+                                              int64_t ld_x, const uint16_t *xs0, int64_t nb, float *lds,
+                                              uint32_t *scr, int lane, Wait &&hooks) {
+    constexpr bool F32 = sizeof(ACT) == 4;
+    GroupRegsMF cur, nxt;
+    float4 xv[M], xn[M];
+    const bool any = g0 < g1;
+    hooks.before();
+    if (any) load_group_mf(cur, rec0 + (int64_t)g0 * RECORD_BYTES, lane);
+    hooks();
+    if constexpr (F32) {
+        if (any) {
+#pragma unroll
+            for (int m = 0; m < M; m++)
+                xv[m] = *reinterpret_cast<const float4 *>(x0 + m * ld_x + g0 * GROUP_K + 4 * lane);
+        }
+    }
+    hooks.after();
+    if (!any) return;
+    for (int g = g0; g < g1; g += step) {
+        if (!ONE && g + step < g1) {
+            if constexpr (F32) {
+#pragma unroll
+                for (int m = 0; m < M; m++)
+                    xn[m] = *reinterpret_cast<const float4 *>(x0 + m * ld_x + (g + step) * GROUP_K + 4 * lane);
+            }
+            load_group_mf(nxt, rec0 + (int64_t)(g + step) * RECORD_BYTES, lane);
+        }
+        float u[2][4];
+        if constexpr (F32) {
+            quantize_group<M>(xv, scr, lane);
+            group_sums_mf<M>(cur, ScratchOperands<M>{scr, lane}, u);
+        } else {
+            ActOperands<M> src;
+            src.init((const int8_t *)x0, ld_x, xs0, nb, g, lane);
+            group_sums_mf<M>(cur, src, u);
+        }
+#pragma unroll
+        for (int th = 0; th < 2; th++)
+#pragma unroll
+            for (int p = 0; p < (M < 4 ? M : 4); p++) {
+                const int m = 4 * (lane >> 5) + p;
+                if (m < M) lds[((g - g0) * M + m) * TILE_ROWS + 32 * th + (lane & 31)] = u[th][p];
+            }
+        if (ONE) break;
+        cur = nxt;
+        if constexpr (F32) {
+#pragma unroll
+            for (int m = 0; m < M; m++) xv[m] = xn[m];
+        }
+    }
+}
+
 struct NoWait {
     __device__ void before() const {}
     __device__ void operator()() const {}
@@ -246,9 +473,11 @@ struct NoWait {
 // workgroup only leaves its segment sums (complete when it returns) for a
 // later finish_split (the sequence kernel's next step chains them).  Every
 // thread of the workgroup calls this (it contains barriers); lds_u holds
-// [groups of the workgroup][M][64] floats.  Workspace: uint32 counters [tiles]
+// [groups of the workgroup][M][64] floats, followed by the waves' MFMA-form
+// scratch when M >= MF_MIN (packed weights take the MFMA form from MF_MIN
+// activation rows on: the choice changes speed only, never bits).  Workspace: uint32 counters [tiles]
 // (256-byte aligned), then fp32 segment sums [S][M][n].
-template <int M, int LAYOUT, typename ACT, bool ONE, typename Wait>
+template <int M, int LAYOUT, typename ACT, bool ONE, int MF_MIN, typename Wait>
 __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld_x, const uint16_t *__restrict__ xs,
                                           const uint8_t *__restrict__ w, int64_t n, int64_t k, float *__restrict__ y,
                                           int64_t ld_y, int64_t T, int wi, int wgs_per_tile, int segs_per_wg,
@@ -273,10 +502,19 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
     }
     const uint8_t *wbase = LAYOUT == 1 ? w + T * G * RECORD_BYTES + lane * 16 : w + row_c * (k / QK) * BLOCK_BYTES;
     const int64_t gstride = LAYOUT == 1 ? RECORD_BYTES : ROW_GROUP_BYTES;
-    float unused[M];
     // wave wv takes the workgroup's groups ga + wv, ga + wv + W, ...; each sum lands in its group's LDS slot
-    row_groups<M, LAYOUT, true, ACT, ONE>(wbase, gstride, ga + wv, gb, W, xrow, srow, unused,
-                                          lds_u + wv * M * TILE_ROWS, lane, hooks);
+    if constexpr (M >= MF_MIN && LAYOUT == 1) {
+        // MFMA form; the waves' scratch follows the group slots (the plan's
+        // LDS holds min(segs_per_wg * 8, G) slots of M x 64 floats)
+        const int slots = segs_per_wg * SEG_GROUPS < G ? segs_per_wg * SEG_GROUPS : G;
+        uint32_t *scr = reinterpret_cast<uint32_t *>(lds_u + slots * M * TILE_ROWS) + wv * MfScratch<M>::DWORDS;
+        row_groups_mf<M, ACT, ONE>(w + T * G * RECORD_BYTES, ga + wv, gb, W, xq, ld_x, xs, k / QK,
+                                   lds_u + wv * M * TILE_ROWS, scr, lane, hooks);
+    } else {
+        float unused[M];
+        row_groups<M, LAYOUT, true, ACT, ONE>(wbase, gstride, ga + wv, gb, W, xrow, srow, unused,
+                                              lds_u + wv * M * TILE_ROWS, lane, hooks);
+    }
     __syncthreads();
 
     const int t = threadIdx.x;  // the plan gives at least M waves: one thread per (m, row)

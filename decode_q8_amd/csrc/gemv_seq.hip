@@ -202,7 +202,8 @@ gemv_sequence_kernel(const SeqArgs a) {
         for (int u = first; u < units; u += nwg) {
             const int T = u / st.wgs, wi = u - T * st.wgs;
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // previous unit's LDS reads done
-            tile_unit<M, 1, float, ONE>(st.x, st.ld_x, nullptr, st.w, st.n, st.k, st.y, st.ld_y, T, wi, st.wgs,
+            tile_unit<M, 1, float, ONE, SEQ_MF_MIN_ROWS>(st.x, st.ld_x, nullptr, st.w, st.n, st.k, st.y, st.ld_y, T, wi,
+                                                        st.wgs,
                                         st.segs, ctr, part, lds_u, &last_wg, handover,
                                         SeqHooks<M>{a, p, wg, u, units, ready, prev_p >= 0 && p > prev_p + 1,
                                                     __builtin_amdgcn_s_memrealtime(), status});

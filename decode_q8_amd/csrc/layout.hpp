@@ -22,6 +22,14 @@ constexpr int SEG_GROUPS = 8;     // groups per summation segment (2048 values)
 // LDS must fit in 64 KB
 constexpr int GEMV_MAX_WAVES = 8;
 constexpr int64_t GEMV_LDS_LIMIT = 64 * 1024;
+// Activation rows from which a GEMV on packed weights takes the MFMA form
+// (the int8 block dots of all rows from one MFMA per block and 32 weight
+// rows) instead of a lane per weight row with every activation code
+// broadcast: from 4 rows in the per-matrix kernel, from 6 in the sequence
+// kernel, whose 128-register cap makes the MFMA form spill below that
+// (measured; only speed depends on it).
+constexpr int GEMV_MF_MIN_ROWS = 4;
+constexpr int SEQ_MF_MIN_ROWS = 6;
 
 // Sequence workspace: [0, 4) status word; from byte 256 SEQ_CTR_PER_STEP
 // counters of SEQ_CTR_LINE bytes per step (the step's counter, then its

@@ -4,6 +4,8 @@
 #include "launch.hpp"
 #include "layout.hpp"
 
+static_assert(q8k::SEQ_MF_MIN_ROWS >= q8k::GEMV_MF_MIN_ROWS, "the plan reserves scratch from GEMV_MF_MIN_ROWS");
+
 namespace q8k {
 
 // Execution plan of a GEMV.  Only speed depends on it; every plan produces
@@ -35,6 +37,11 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k) {
     if (waves < m) waves = m;
     p.waves = (int)waves;
     p.lds = (size_t)(gpw * m * TILE_ROWS) * sizeof(float);
+    // the MFMA form (packed weights, m >= GEMV_MF_MIN_ROWS): each of up to 8
+    // waves keeps the group's m rows of packed codes (m x 64 dwords) and 8 x 8
+    // activation scales after the group slots
+    if (m >= GEMV_MF_MIN_ROWS && m >= 2)
+        p.lds += (size_t)GEMV_MAX_WAVES * (m * 64 + GROUP_BLOCKS * 8) * sizeof(uint32_t);
     p.workspace = 0;
     if (wgs > 1) p.workspace = (size_t)((p.tiles * 4 + 255) / 256 * 256) + (size_t)(S * m * n) * sizeof(float);
     return p;
