@@ -177,11 +177,14 @@ struct SeqHooks {
     }
 };
 
-// ONE (at most one group per wave): at most 128 VGPRs, so that two 512-thread
-// workgroups fit on a CU for every m (m >= 4 then spills a few registers,
-// which costs less than halving the workgroups that stream and compute).
+// ONE (at most one group per wave), lane form (m below SEQ_MF_MIN_ROWS): at
+// most 128 VGPRs, so that two 512-thread workgroups fit on a CU.  The MFMA
+// form (m >= SEQ_MF_MIN_ROWS) keeps up to 256 VGPRs and one workgroup per CU:
+// capped at 128 it spilled ~190 bytes per lane, and the reloads on each
+// step's critical path cost more than the halved grid (m = 8: 906 -> 698 us
+// per decode step).
 template <int M, bool ONE>
-__global__ __launch_bounds__(SEQ_THREADS) __attribute__((amdgpu_waves_per_eu(ONE ? 4 : 1, 8))) void
+__global__ __launch_bounds__(SEQ_THREADS) __attribute__((amdgpu_waves_per_eu(ONE && M < SEQ_MF_MIN_ROWS ? 4 : 1, 8))) void
 gemv_sequence_kernel(const SeqArgs a) {
     extern __shared__ float lds_u[];  // [groups of a unit][M][64]
     __shared__ int last_wg;

@@ -25,11 +25,12 @@ constexpr int64_t GEMV_LDS_LIMIT = 64 * 1024;
 // Activation rows from which a GEMV on packed weights takes the MFMA form
 // (the int8 block dots of all rows from one MFMA per block and 32 weight
 // rows) instead of a lane per weight row with every activation code
-// broadcast: from 4 rows in the per-matrix kernel, from 6 in the sequence
-// kernel, whose 128-register cap makes the MFMA form spill below that
-// (measured; only speed depends on it).
-constexpr int GEMV_MF_MIN_ROWS = 4;
-constexpr int SEQ_MF_MIN_ROWS = 6;
+// broadcast: from 3 rows in the per-matrix kernel and from 4 in the sequence
+// kernel, where the MFMA form runs with up to 256 registers (one workgroup per
+// CU, no spills) and the lane form with 128 (two per CU).  Measured; only
+// speed depends on it.
+constexpr int GEMV_MF_MIN_ROWS = 3;
+constexpr int SEQ_MF_MIN_ROWS = 4;
 
 // Sequence workspace: [0, 4) status word; from byte 256 SEQ_CTR_PER_STEP
 // counters of SEQ_CTR_LINE bytes per step (the step's counter, then its
