@@ -253,6 +253,36 @@ __device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const L
         for (int r = 0; r < 16; r++) acc[j][r] += ga[j][r];
 }
 
+// Output tile of this workgroup, XCD-aware.  A launch's workgroups go to the
+// 8 XCDs round-robin by linear id, and each XCD has its own L2.  The tiles are
+// put in a grouped order -- XCD_GROUP_M row blocks at a time, all column
+// blocks of the group, the row blocks fastest -- and XCD x takes the x-th
+// eighth of that order, so the workgroups one XCD runs at the same time
+// cover a compact block of rows and columns and share their operand stages in
+// its L2 (with the plain order, one XCD would hold every row block of a few
+// column blocks and stream all of A through its L2).  Grids whose tile count
+// is not a multiple of 8 keep the plain order.  Only speed depends on this.
+constexpr int XCDS = 8;
+constexpr int XCD_GROUP_M = 4;
+
+__device__ __forceinline__ void xcd_tile(int &tm, int &tn) {
+    const int tiles_n = gridDim.x, tiles_m = gridDim.y;
+    const int total = tiles_n * tiles_m;
+    const int id = blockIdx.x + tiles_n * blockIdx.y;
+    if (total % XCDS) {
+        tn = blockIdx.x;
+        tm = blockIdx.y;
+        return;
+    }
+    const int t = (id % XCDS) * (total / XCDS) + id / XCDS;  // position in the grouped order
+    const int per_group = XCD_GROUP_M * tiles_n;
+    const int first_m = (t / per_group) * XCD_GROUP_M;
+    const int gm = tiles_m - first_m < XCD_GROUP_M ? tiles_m - first_m : XCD_GROUP_M;
+    const int r = t % per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
 template <int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__restrict__ xq,
                                                              const uint16_t *__restrict__ xs, int64_t M,
@@ -265,9 +295,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
     const int wm = wave % WM, wn = wave / WM;  // 32-row strip wm of packed tile wn
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t tiles = N / TILE_ROWS;
-    const int64_t T0 = (int64_t)blockIdx.x * WN;  // the workgroup's first packed weight tile
+    int tm, tn;  // the workgroup's output tile (row block, column block)
+    xcd_tile(tm, tn);
+    const int64_t T0 = (int64_t)tn * WN;  // the workgroup's first packed weight tile
     const int64_t G = K / GROUP_K, S = 2 * G;
-    const int64_t m_tile = (int64_t)blockIdx.y * T::ROWS;
+    const int64_t m_tile = (int64_t)tm * T::ROWS;
     const bool ragged = T0 + WN > tiles;
     StageLoads<WM, WN> sl;
     // tiles past the last one (N not a multiple of the workgroup's columns) reload the last tile
