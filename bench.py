@@ -135,6 +135,11 @@ def hbm_roofline(kernel, bytes_per_launch, avg_ms):
     }
 
 
+# Kernel sources whose sha256 a committed profile summary must match before its
+# counter-derived traffic is reported.
+SEQ_SOURCES = ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp", "decode_q8_amd/csrc/layout.hpp"]
+GEMM_SOURCES = "decode_q8_amd/csrc/gemm.hip"
+
 # Spread of the per-replay times of the most recent graph_time call (ms at the
 # 10th, 50th and 90th percentile), reported beside the mean in every record.
 STEP_SPREAD = {}
@@ -263,11 +268,11 @@ def profiled_field(profile: str, source, key: str):
     return float(fields[key])
 
 
-def profiled_traffic(profile: str, source: str):
-    """HBM bytes per launch recorded in profiles/<profile> by the rocprofv3
-    FETCH_SIZE / WRITE_SIZE runs, if that summary was taken from the current
-    kernel source (the sha256 of the source file, or of the listed files
-    concatenated, matches); otherwise None."""
+def profiled_traffic(profile: str, source, key: str = "traffic_bytes_per_launch"):
+    """HBM bytes per launch recorded in profiles/<profile> (field `key`) by the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if that summary was taken from the
+    current kernel source (the sha256 of the source file, or of the listed
+    files concatenated, matches); otherwise None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
@@ -275,16 +280,16 @@ def profiled_traffic(profile: str, source: str):
     fields = {}
     for line in open(path):
         if ":" in line:
-            key, val = line.split(":", 1)
-            fields[key.strip()] = val.strip()
+            name, val = line.split(":", 1)
+            fields[name.strip()] = val.strip()
     sources = [source] if isinstance(source, str) else list(source)
     h = hashlib.sha256()
     for src in sources:
         h.update(open(os.path.join(ROOT, src), "rb").read())
     sha = h.hexdigest()
-    if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("source_sha256") != sha or key not in fields:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return int(fields[key])
 
 
 def sequence_ms(run, stream, g_filler, reps):
@@ -537,8 +542,7 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
         roof = hbm_roofline(kname, float(gemv_bytes.sum()), seq_ms)
         roof["timing"] = "one event pair around the step's single launch, queued ahead"
         if m == 1 and len(mats) == 65:
-            roof["traffic"] = profiled_traffic("gemv_sequence_decode_step_llama1b.txt",
-                                               ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
+            roof["traffic"] = profiled_traffic("gemv_sequence_decode_step_llama1b.txt", SEQ_SOURCES)
     else:
         kname = "q8k::gemv_kernel<%d, %s, %s>" % (m, args.layout, "fp32 in" if step.fused else "int8 in")
         avg_ms = seq_ms if seq_ms is not None else float(gemv_ms.mean())
@@ -665,13 +669,15 @@ def prefill_measure(args):
         kname = gemm_kernel_for(c["m"], c["n"])
         o, t, names = kernels.get(kname, (0.0, 0.0, []))
         kernels[kname] = (o + ops[i], t + ms[i], names + [f"M{c['m']}_N{c['n']}_K{c['k']}"])
-    mfma_busy = profiled_field("gemm_prefill_counters.txt", "decode_q8_amd/csrc/gemm.hip", "mfma_busy_pct")
+    mfma_busy = profiled_field("gemm_prefill_counters.txt", GEMM_SOURCES, "mfma_busy_pct")
     rooflines = {}
     for kname, (o, t, names) in kernels.items():
         achieved = o / (t * 1e-3) / 1e12
+        tkey = "traffic_bytes_per_launch_" + ("tiled" if kname.startswith("gemm_kernel") else "strip")
         rooflines[kname] = {"kernel": "q8k::" + kname, "bound": "mfma", "achieved": round(achieved, 1),
                             "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4),
-                            "traffic": None, "avg_launch_us": round(t / len(names) * 1e3, 3),
+                            "traffic": profiled_traffic("gemm_prefill.txt", GEMM_SOURCES, tkey),
+                            "avg_launch_us": round(t / len(names) * 1e3, 3),
                             "algorithmic_ops_per_launch": int(o / len(names)), "shapes": names,
                             "timing": "one event pair per launch on the launch stream, queued ahead; "
                                       "achieved = total ops / total duration over its shapes"}
@@ -707,7 +713,6 @@ def bench_prefill(args):
     p = prefill_measure(args)
     tiled = p["rooflines"].get("gemm_kernel<4, 2>")
     roof = dict(tiled) if tiled else dict(next(iter(p["rooflines"].values())))
-    roof["traffic"] = profiled_traffic("gemm_prefill.txt", "decode_q8_amd/csrc/gemm.hip")
     roof["mfma_busy_pct"] = p["mfma_busy_pct"]
     config = {"workload": p["workload"], "ops_per_step": p["ops_per_step"],
               "frac_of_int8_peak": p["frac_of_int8_peak"], "tops_by_case": p["tops_by_case"],
