@@ -138,7 +138,7 @@ def hbm_roofline(kernel, bytes_per_launch, avg_ms):
 # Kernel sources whose sha256 a committed profile summary must match before its
 # counter-derived traffic is reported.
 SEQ_SOURCES = ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp", "decode_q8_amd/csrc/layout.hpp"]
-GEMM_SOURCES = "decode_q8_amd/csrc/gemm.hip"
+GEMM_SOURCES = ["decode_q8_amd/csrc/gemm.hip", "decode_q8_amd/csrc/gemm_loop.inc"]
 
 # Spread of the per-replay times of the most recent graph_time call (ms at the
 # 10th, 50th and 90th percentile), reported beside the mean in every record.
@@ -600,7 +600,7 @@ def gemm_kernel_for(m: int, n: int) -> str:
     """The GEMM kernel libq8 runs for an m x n output (its rule: 128 x 128
     workgroup tiles when there are at least 256 of them, else 32 x 64 strips
     with k split across the waves)."""
-    return "gemm_kernel<4, 2>" if ((m + 127) // 128) * ((n + 127) // 128) >= 256 else "gemm_strip_kernel"
+    return "gemm_kernel" if ((m + 127) // 128) * ((n + 127) // 128) >= 256 else "gemm_strip_kernel"
 
 
 PREFILL_ORDER_SEED = 20261202
@@ -711,7 +711,7 @@ def prefill_measure(args):
 
 def bench_prefill(args):
     p = prefill_measure(args)
-    tiled = p["rooflines"].get("gemm_kernel<4, 2>")
+    tiled = p["rooflines"].get("gemm_kernel")
     roof = dict(tiled) if tiled else dict(next(iter(p["rooflines"].values())))
     roof["mfma_busy_pct"] = p["mfma_busy_pct"]
     config = {"workload": p["workload"], "ops_per_step": p["ops_per_step"],

@@ -16,17 +16,17 @@
 // the staging of the operands through LDS.
 //
 // Tiling: each wave owns a 32 x 64 output strip (1 x 2 MFMA tiles); a
-// workgroup of WM x WN = 4 x 2 waves owns a 128 x 128 tile when the problem
-// has at least 256 such tiles; smaller problems run gemm_strip_kernel below
-// (32 x 64 strips, k split across 8 waves).  The k loop runs in stages of 4
-// blocks (128 values).  Stages move
-// from HBM straight into LDS with global_load_lds_dwordx4 / _dword (no
-// register staging), NS = 4 stages deep, so three stages are in flight while
-// one is computed.  Every wave issues exactly LOADS_PER_STAGE such loads per
-// stage; loads return in issue order, so "stage s has landed" is a vmcnt
-// threshold, followed by one barrier per stage.  The k order inside one MFMA
-// is the same for both operands (lane half h holds values 16h..16h+15 of the
-// block), which is all an exact integer dot needs.
+// workgroup of 4 x 2 waves owns a 128 x 128 tile when the problem has at
+// least 256 such tiles; smaller problems run gemm_strip_kernel below (32 x 64
+// strips, k split across 8 waves).  The 128 x 128 kernel's k loop is the
+// generated inline-asm block of gemm_loop.inc (explicit registers and
+// schedule): stages of 4 blocks (128 values) move from HBM straight into LDS
+// with global_load_lds_dwordx4 / _dword (no register staging), four stages
+// resident; every wave issues the same 5 loads per stage, so "stage s has
+// landed" is a vmcnt threshold, followed by one barrier per stage; operand
+// reads and MFMAs run one block ahead of the epilogue.  The k order inside
+// one MFMA is the same for both operands (lane half h holds values
+// 16h..16h+15 of the block), which is all an exact integer dot needs.
 //
 // LDS stage layout (128 x 128: 34 KB, NS = 4 stages = 136 KB of gfx950's
 // 160 KB):
@@ -36,6 +36,7 @@
 //   SX  activation scales [row][4 blocks]
 //   SW  weight scales [tile][row][4 blocks]
 #include "device.hpp"
+#include "gemm_loop.inc"
 #include "launch.hpp"
 
 namespace q8k {
@@ -71,188 +72,6 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
-// Operand of the rank-1 scale MFMA: the lane's fp16 scale in k = 0, zeros in
-// k = 1..3.  One v_mfma_f32_32x32x4_2b_f16 then yields the scale products
-// Dx * Dw of both 32 x 32 tiles of a wave (block 0 of the instruction: lanes
-// 0..31, tile 0; block 1: lanes 32..63, tile 1), each in the register layout of
-// the i8 MFMA's output.
-__device__ __forceinline__ v4h rank1_operand(const uint8_t *p) {
-    const v2u v = {(uint32_t)*reinterpret_cast<const uint16_t *>(p), 0u};
-    return __builtin_bit_cast(v4h, v);
-}
-
-// This wave's PER_WAVE direct-to-LDS loads of a stage (load i of a stage goes
-// to wave i % WAVES).  Each load writes 64 lanes x size bytes contiguously
-// from a wave-uniform LDS offset; the lane decides which global bytes it
-// fetches.  Every address is this lane's stage-0 address plus a wave-uniform
-// offset of the stage, (s >> 1) * p + (s & 1) * q (two stages per 256-value
-// group; the weight records of group s / 2 are RECORD_BYTES apart), so a
-// stage costs one 64-bit add per load instead of the address arithmetic.
-template <int WM, int WN>
-struct StageLoads {
-    using T = Tile<WM, WN>;
-    const uint8_t *g[T::PER_WAVE];  // this lane's global address in stage 0
-    int lds[T::PER_WAVE];           // offset in the stage buffer (wave-uniform)
-    int p[T::PER_WAVE], q[T::PER_WAVE];
-    bool wide[T::PER_WAVE];         // 16-byte loads (operands), else 4-byte (scales)
-
-    // Stage 0 of the workgroup at output rows m_tile.. and packed tiles from
-    // w_tiles (tile_stride bytes apart; 0: one tile, reloaded).  Activation
-    // rows past M read row M - 1 (their outputs are not stored).
-    __device__ __forceinline__ void init(const int8_t *xq, const uint16_t *xs, int64_t M, int64_t m_tile,
-                                         const uint8_t *w_tiles, int64_t tile_stride, int64_t K, int64_t nb, int wave,
-                                         int lane) {
-#pragma unroll
-        for (int u = 0; u < T::PER_WAVE; u++) {
-            int i = wave + T::WAVES * u;
-            i = i < T::LOADS ? i : T::LOADS - 1;  // a wave short of work repeats the last load
-            if (i < T::NA) {  // activations: 8 rows x 128 bytes, row r's chunk c at position c ^ (r & 7)
-                const int r = 8 * i + (lane >> 3);
-                const int c = (lane & 7) ^ (lane >> 3);
-                int64_t row = m_tile + r;
-                row = row < M ? row : M - 1;
-                g[u] = reinterpret_cast<const uint8_t *>(xq + row * K + c * 16);
-                lds[u] = i * 1024;
-                p[u] = 2 * SB * QK;
-                q[u] = SB * QK;
-                wide[u] = true;
-            } else if (i < T::NA + T::NB) {  // weights: a tile's 4 block records are 8 KB contiguous
-                const int e = i - T::NA;
-                g[u] = w_tiles + (e >> 3) * tile_stride + (e & 7) * 1024 + lane * 16;
-                lds[u] = T::A_BYTES + e * 1024;
-                p[u] = RECORD_BYTES;
-                q[u] = SB * 2048;
-                wide[u] = true;
-            } else if (i < T::NA + T::NB + T::NSX) {  // activation scales [row][4], 4 bytes per lane
-                const int e = i - T::NA - T::NB;
-                const int d = e * 64 + lane;
-                int64_t row = m_tile + (d >> 1);
-                row = row < M ? row : M - 1;
-                g[u] = reinterpret_cast<const uint8_t *>(xs + row * nb + 2 * (d & 1));
-                lds[u] = T::SX_OFF + e * 256;
-                p[u] = 2 * SB * 2;
-                q[u] = SB * 2;
-                wide[u] = false;
-            } else {  // weight scales [tile][row][4], 4 bytes per lane
-                const int e = i - T::NA - T::NB - T::NSX;
-                const int d = e * 64 + lane;
-                g[u] = w_tiles + (d >> 7) * tile_stride + RECORD_Q_BYTES + ((d >> 1) & 63) * 16 + (d & 1) * 4;
-                lds[u] = T::SW_OFF + e * 256;
-                p[u] = RECORD_BYTES;
-                q[u] = SB * 2;
-                wide[u] = false;
-            }
-        }
-    }
-
-    __device__ __forceinline__ void issue(uint8_t *buf, int64_t s) const {
-        const int half = (int)(s >> 1), odd = (int)(s & 1);
-#pragma unroll
-        for (int u = 0; u < T::PER_WAVE; u++) {
-            const uint8_t *src = g[u] + ((int64_t)half * p[u] + odd * q[u]);
-            if (wide[u])
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + lds[u]), 16, 0, 0);
-            else
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)(buf + lds[u]), 4, 0, 0);
-        }
-    }
-};
-
-// Wait until this wave's loads of the stage about to be computed have landed
-// (pending = how many later stages it has issued since), then barrier, so
-// every wave's loads have landed and every wave is done with the stage
-// before it.
-template <int L>
-__device__ __forceinline__ void stage_barrier(int pending) {
-    static_assert(NS == 4, "thresholds below assume at most two later stages in flight");
-    if (pending >= 2)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * L) : "memory");
-    else if (pending == 1)
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(L) : "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-struct Lane {
-    int a_off[SB];  // activation chunk offsets of this lane's row, per block
-    int b_off;      // weight chunk offset in the wave's tile
-    int sx_off, sw_off;
-};
-
-
-// Read block bb's operands from the stage buffer and issue its MFMAs: the
-// exact int32 block dots (one i8 MFMA per 32 x 32 tile) and the rank-1 scale
-// products Dx * Dw in the same register layout.
-template <typename T>
-__device__ __forceinline__ void mfma_block(v16i (&sv)[2], v16f (&sp)[2], const uint8_t *buf, const Lane &ln, int bb) {
-    const v4i av = *reinterpret_cast<const v4i *>(buf + ln.a_off[bb]);
-    const v4h as = rank1_operand(buf + ln.sx_off + bb * 2);
-    const v4h bs = rank1_operand(buf + ln.sw_off + bb * 2);
-    v4i b[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) b[j] = *reinterpret_cast<const v4i *>(buf + T::A_BYTES + ln.b_off + bb * 2048 + j * 512);
-    const v16i zi = {0};
-    const v32f zf = {0};
-#pragma unroll
-    for (int j = 0; j < 2; j++) sv[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b[j], zi, 0, 0, 0);
-    const v32f pp = __builtin_amdgcn_mfma_f32_32x32x4f16(as, bs, zf, 0, 0, 0);
-    sp[0] = __builtin_shufflevector(pp, pp, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-    sp[1] = __builtin_shufflevector(pp, pp, 16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31);
-}
-
-// One 256-value group = stages 2g and 2g + 1, resident in buffers 2P and 2P + 1.
-template <int WM, int WN, int P>
-__device__ __forceinline__ void group(float (&acc)[2][16], uint8_t *lds, const Lane &ln, const StageLoads<WM, WN> &sl,
-                                      int64_t S, int64_t g) {
-    using T = Tile<WM, WN>;
-    float ga[2][16];
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int64_t s = 2 * g + h;
-        const int64_t last = s + NS - 2 < S - 1 ? s + NS - 2 : S - 1;  // latest stage issued so far
-        stage_barrier<T::PER_WAVE>((int)(last - s));
-        if (s + NS - 1 < S) sl.issue(lds + ((2 * P + h + NS - 1) % NS) * T::STAGE_BYTES, s + NS - 1);
-        const uint8_t *buf = lds + (2 * P + h) * T::STAGE_BYTES;
-        // Software pipeline over the stage's blocks: the MFMAs of block bb + 1
-        // are issued before the VALU epilogue of block bb, so the matrix core
-        // works while the VALU converts and accumulates the previous result.
-        v16i sv[2][2];
-        v16f sp[2][2];
-        mfma_block<T>(sv[0], sp[0], buf, ln, 0);
-#pragma unroll
-        for (int bb = 0; bb < SB; bb++) {
-            if (bb + 1 < SB) mfma_block<T>(sv[(bb + 1) & 1], sp[(bb + 1) & 1], buf, ln, bb + 1);
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    ga[j][r] = (h == 0 && bb == 0)
-                                   ? (float)sv[bb & 1][j][r] * sp[bb & 1][j][r]
-                                   : __builtin_fmaf((float)sv[bb & 1][j][r], sp[bb & 1][j][r], ga[j][r]);
-            // pin the block's results here, so the epilogue is not sunk past the
-            // next stage's barrier with every MFMA result of the stage live
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) asm volatile("" : "+v"(ga[j][r]));
-            // interleave: operand reads, then each MFMA followed by a slice of the
-            // epilogue, so the VALU runs while the matrix core is busy
-            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
-#pragma unroll
-            for (int i = 0; i < 3; i++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);  // VALU
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[j][r] += ga[j][r];
-}
-
 // Output tile of this workgroup, XCD-aware.  A launch's workgroups go to the
 // 8 XCDs round-robin by linear id, and each XCD has its own L2.  The tiles are
 // put in a grouped order -- XCD_GROUP_M row blocks at a time, all column
@@ -283,47 +102,112 @@ __device__ __forceinline__ void xcd_tile(int &tm, int &tn) {
     tn = r / gm;
 }
 
-template <int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__restrict__ xq,
-                                                             const uint16_t *__restrict__ xs, int64_t M,
-                                                             const uint8_t *__restrict__ w, int64_t N, int64_t K,
-                                                             float *__restrict__ y, int64_t ld_y) {
-    using T = Tile<WM, WN>;
+// The main loop is the generated inline-asm block of gemm_loop.inc (explicit
+// registers and schedule; its header comment gives the register map and the
+// pipeline).  This function computes the lane's LDS read addresses, the
+// stage-0 load offsets and destinations, runs the loop and stores the tile.
+__global__ __launch_bounds__(512) void gemm_kernel(const int8_t *__restrict__ xq, const uint16_t *__restrict__ xs,
+                                                    int64_t M, const uint8_t *__restrict__ w, int64_t N, int64_t K,
+                                                    float *__restrict__ y, int64_t ld_y) {
+    using T = Tile<4, 2>;
+    static_assert(T::STAGE_BYTES == 34816 && T::A_BYTES == 16384 && T::PER_WAVE == 5 && T::WAVES == 8,
+                  "gemm_loop.inc is generated for this stage layout");
+    static_assert(T::NA == 16 && T::NB == 16 && T::NSX == 4 && T::NSW == 4, "load split of gemm_loop.inc");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * T::STAGE_BYTES];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = wave_id();
-    const int wm = wave % WM, wn = wave / WM;  // 32-row strip wm of packed tile wn
+    const int wm = wave % 4, wn = wave / 4;  // 32-row strip wm of packed tile wn
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t tiles = N / TILE_ROWS;
     int tm, tn;  // the workgroup's output tile (row block, column block)
     xcd_tile(tm, tn);
-    const int64_t T0 = (int64_t)tn * WN;  // the workgroup's first packed weight tile
-    const int64_t G = K / GROUP_K, S = 2 * G;
+    const int64_t T0 = (int64_t)tn * 2;  // the workgroup's first packed weight tile
+    const int64_t G = K / GROUP_K, nb = K / QK;
     const int64_t m_tile = (int64_t)tm * T::ROWS;
-    const bool ragged = T0 + WN > tiles;
-    StageLoads<WM, WN> sl;
-    // tiles past the last one (N not a multiple of the workgroup's columns) reload the last tile
-    sl.init(xq, xs, M, m_tile, w + (T0 * G) * RECORD_BYTES, ragged ? 0 : G * RECORD_BYTES, K, K / QK, wave, lane);
-    for (int s = 0; s < NS - 1; s++)
-        if (s < S) sl.issue(lds + s * T::STAGE_BYTES, s);
+    const bool ragged = T0 + 2 > tiles;
+    // tiles past the last one (N not a multiple of 128) reload the last tile
+    const uint8_t *w_tiles = w + (T0 * G) * RECORD_BYTES;
+    const uint32_t tile_stride = ragged ? 0u : (uint32_t)(G * RECORD_BYTES);
 
-    Lane ln;
-    const int row = wm * 32 + l32;
+    // Stage-0 loads of this wave (load i of a stage goes to wave i % 8): 1 KB
+    // activation loads i = wave, wave + 8 (8 rows x 128 bytes, row r's 16-byte
+    // chunk c stored at position c ^ (r & 7)), weight loads i = 16 + wave,
+    // 24 + wave (a tile's 4 block records are 8 KB contiguous), and one
+    // 256-byte scale load (activation scales [row][4] for waves 0-3, weight
+    // scales [tile][row][4] for waves 4-7).  Offsets are from the row block's
+    // first activation row / scale row and from the first weight tile;
+    // activation rows past M read row M - 1 (their outputs are not stored).
+    v4i gl;       // loads 2, 3 (weights), 4 (scales), unused
+    uint32_t g01[2];
+    uint32_t ldst[5];
 #pragma unroll
-    for (int bb = 0; bb < SB; bb++) ln.a_off[bb] = row * 128 + (((2 * bb + half) ^ (row & 7)) * 16);
-    ln.b_off = wn * SB * 2048 + half * 1024 + l32 * 16;
-    ln.sx_off = T::SX_OFF + row * 8;
-    ln.sw_off = T::SW_OFF + (wn * 64 + half * 32 + l32) * 8;
-
-    float acc[2][16];
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[j][r] = -0.0f;  // -0 + x == x for every x
-    for (int64_t g = 0; g < G; g += 2) {
-        group<WM, WN, 0>(acc, lds, ln, sl, S, g);
-        if (g + 1 < G) group<WM, WN, 1>(acc, lds, ln, sl, S, g + 1);
+    for (int u = 0; u < 2; u++) {
+        const int i = wave + 8 * u;
+        const int r = 8 * i + (lane >> 3), c = (lane & 7) ^ (lane >> 3);
+        const int64_t row = m_tile + r < M ? r : M - 1 - m_tile;
+        g01[u] = (uint32_t)(row * K + c * 16);
+        ldst[u] = lds0 + i * 1024;
     }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const int e = wave + 8 * u;
+        gl[u] = (int)((uint32_t)(e >> 3) * tile_stride + (e & 7) * 1024 + lane * 16);
+        ldst[2 + u] = lds0 + T::A_BYTES + e * 1024;
+    }
+    const uint8_t *sbase;
+    uint32_t sinc;  // scale base step from an odd stage to the next (even) one
+    if (wave < 4) {
+        const int d = wave * 64 + lane;
+        const int64_t row = m_tile + (d >> 1) < M ? (d >> 1) : M - 1 - m_tile;
+        gl[2] = (int)(row * nb * 2 + (d & 1) * 4);
+        ldst[4] = lds0 + T::SX_OFF + wave * 256;
+        sbase = reinterpret_cast<const uint8_t *>(xs + m_tile * nb);
+        sinc = 8;
+    } else {
+        const int d = (wave - 4) * 64 + lane;
+        gl[2] = (int)((uint32_t)(d >> 7) * tile_stride + RECORD_Q_BYTES + ((d >> 1) & 63) * 16 + (d & 1) * 4);
+        ldst[4] = lds0 + T::SW_OFF + (wave - 4) * 256;
+        sbase = w_tiles;
+        sinc = RECORD_BYTES - 8;
+    }
+    gl[3] = 0;
+
+    // LDS read addresses of this lane, for stage buffers 0 / 1 (immediate
+    // offset 0 or one stage) and 2 / 3 (the same + two stages)
+    const int row = wm * 32 + l32;
+    v16i ad;
+#pragma unroll
+    for (int bb = 0; bb < SB; bb++) {
+        ad[bb] = (int)(lds0 + row * 128 + (((2 * bb + half) ^ (row & 7)) * 16));
+        ad[4 + bb] = ad[bb] + 2 * T::STAGE_BYTES;
+    }
+    ad[8] = (int)(lds0 + T::A_BYTES + wn * SB * 2048 + half * 1024 + l32 * 16);
+    ad[9] = ad[8] + 2 * T::STAGE_BYTES;
+    ad[10] = (int)(lds0 + T::SX_OFF + row * 8);
+    ad[11] = ad[10] + 2 * T::STAGE_BYTES;
+    ad[12] = (int)(lds0 + T::SW_OFF + (wn * 64 + half * 32 + l32) * 8);
+    ad[13] = ad[12] + 2 * T::STAGE_BYTES;
+    ad[14] = (int)g01[0];
+    ad[15] = (int)g01[1];
+
+    typedef uint32_t v8u __attribute__((ext_vector_type(8)));
+    v8u sc = {sinc, ldst[0], ldst[1], ldst[2], ldst[3], ldst[4], (uint32_t)(2 * G), (uint32_t)G};
+    uint64_t abase = (uint64_t)(xq + m_tile * K), bbase = (uint64_t)w_tiles, sb = (uint64_t)sbase;
+    v32f acc, ga;
+#pragma unroll
+    for (int r = 0; r < 32; r++) acc[r] = ga[r] = -0.0f;  // -0 + x == x for every x
+    // m0 is written by the loop (LDS destinations of the stage loads); clang
+    // warns that a clobbered reserved register is not preserved, which is the intent
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile(Q8_GEMM_LOOP_ASM
+                 : "+{v[0:31]}"(acc), "+{v[32:63]}"(ga), "+{s[40:41]}"(abase), "+{s[42:43]}"(bbase),
+                   "+{s[44:45]}"(sb), "+{s[48:55]}"(sc)
+                 : "{v[226:241]}"(ad), "{v[242:245]}"(gl)
+                 : Q8_GEMM_LOOP_CLOBBERS, "memory", "m0", "scc");
+#pragma clang diagnostic pop
+
     if (ragged && T0 + wn >= tiles) return;
     const int64_t n_wave = (T0 + wn) * TILE_ROWS;
     // lane holds column l32 of each 32 x 32 tile and rows 8q + 4*half + p
@@ -332,16 +216,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const int8_t *__rest
         const int64_t orow = m_tile + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (orow >= M) continue;
 #pragma unroll
-        for (int j = 0; j < 2; j++) y[orow * ld_y + n_wave + j * 32 + l32] = acc[j][r];
+        for (int j = 0; j < 2; j++) y[orow * ld_y + n_wave + j * 32 + l32] = acc[16 * j + r];
     }
 }
 
-template <int WM, int WN>
 static hipError_t launch_tiles(const int8_t *xq, const uint16_t *xs, int64_t m, const uint8_t *w, int64_t n,
                                int64_t k, float *y, int64_t ld_y, hipStream_t s) {
-    using T = Tile<WM, WN>;
+    using T = Tile<4, 2>;
     const dim3 grid((unsigned)((n + T::COLS - 1) / T::COLS), (unsigned)((m + T::ROWS - 1) / T::ROWS));
-    hipLaunchKernelGGL((gemm_kernel<WM, WN>), grid, dim3(T::THREADS), 0, s, xq, xs, m, w, n, k, y, ld_y);
+    hipLaunchKernelGGL(gemm_kernel, grid, dim3(T::THREADS), 0, s, xq, xs, m, w, n, k, y, ld_y);
     return hipGetLastError();
 }
 
@@ -447,7 +330,7 @@ hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int
     const int8_t *xq = (const int8_t *)x_q;
     const uint16_t *xs = (const uint16_t *)((const uint8_t *)x_q + m * k);
     const uint8_t *wb = (const uint8_t *)w;
-    if (gemm_tiled(m, n)) return launch_tiles<4, 2>(xq, xs, m, wb, n, k, y, ld_y, s);
+    if (gemm_tiled(m, n)) return launch_tiles(xq, xs, m, wb, n, k, y, ld_y, s);
     const dim3 grid((unsigned)(n / TILE_ROWS), (unsigned)((m + 31) / 32));
     hipLaunchKernelGGL(gemm_strip_kernel, grid, dim3(512), 0, s, xq, xs, m, wb, n, k, y, ld_y);
     return hipGetLastError();
