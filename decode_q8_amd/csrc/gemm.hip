@@ -37,6 +37,7 @@
 //   SW  weight scales [tile][row][4 blocks]
 #include "device.hpp"
 #include "gemm_loop.inc"
+#include "gemm_strip.inc"
 #include "launch.hpp"
 
 namespace q8k {
@@ -228,24 +229,28 @@ static hipError_t launch_tiles(const int8_t *xq, const uint16_t *xs, int64_t m, 
     return hipGetLastError();
 }
 
-// Small problems: one workgroup of 8 waves owns a 32 x 64 output strip (32
-// rows, one packed weight tile) and splits k across its waves instead.  The k
-// loop runs in batches of up to 8 groups, one per wave: each wave loads its
-// group's operands straight into registers (26 16-byte loads per lane, all in
-// flight together), forms the group accumulator a_g exactly as the tiled
-// kernel does (same MFMAs, same convert / multiply / fma sequence), and parks
-// it in LDS; after a barrier the 512 threads fold the batch's a_g into their
+// Small problems: one workgroup owns a 32 x 64 output strip (32 rows, one
+// packed weight tile) and splits k across its W waves (4, or 8 when the grid
+// would leave SIMDs without a wave): wave w takes groups w, w + W, ...; each
+// wave forms its group's sums exactly as the tiled kernel does (same MFMAs,
+// same convert / multiply / fma sequence) and parks them in LDS; after a
+// barrier the workgroup's threads fold each batch of group sums into their
 // outputs' running sums in group order, so every output sees the same
 // sequence of fp32 operations as in the tiled kernel and rows stay
-// bit-identical whichever kernel m selects.  Many small strips with all waves
-// busy replace few large tiles with one wave per SIMD.
-constexpr int STRIP_WAVES = 8;
-
-__global__ __launch_bounds__(512) void gemm_strip_kernel(const int8_t *__restrict__ xq,
-                                                         const uint16_t *__restrict__ xs, int64_t M,
-                                                         const uint8_t *__restrict__ w, int64_t N, int64_t K,
-                                                         float *__restrict__ y, int64_t ld_y) {
-    __shared__ float park[STRIP_WAVES][2 * 16 * 64];  // [wave][(j * 16 + r) * 64 + lane]: 64 KB
+// bit-identical whichever kernel m selects.  The k loop is the generated
+// inline-asm block of gemm_strip.inc (operands straight into registers, the
+// wave's next group loading while it computes the current one; its header
+// comment gives the register map).
+template <int W>
+__global__ __launch_bounds__(64 * W) void gemm_strip_kernel(const int8_t *__restrict__ xq,
+                                                             const uint16_t *__restrict__ xs, int64_t M,
+                                                             const uint8_t *__restrict__ w, int64_t N, int64_t K,
+                                                             float *__restrict__ y, int64_t ld_y) {
+    static_assert(W == 4 || W == 8, "gemm_strip.inc has the 4- and 8-wave loops");
+    constexpr int PER = 32 / W;  // outputs per thread
+    // park[buffer][wave][(j * 16 + r) * 64 + lane]: 2 x W x 8 KB
+    __shared__ __attribute__((aligned(16))) float park[2 * W * 2048];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *)park;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = wave_id();
     const int half = lane >> 5, l32 = lane & 31;
@@ -253,72 +258,56 @@ __global__ __launch_bounds__(512) void gemm_strip_kernel(const int8_t *__restric
     const int64_t T = blockIdx.x;
     const int G = (int)(K >> 8), nb = (int)(K >> 5);
     int64_t row = m0 + l32;
-    row = row < M ? row : M - 1;
-    const int8_t *xrow = xq + row * K + half * 16;
-    const uint16_t *xsrow = xs + row * nb;
+    row = row < M ? row : M - 1;  // rows past M read row M - 1 (their outputs are not stored)
     const uint8_t *wt = w + T * (int64_t)G * RECORD_BYTES;
-    float acc[4];
+
+    typedef int v8i __attribute__((ext_vector_type(8)));
+    v8i off;  // v222-229 of the loop: lane offsets and LDS addresses
+    off[0] = (int)(row * K + half * 16);
+    off[1] = (int)(row * nb * 2);
+    off[2] = half * 1024 + l32 * 16;
+    off[3] = RECORD_Q_BYTES + lane * 16;
+    off[4] = (int)(lds0 + wave * 8192 + lane * 4);
+    off[5] = (int)(lds0 + tid * 4);
+    off[6] = off[4] + W * 8192;
+    off[7] = off[5] + W * 8192;
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    v4u ctl = {(uint32_t)wave, (uint32_t)G, 0u, 0u};
+    v4u steps = {256u * W, (uint32_t)RECORD_BYTES * W, 16u * W, 0u};
+    uint64_t abase = (uint64_t)(xq + wave * 256), wbase = (uint64_t)(wt + (int64_t)wave * RECORD_BYTES),
+             xbase = (uint64_t)(reinterpret_cast<const uint8_t *>(xs) + wave * 16);
+    typedef float v8f __attribute__((ext_vector_type(8)));
+    v8f acc;
 #pragma unroll
-    for (int i = 0; i < 4; i++) acc[i] = -0.0f;  // -0 + x == x for every x
-    for (int g0 = 0; g0 < G; g0 += STRIP_WAVES) {
-        const int g = g0 + wave;
-        if (g < G) {
-            const uint8_t *rec = wt + (int64_t)g * RECORD_BYTES;
-            // scales first: loads complete in order, so block 0 can start while the rest arrive
-            const uint4 sx = *reinterpret_cast<const uint4 *>(xsrow + g * GROUP_BLOCKS);  // the row's 8 scales
-            const uint4 sw = *reinterpret_cast<const uint4 *>(rec + RECORD_Q_BYTES + (half * 32 + l32) * 16);
-            __builtin_amdgcn_sched_barrier(0);
-            v4i a[GROUP_BLOCKS], b[GROUP_BLOCKS][2];
-#pragma unroll
-            for (int bb = 0; bb < GROUP_BLOCKS; bb++) {
-                a[bb] = *reinterpret_cast<const v4i *>(xrow + (g * GROUP_BLOCKS + bb) * QK);
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    b[bb][j] = *reinterpret_cast<const v4i *>(rec + bb * 2048 + half * 1024 + (j * 32 + l32) * 16);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // all of the group's loads are in flight before the first MFMA
-            float ga[2][16];
-#pragma unroll
-            for (int bb = 0; bb < GROUP_BLOCKS; bb++) {
-                const v2u xa = {(word_of(sx, bb >> 1) >> (16 * (bb & 1))) & 0xffffu, 0u};
-                const v2u wa = {(word_of(sw, bb >> 1) >> (16 * (bb & 1))) & 0xffffu, 0u};
-                const v16i zi = {0};
-                const v32f zf = {0};
-                v16i sv[2];
-#pragma unroll
-                for (int j = 0; j < 2; j++) sv[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[bb], b[bb][j], zi, 0, 0, 0);
-                const v32f pp = __builtin_amdgcn_mfma_f32_32x32x4f16(__builtin_bit_cast(v4h, xa),
-                                                                     __builtin_bit_cast(v4h, wa), zf, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        ga[j][r] = bb == 0 ? (float)sv[j][r] * pp[16 * j + r]
-                                           : __builtin_fmaf((float)sv[j][r], pp[16 * j + r], ga[j][r]);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) park[wave][(j * 16 + r) * 64 + lane] = ga[j][r];
-        }
-        __syncthreads();
-        const int gn = G - g0 < STRIP_WAVES ? G - g0 : STRIP_WAVES;
-        for (int q = 0; q < gn; q++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) acc[i] += park[q][tid + 512 * i];
-        __syncthreads();
+    for (int i = 0; i < 8; i++) acc[i] = -0.0f;  // -0 + x == x for every x
+    if constexpr (W == 4) {
+        asm volatile(Q8_GEMM_STRIP_ASM_W4
+                     : "+{v[214:221]}"(acc), "+{s[40:41]}"(abase), "+{s[42:43]}"(wbase), "+{s[44:45]}"(xbase),
+                       "+{s[48:51]}"(ctl)
+                     : "{v[222:229]}"(off), "{s[52:55]}"(steps)
+                     : Q8_GEMM_STRIP_CLOBBERS, "s46", "s47", "memory", "scc");
+    } else {
+        asm volatile(Q8_GEMM_STRIP_ASM_W8
+                     : "+{v[214:221]}"(acc), "+{s[40:41]}"(abase), "+{s[42:43]}"(wbase), "+{s[44:45]}"(xbase),
+                       "+{s[48:51]}"(ctl)
+                     : "{v[222:229]}"(off), "{s[52:55]}"(steps)
+                     : Q8_GEMM_STRIP_CLOBBERS, "s46", "s47", "memory", "scc");
     }
-    // thread tid holds outputs o = tid + 512 i, o = (j * 16 + r) * 64 + lane of the MFMA layout:
+    // thread tid holds outputs o = tid + 64 W i, o = (j * 16 + r) * 64 + lane of the MFMA layout:
     // column j * 32 + (lane & 31), row 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int o = tid + 512 * i;
+    for (int i = 0; i < PER; i++) {
+        const int o = tid + 64 * W * i;
         const int ol = o & 63, r = (o >> 6) & 15, j = o >> 10;
         const int64_t orow = m0 + 8 * (r >> 2) + 4 * (ol >> 5) + (r & 3);
         if (orow < M) y[orow * ld_y + T * TILE_ROWS + j * 32 + (ol & 31)] = acc[i];
     }
 }
+
+// The 8-wave strip kernel when the 4-wave grid would have fewer waves than
+// the 1024 SIMDs of the GPU (the split over more waves then costs no
+// occupancy); else the 4-wave one (two workgroups per CU).
+constexpr int64_t STRIP_W8_BELOW_WAVES = 1024;
 
 // Kernel by problem size: 128 x 128 tiles when there are at least 256 of them
 // (one per CU), else 32 x 64 strips with k split across the waves.  Each
@@ -332,7 +321,10 @@ hipError_t launch_gemm(const void *x_q, int64_t m, const void *w, int64_t n, int
     const uint8_t *wb = (const uint8_t *)w;
     if (gemm_tiled(m, n)) return launch_tiles(xq, xs, m, wb, n, k, y, ld_y, s);
     const dim3 grid((unsigned)(n / TILE_ROWS), (unsigned)((m + 31) / 32));
-    hipLaunchKernelGGL(gemm_strip_kernel, grid, dim3(512), 0, s, xq, xs, m, wb, n, k, y, ld_y);
+    if ((int64_t)grid.x * grid.y * 4 < STRIP_W8_BELOW_WAVES)
+        hipLaunchKernelGGL(gemm_strip_kernel<8>, grid, dim3(512), 0, s, xq, xs, m, wb, n, k, y, ld_y);
+    else
+        hipLaunchKernelGGL(gemm_strip_kernel<4>, grid, dim3(256), 0, s, xq, xs, m, wb, n, k, y, ld_y);
     return hipGetLastError();
 }
 
