@@ -138,7 +138,7 @@ def hbm_roofline(kernel, bytes_per_launch, avg_ms):
 # Kernel sources whose sha256 a committed profile summary must match before its
 # counter-derived traffic is reported.
 SEQ_SOURCES = ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp", "decode_q8_amd/csrc/layout.hpp"]
-GEMM_SOURCES = ["decode_q8_amd/csrc/gemm.hip", "decode_q8_amd/csrc/gemm_loop.inc"]
+GEMM_SOURCES = ["decode_q8_amd/csrc/gemm.hip", "decode_q8_amd/csrc/gemm_loop.inc", "decode_q8_amd/csrc/gemm_strip.inc"]
 
 # Spread of the per-replay times of the most recent graph_time call (ms at the
 # 10th, 50th and 90th percentile), reported beside the mean in every record.
