@@ -6,17 +6,27 @@
 //
 // One workgroup per record: 1,088 coalesced 16-byte loads of the 64 source
 // row segments (272 bytes each, 16-byte aligned because k % 256 == 0) into LDS,
-// then 1,088 coalesced 16-byte stores of the reordered record.
+// then 1,088 coalesced 16-byte stores of the reordered record.  A 272-byte
+// segment is not a whole number of 128-byte cache lines, so consecutive
+// records of a tile share their boundary lines.  Workgroups go to the 8 XCDs
+// round-robin by id, each with its own L2, so records are taken XCD-aware:
+// XCD x gets the x-th eighth of the records, consecutive records on one XCD
+// at about the same time, and a shared line is fetched from memory once
+// instead of once per XCD (only speed and memory traffic depend on this).
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace q8k {
 
+constexpr int XCDS = 8;
+
 __global__ __launch_bounds__(256) void repack_kernel(const uint8_t *__restrict__ src, int64_t k,
                                                      uint8_t *__restrict__ dst) {
     __shared__ uint4 lds[RECORD_BYTES / 16];  // 64 rows x 17 chunks
     const int64_t groups = k / GROUP_K;
-    const int64_t rec = blockIdx.x;
+    const int64_t records = gridDim.x;
+    const int64_t rec = records % XCDS ? (int64_t)blockIdx.x
+                                       : (int64_t)(blockIdx.x % XCDS) * (records / XCDS) + blockIdx.x / XCDS;
     const int64_t T = rec / groups, G = rec - T * groups;
     const int64_t row_bytes = (k / QK) * BLOCK_BYTES;
 
