@@ -97,3 +97,24 @@ def test_tiled_ragged_n_whole_output(m, n, k):
     y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
                              threads=THREADS)
     check_tol(yfull[:, :n], y_ref, S, f"ragged tiled m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(2048, 2048, 256), (2048, 2048, 768), (2053, 2048, 1280)])
+def test_tiled_short_and_odd_k_whole_output(m, n, k):
+    """Tiled kernel with fewer stages than its four stage buffers (k = 256: two
+    stages, so the first wait is for every load issued) and with an odd number
+    of 256-value groups (k = 768, 1280: the loop leaves after the first group of
+    its two-group body), and a row count that is not a multiple of 128: every
+    output against the oracle, and the rows are bit-identical to the strip
+    kernel's (the same rows computed inside a small problem)."""
+    x = wl.activation(wl.PREFILL, 90 + k, m, k, outliers=True)
+    w = wl.weight(wl.PREFILL, 90 + n, n, k)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    _, wp = weights_packed(w)
+    y = _gemm(xq, m, wp, n, k)
+    y_ref, S = oracle.matmul(ref_quantize(x, oracle.LAYOUT_ACT), m, ref_quantize(w, oracle.LAYOUT_ROWS), n, k,
+                             threads=THREADS)
+    check_tol(y, y_ref, S, f"tiled m={m} n={n} k={k}")
+    rows = [0, 1, 2, 127, 128, 129, 500, 1000, 1500, 2000, m - 2, m - 1]
+    ys = _gemm(quantize(x[rows], q8.Q8_LAYOUT_ACT), len(rows), wp, n, k)  # 12 rows (> 8: GEMM): strip kernel
+    assert bits_equal(ys, y[rows]), "tiled and strip kernels differ"

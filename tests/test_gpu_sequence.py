@@ -53,7 +53,7 @@ def _single(s, m):
 LAYER = [(3072, 2048), (2048, 2048), (16384, 2048), (2048, 8192)]  # fused QKV, O, gate||up, down
 
 
-@pytest.mark.parametrize("m", [1, 4, 6, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decode_layers_bit_identical_to_single_launches(m):
     """Two decode layers plus a head: every step equals its own launch bit for
     bit, sampled outputs meet the oracle bound, the workspace returns to zero."""
