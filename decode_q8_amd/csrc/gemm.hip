@@ -206,7 +206,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const int8_t *__restrict__ xq
                  : "+{v[0:31]}"(acc), "+{v[32:63]}"(ga), "+{s[40:41]}"(abase), "+{s[42:43]}"(bbase),
                    "+{s[44:45]}"(sb), "+{s[48:55]}"(sc)
                  : "{v[226:241]}"(ad), "{v[242:245]}"(gl)
-                 : Q8_GEMM_LOOP_CLOBBERS, "memory", "m0", "scc");
+                 : Q8_GEMM_LOOP_CLOBBERS, "memory", "m0", "scc", "s57");
 #pragma clang diagnostic pop
 
     if (ragged && T0 + wn >= tiles) return;

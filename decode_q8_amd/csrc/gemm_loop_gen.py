@@ -37,12 +37,17 @@ SGPRs: s[40:41] A base, s[42:43] B base, s[44:45] scale base (activation
 scales for waves 0-3, weight scales for waves 4-7), s48 scale-base step from
 an odd to an even stage, s49-53 the five loads' LDS destinations in buffer 0,
 s54 stages not yet loaded, s55 groups left (s48-55 passed in as one vector;
-tuples of more than two SGPRs start at a multiple of 4).
+tuples of more than two SGPRs start at a multiple of 4); s57 whether the stage
+load being spread over slots is a real one (clobbered).
 
 Stage loads: every wave issues 5 direct-to-LDS loads per 128-value stage (2
 activation, 2 weight, 1 scale), four stages deep.  Stage s + 1 is waited for
 (vmcnt) and barriered in slot 2 of stage s; right after that barrier every
-wave has finished reading stage s, so stage s + 4 is loaded into its buffer.
+wave has finished reading stage s, so stage s + 4 is loaded into its buffer,
+its five loads spread over slots 2 and 3 of stage s and slots 0 and 1 of
+stage s + 1 (issuing all 40 KB of a workgroup's loads right after the barrier
+measured 2-3% slower); all of them are issued before the wait for stage s + 2,
+so the loads outstanding after stage s + 1's are always stages s + 2 and s + 3.
 Once no real stage is left to load, the wait becomes vmcnt(0) (everything
 issued has landed) and nothing more is loaded.
 
@@ -70,6 +75,7 @@ VX = (236, 237)
 VW = (238, 239)
 VG = 240  # 240..244
 S_ABASE, S_BBASE, S_SBASE, S_SINC, S_LDS, S_LEFT, S_GLEFT = 40, 42, 44, 48, 49, 54, 55
+S_ISSUING = 57  # 1 while the stage load started in slot 2 still has parts to issue
 
 PRIO_AFTER_BARRIER = {2: 3, 3: 2, 0: 1, 1: 0}  # slot b -> wave priority (the barrier is in slot 2)
 
@@ -143,6 +149,39 @@ def issue(buf, parity):
     return out
 
 
+SPREAD = [[0, 1], [2], [3], [4]]  # the stage's five loads over four slots
+
+
+def issue_part(buf, parity, part):
+    """Part `part` of loading the next stage into buffer buf: the loads are
+    spread over four slots (slot 2 right after the barrier, slot 3, and slots
+    0 and 1 of the next stage) instead of all eight waves issuing 40 KB at
+    once; the buffer is not read before the barrier three stages later.  The
+    first part decides whether a stage is left to load (s57), the last one
+    advances the bases."""
+    kinds = [("dwordx4", S_ABASE), ("dwordx4", S_ABASE), ("dwordx4", S_BBASE), ("dwordx4", S_BBASE),
+             ("dword", S_SBASE)]
+    out = []
+    if part == 0:
+        out += [f"s_cmp_eq_u32 s{S_LEFT}, 0", f"s_cselect_b32 s{S_ISSUING}, 0, 1"]
+    out += [f"s_cmp_eq_u32 s{S_ISSUING}, 0", "s_cbranch_scc1 6f"]
+    for u in SPREAD[part]:
+        size, sb = kinds[u]
+        out += [f"s_add_u32 m0, s{S_LDS+u}, {buf * STAGE_BYTES}", "s_nop 0",
+                f"global_load_lds_{size} v{VG+u}, s[{sb}:{sb+1}]"]
+    if part == len(SPREAD) - 1:
+        inc_b = INC_B[parity]
+        inc_s = str(INC_SX_EVEN) if parity == 0 else f"s{S_SINC}"
+        out += [f"s_cmp_gt_u32 s{S_LEFT}, 1", "s_cbranch_scc0 2f",
+                f"s_add_u32 s{S_ABASE}, s{S_ABASE}, {INC_A}", f"s_addc_u32 s{S_ABASE+1}, s{S_ABASE+1}, 0",
+                f"s_add_u32 s{S_BBASE}, s{S_BBASE}, {inc_b}", f"s_addc_u32 s{S_BBASE+1}, s{S_BBASE+1}, 0",
+                f"s_add_u32 s{S_SBASE}, s{S_SBASE}, {inc_s}", f"s_addc_u32 s{S_SBASE+1}, s{S_SBASE+1}, 0",
+                "2:",
+                f"s_sub_u32 s{S_LEFT}, s{S_LEFT}, 1"]
+    out += ["6:"]
+    return out
+
+
 def slot(i, b):
     """Stage i of the four-stage loop body (buffer i), block b."""
     nxt_set = (b + 1) & 1
@@ -159,7 +198,11 @@ def slot(i, b):
         head = [f"s_cmp_eq_u32 s{S_LEFT}, 0", "s_cbranch_scc1 4f",
                 "s_waitcnt vmcnt(10) lgkmcnt(0)", "s_branch 5f",
                 "4:", "s_waitcnt vmcnt(0) lgkmcnt(0)",
-                "5:", "s_barrier"] + issue(i, i & 1)
+                "5:", "s_barrier"] + issue_part(i, i & 1, 0)
+    elif b == 3:
+        head = head + issue_part(i, i & 1, 1)
+    else:  # slots 0 and 1 finish the load the previous stage started
+        head = head + issue_part((i - 1) % NBUF, (i - 1) & 1, 2 + b)
     # wave priority falls as the wave moves from one barrier to the next
     # (3 right after it, 0 in the slot before the next), so of the two waves
     # sharing a SIMD the one behind wins issue and they reach the barrier
@@ -178,7 +221,7 @@ def slot(i, b):
 
 
 def loop():
-    lines = [f"v_mov_b32 v{OP[st]+k}, 0" for st in (0, 1) for k in (13, 15)]
+    lines = [f"v_mov_b32 v{OP[st]+k}, 0" for st in (0, 1) for k in (13, 15)] + [f"s_mov_b32 s{S_ISSUING}, 0"]
     for buf in range(NBUF):
         lines += issue(buf, buf & 1)
     # stage 0 landed: 15 later loads may be in flight if 4 stages were issued (2+ groups)
