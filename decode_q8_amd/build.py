@@ -42,7 +42,7 @@ def source_digest() -> str:
     refuses a library whose digest differs from the tree's."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".cpp", ".h")))
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".cpp", ".h", ".inc")))
     for name in files:
         h.update(name.encode() + b"\0")
         h.update(open(os.path.join(CSRC, name), "rb").read())

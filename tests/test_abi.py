@@ -259,6 +259,21 @@ def test_stale_library_is_refused(monkeypatch):
         q8._lib = saved
 
 
+def test_digest_covers_every_included_file():
+    """Every file a kernel or host source includes from the source folder
+    (the generated GEMM loops among them) is part of the build digest, so
+    regenerating one makes the old library stale."""
+    import re
+    from decode_q8_amd import build
+    names = set(os.listdir(build.CSRC))
+    covered = {f for f in names if f.endswith((".hip", ".hpp", ".cpp", ".h", ".inc"))}
+    for f in covered:
+        for inc in re.findall(r'#include\s+"([^"]+)"', open(os.path.join(build.CSRC, f)).read()):
+            if inc in names:
+                assert inc in covered, (f, inc)
+    assert {"gemm_loop.inc", "gemm_strip.inc"} <= covered
+
+
 def test_device_queries_need_a_device():
     """Without a GPU no call gets as far as a device query."""
     before = q8.q8_device_queries()
