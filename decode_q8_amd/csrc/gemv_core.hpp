@@ -91,15 +91,111 @@ __device__ __forceinline__ void group_sums(const GroupRegs &g, const int8_t *con
     }
 }
 
+// Round half away from zero of an fp32 q with |q| < 2^23: q + copysign(0.5 -
+// 2^-25, q), truncated.  Equal to (int)roundf(q) for every such q (checked
+// exhaustively on the host for |q| <= 128): the offset just below one half
+// keeps 0.5 - 2^-25 itself from rounding up to 1, and at an exact half the
+// sum n + 1 - 2^-25 still rounds (to nearest even) to n + 1.
+__device__ __forceinline__ int round_half_away(float q) { return (int)(q + __builtin_copysignf(0x1.fffffep-2f, q)); }
+
+// Lane l's four codes x / d, rounded half away from zero (0 when d == 0),
+// packed low byte first.  For d in [2^-96, 2^96] the four quotients share one
+// reciprocal of d refined by a Newton-Raphson step, and each is x * r
+// corrected twice by its exact fma residual (Markstein's method).  These are
+// exactly the operations of the compiler's correctly rounded fp32 division
+// without its range-scaling steps, and in this range those steps change
+// nothing whenever the quotient can round to a nonzero code (they act only on
+// a zero or very small numerator or a subnormal quotient, where both paths
+// give code 0); so the codes equal (int)roundf(x / d).  Other d: the IEEE
+// division itself.
+__device__ __forceinline__ uint32_t quantize4(const float4 &v, float d) {
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (d >= 0x1p-96f && d <= 0x1p96f) {
+        const float r0 = __builtin_amdgcn_rcpf(d);
+        const float r = fmaf(fmaf(-d, r0, 1.0f), r0, r0);
+        auto quot = [d, r](float x) {
+            const float qa = x * r;
+            const float qb = fmaf(fmaf(-d, qa, x), r, qa);
+            return fmaf(fmaf(-d, qb, x), r, qb);
+        };
+        q0 = round_half_away(quot(v.x));
+        q1 = round_half_away(quot(v.y));
+        q2 = round_half_away(quot(v.z));
+        q3 = round_half_away(quot(v.w));
+    } else if (d != 0.0f) {
+        q0 = (int)roundf(v.x / d);
+        q1 = (int)roundf(v.y / d);
+        q2 = (int)roundf(v.z / d);
+        q3 = (int)roundf(v.w / d);
+    }
+    return ((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
+           ((uint32_t)q3 << 24);
+}
+
+// Block scale of lane l's block (the 8 aligned lanes l & ~7): amax over the
+// block by an exact max butterfly, d = amax / 127 (IEEE division).
+__device__ __forceinline__ float block_scale(const float4 &v) {
+    const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    return amax / 127.0f;
+}
+
+// The wave's 64 packed code dwords (dword l in lane l) copied into every
+// 16-lane row: x16[i] holds dwords 16 i .. 16 i + 15 in lanes 16 r .. 16 r +
+// 15 of each row r, so an operand with DPP row_newbcast:j reads dword 16 i +
+// j in all 64 lanes.  One 32-lane swap gives [r0 r1 r0 r1] and [r2 r3 r2 r3]
+// (rows of 16 dwords), a 16-lane swap of each with itself the four copies.
+// Needs every lane active.
+__device__ __forceinline__ void replicate_rows(uint32_t qd, uint32_t (&x16)[4]) {
+    const auto h = __builtin_amdgcn_permlane32_swap(qd, qd, false, false);
+    const auto lo = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    x16[0] = lo[0];
+    x16[1] = lo[1];
+    x16[2] = hi[0];
+    x16[3] = hi[1];
+}
+
+// s0 += the int8 dot of block 2i (weight chunks a0, a1) and s1 += that of
+// block 2i + 1 (b0, b1) with the activation codes in x = x16[i] (dwords 0..7
+// of the row are block 2i, 8..15 block 2i + 1), each code dword broadcast by
+// DPP straight into v_dot4c.  The two chains are interleaved.  The compiler
+// does not see inside the asm, so it carries its own wait states: 2 before
+// the first DPP read of x (written by VALU just before), and 3 after the last
+// dot, which another VALU instruction may otherwise read before the result is
+// written (a dot-write hazard of this chip family).
+__device__ __forceinline__ void dot_pair(int &s0, int &s1, uint32_t x, const uint4 &a0, const uint4 &a1,
+                                         const uint4 &b0, const uint4 &b1) {
+    asm("s_nop 1\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %13 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %6 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %14 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %7 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %15 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %8 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %9 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %10 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %1, %2, %18 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 2"
+        : "+v"(s0), "+v"(s1)
+        : "v"(x), "v"(a0.x), "v"(a0.y), "v"(a0.z), "v"(a0.w), "v"(a1.x), "v"(a1.y), "v"(a1.z), "v"(a1.w),
+          "v"(b0.x), "v"(b0.y), "v"(b0.z), "v"(b0.w), "v"(b1.x), "v"(b1.y), "v"(b1.z), "v"(b1.w));
+}
+
 // Group sums with the activation quantization fused in: xv[m] holds lane l's
 // values 4l..4l+3 of the group's 256 fp32 values of row m (loaded by the
 // caller ahead of the weights, so the quantization does not wait for them).
-// Lane l quantizes values 4l..4l+3 (block
-// l / 8) with exactly the arithmetic of the standalone quantizer (amax over
-// the block by an exact max butterfly, d = amax / 127, q = round-half-away of
-// x / d, stored scale fp16(d)), so the codes and scales are bit-identical to
-// q8_quantize_rows.  The packed codes and scales are then broadcast from their
-// lane to the whole wave (v_readlane) as v_dot4c's scalar operand.
+// Lane l quantizes values 4l..4l+3 (block l / 8) with exactly the arithmetic
+// of the standalone quantizer (bit-identical codes and scales, see
+// quantize4).  The packed codes are copied into every 16-lane row and fed to
+// v_dot4c by DPP broadcast; each block's activation scale comes from its
+// lane by v_readlane.
 template <int M>
 __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 (&xv)[M], float (&u)[M]) {
     float dw[8];
@@ -107,31 +203,20 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 
     for (int bb = 0; bb < 8; bb++) dw[bb] = half_bits_to_float(half_of(g.c[16], bb));
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const float4 v = xv[m];
-        const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        const float d = amax / 127.0f;
-        int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-        if (d != 0.0f) {
-            q0 = (int)roundf(v.x / d);
-            q1 = (int)roundf(v.y / d);
-            q2 = (int)roundf(v.z / d);
-            q3 = (int)roundf(v.w / d);
-        }
-        const int qd = (int)(((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
-                             ((uint32_t)q3 << 24));
+        const float d = block_scale(xv[m]);
+        uint32_t x16[4];
+        replicate_rows(quantize4(xv[m], d), x16);
         const float dxl = half_bits_to_float(float_to_half_bits(d));
         float t[8];
 #pragma unroll
-        for (int bb = 0; bb < 8; bb++) {
-            int s = 0;
-#pragma unroll
-            for (int h = 0; h < 2; h++)
-#pragma unroll
-                for (int c = 0; c < 4; c++)
-                    s = __builtin_amdgcn_sdot4((int)word_of(g.c[2 * bb + h], c),
-                                               __builtin_amdgcn_readlane(qd, 8 * bb + 4 * h + c), s, false);
-            const float dx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dxl), 8 * bb));
-            t[bb] = (float)s * (dw[bb] * dx);
+        for (int i = 0; i < 4; i++) {
+            int s0 = 0, s1 = 0;
+            dot_pair(s0, s1, x16[i], g.c[4 * i], g.c[4 * i + 1], g.c[4 * i + 2], g.c[4 * i + 3]);
+            const float dx0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dxl), 16 * i));
+            const float dx1 =
+                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dxl), 16 * i + 8));
+            t[2 * i] = (float)s0 * (dw[2 * i] * dx0);
+            t[2 * i + 1] = (float)s1 * (dw[2 * i + 1] * dx1);
         }
         u[m] = tree8(t);
     }
@@ -342,18 +427,8 @@ __device__ __forceinline__ void quantize_group(const float4 (&xv)[M], uint32_t *
     float *sdx = reinterpret_cast<float *>(scr + M * 64);
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const float4 v = xv[m];
-        const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        const float d = amax / 127.0f;
-        int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-        if (d != 0.0f) {
-            q0 = (int)roundf(v.x / d);
-            q1 = (int)roundf(v.y / d);
-            q2 = (int)roundf(v.z / d);
-            q3 = (int)roundf(v.w / d);
-        }
-        scr[m * 64 + lane] = ((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
-                             ((uint32_t)q3 << 24);
+        const float d = block_scale(xv[m]);
+        scr[m * 64 + lane] = quantize4(xv[m], d);
         if ((lane & 7) == 0) sdx[(lane >> 3) * 8 + m] = half_bits_to_float(float_to_half_bits(d));
     }
     // the wave's own LDS writes complete before its lanes read each other's

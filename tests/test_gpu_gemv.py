@@ -151,7 +151,7 @@ def _half_integer_activations(m, k, seed):
     return x
 
 
-@pytest.mark.parametrize("m", [1, 4, 8])
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
 def test_fused_quantization_half_integer_quotients(m):
     """The fused quantization equals the standalone quantizer bitwise where the
     quotients are exact or near half-integers (ties away from zero)."""
@@ -166,6 +166,54 @@ def test_fused_quantization_half_integer_quotients(m):
     assert bits_equal(down(y), ref)
     # and the standalone codes are the oracle's (ties away from zero)
     assert np.array_equal(down(quantize(x, q8.Q8_LAYOUT_ACT)), ref_quantize(x, q8.Q8_LAYOUT_ACT))
+
+
+def _tie_neighbour_activations(m, k, seed):
+    """Per 32-value block a scale d0 of 2^-120 .. 2^-90 (across the lower end
+    2^-96 of the range where the fused path divides by a shared refined
+    reciprocal; such blocks add 0 to y, since their fp16 scale is 0) or 2^-30
+    .. 2^14 (inside it, where every code shows in y), the block maximum
+    127 * d0, and values at the exact fp32 ties (j + 0.5) * d and 1 or 2 ulps
+    to either side, where d = fp32(amax / 127) is the scale the quantizer
+    computes: quotients that a division one ulp off would round the other way.
+    (Larger scales overflow the fp16 scale and turn outputs into inf / NaN.)"""
+    rng = np.random.default_rng(seed)
+    x = np.empty((m, k), np.float32)
+    exps = np.concatenate([np.arange(-120, -90), np.arange(-30, 15), np.arange(-30, 15)])
+    for r in range(m):
+        for b in range(k // 32):
+            d0 = np.float32(rng.uniform(1.0, 2.0) * 2.0 ** int(rng.choice(exps)))
+            amax = np.float32(127) * d0
+            d = amax / np.float32(127)
+            j = rng.integers(-127, 127, size=32).astype(np.float32)
+            v = ((j + np.float32(0.5)) * d).astype(np.float32)
+            for _ in range(2):
+                step = rng.integers(-1, 2, size=32)
+                v = np.where(step > 0, np.nextafter(v, np.float32(np.inf)),
+                             np.where(step < 0, np.nextafter(v, np.float32(-np.inf)), v)).astype(np.float32)
+            v = np.clip(v, -amax, amax)
+            v[rng.integers(0, 32)] = amax if rng.random() < 0.5 else -amax
+            x[r, 32 * b:32 * b + 32] = v
+    return x
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 8])
+def test_fused_quantization_tie_neighbours_and_scale_range(m):
+    """The fused quantization equals the standalone quantizer (IEEE division)
+    bitwise on exact ties and their 1- and 2-ulp neighbours, at scales inside
+    and outside the range where the fused path divides by a shared refined
+    reciprocal; the standalone codes are the oracle's."""
+    n, k = 256, 4096
+    x = _tie_neighbour_activations(m, k, seed=91 + m)
+    _, w = _case(m, n, k, seed=7 * m)
+    _, wp = weights_packed(w)
+    xq = quantize(x, q8.Q8_LAYOUT_ACT)
+    assert np.array_equal(down(xq), ref_quantize(x, q8.Q8_LAYOUT_ACT))
+    ref = _gemv(xq, m, wp, 1, n, k)
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    ws = q8.workspace(m, n, k)
+    q8.q8_quantize_matmul(up(x), k, m, wp, q8.Q8_LAYOUT_PACKED, n, k, y, n, ws, 0 if ws is None else ws.numel())
+    assert bits_equal(down(y), ref)
 
 
 def test_ld_y_and_workspace_reuse():
