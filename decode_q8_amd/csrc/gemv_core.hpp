@@ -558,6 +558,12 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
                                           int64_t ld_y, int64_t T, int wi, int wgs_per_tile, int segs_per_wg,
                                           uint32_t *__restrict__ ctr, float *__restrict__ part, float *lds_u,
                                           int *last_wg, bool handover, Wait &&hooks) {
+    // fetched now and kept in registers: in the sequence they come from the
+    // kernel-argument array, and a late scalar load would sit right before
+    // the output store
+    asm volatile("" : "+s"(y), "+s"(ld_y));
+    typedef __attribute__((address_space(1))) float global_float;
+    global_float *const yg = (global_float *)y;  // global stores (a flat store would also count as an LDS access)
     const int lane = threadIdx.x & 63;
     const int wv = wave_id();
     const int W = blockDim.x >> 6;
@@ -599,26 +605,35 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
     const bool out_ok = chain_thread && out_row < n;
     float acc = 0.0f;
     if (chain_thread) {
-        for (int64_t sj = s0; sj < s1; sj++) {
-            const int64_t gs = sj * SEG_GROUPS, ge = (gs + SEG_GROUPS) < G ? (gs + SEG_GROUPS) : G;
+        for (int sj = s0; sj < s1; sj++) {
+            const int gs = sj * SEG_GROUPS, cnt = min(G - gs, SEG_GROUPS);  // groups in the segment, >= 1
+            const float *src = lds_u + ((gs - ga) * M + cm) * TILE_ROWS + cr;
             float v[SEG_GROUPS];  // the segment's group sums, all LDS reads in flight at once
+            float sv;
+            if (cnt == SEG_GROUPS) {  // a whole segment: no per-group tests
 #pragma unroll
-            for (int j = 0; j < SEG_GROUPS; j++)
-                v[j] = gs + j < ge ? lds_u[((gs + j - ga) * M + cm) * TILE_ROWS + cr] : 0.0f;
-            float sv = v[0];
+                for (int j = 0; j < SEG_GROUPS; j++) v[j] = src[j * M * TILE_ROWS];
+                sv = v[0];
 #pragma unroll
-            for (int j = 1; j < SEG_GROUPS; j++)
-                if (gs + j < ge) sv += v[j];
+                for (int j = 1; j < SEG_GROUPS; j++) sv += v[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < SEG_GROUPS; j++) v[j] = j < cnt ? src[j * M * TILE_ROWS] : 0.0f;
+                sv = v[0];
+#pragma unroll
+                for (int j = 1; j < SEG_GROUPS; j++)
+                    if (j < cnt) sv += v[j];
+            }
             if (wgs_per_tile == 1) {
                 acc = sj == 0 ? sv : acc + sv;
             } else if (out_ok) {
-                __hip_atomic_exchange((uint32_t *)&part[(sj * M + cm) * n + out_row], __builtin_bit_cast(uint32_t, sv),
+                __hip_atomic_exchange((uint32_t *)&part[((int64_t)sj * M + cm) * n + out_row], __builtin_bit_cast(uint32_t, sv),
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
     if (wgs_per_tile == 1) {
-        if (out_ok) y[cm * ld_y + out_row] = acc;
+        if (out_ok) yg[cm * ld_y + out_row] = acc;
         return;
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's exchanges have completed
@@ -643,7 +658,7 @@ __device__ __forceinline__ void tile_unit(const ACT *__restrict__ xq, int64_t ld
             for (int j = 0; j < 8; j++)
                 if (b0 + j < S) acc = (b0 + j == 0) ? v[j] : acc + v[j];
         }
-        y[cm * ld_y + out_row] = acc;
+        yg[cm * ld_y + out_row] = acc;
     }
     if (t == 0) __hip_atomic_exchange(&ctr[T], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
