@@ -30,16 +30,19 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int c) {
 // everything derived from it stays scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
-// Maximum over each aligned group of 8 lanes, left in all 8 (DPP lane moves:
-// swap neighbours, swap pairs, then mirror the two halves of the 8 lanes).
-// fmaxf is exact, so the order of the moves does not change the result.
+// Maximum over each aligned group of 8 lanes, left in all 8: three DPP steps
+// (swap neighbours, swap pairs, mirror the two halves of the 8 lanes), each a
+// single v_max_f32 with a DPP source; the s_nop gives a DPP read the 2 wait
+// states it needs after the VALU write of its source.  max is exact, so the
+// order of the steps does not change the result.
 __device__ __forceinline__ float max_over_8_lanes(float x) {
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf,
-                                                                      false)));  // quad_perm [1, 0, 3, 2]
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf,
-                                                                      false)));  // quad_perm [2, 3, 0, 1]
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf,
-                                                                      false)));  // row_half_mirror
+    asm("s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf"
+        : "+v"(x));
     return x;
 }
 

@@ -99,18 +99,18 @@ __device__ __forceinline__ void group_sums(const GroupRegs &g, const int8_t *con
 __device__ __forceinline__ int round_half_away(float q) { return (int)(q + __builtin_copysignf(0x1.fffffep-2f, q)); }
 
 // Lane l's four codes x / d, rounded half away from zero (0 when d == 0),
-// packed low byte first.  For d in [2^-96, 2^96] the four quotients share one
-// reciprocal of d refined by a Newton-Raphson step, and each is x * r
-// corrected twice by its exact fma residual (Markstein's method).  These are
-// exactly the operations of the compiler's correctly rounded fp32 division
-// without its range-scaling steps, and in this range those steps change
-// nothing whenever the quotient can round to a nonzero code (they act only on
-// a zero or very small numerator or a subnormal quotient, where both paths
-// give code 0); so the codes equal (int)roundf(x / d).  Other d: the IEEE
-// division itself.
+// packed low byte first.  When every lane's d lies in [2^-96, 2^96] (the
+// test is wave-uniform) the four quotients share one reciprocal of d refined
+// by a Newton-Raphson step, and each is x * r corrected twice by its exact
+// fma residual (Markstein's method).  These are exactly the operations of the
+// compiler's correctly rounded fp32 division without its range-scaling steps,
+// and in this range those steps change nothing whenever the quotient can
+// round to a nonzero code (they act only on a zero or very small numerator or
+// a subnormal quotient, where both paths give code 0); so the codes equal
+// (int)roundf(x / d).  Otherwise the whole wave takes the IEEE division.
 __device__ __forceinline__ uint32_t quantize4(const float4 &v, float d) {
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    if (d >= 0x1p-96f && d <= 0x1p96f) {
+    if (__builtin_amdgcn_ballot_w64(!(d >= 0x1p-96f && d <= 0x1p96f)) == 0) {
         const float r0 = __builtin_amdgcn_rcpf(d);
         const float r = fmaf(fmaf(-d, r0, 1.0f), r0, r0);
         auto quot = [d, r](float x) {
@@ -128,8 +128,9 @@ __device__ __forceinline__ uint32_t quantize4(const float4 &v, float d) {
         q2 = (int)roundf(v.z / d);
         q3 = (int)roundf(v.w / d);
     }
-    return ((uint32_t)q0 & 0xffu) | (((uint32_t)q1 & 0xffu) << 8) | (((uint32_t)q2 & 0xffu) << 16) |
-           ((uint32_t)q3 << 24);
+    // low bytes of q0, q1 into bytes 0, 1 and of q2, q3 into bytes 2, 3 (v_perm_b32)
+    return __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u) |
+           __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x04000c0cu);
 }
 
 // Block scale of lane l's block (the 8 aligned lanes l & ~7): amax over the
@@ -155,37 +156,58 @@ __device__ __forceinline__ void replicate_rows(uint32_t qd, uint32_t (&x16)[4]) 
     x16[3] = hi[1];
 }
 
-// s0 += the int8 dot of block 2i (weight chunks a0, a1) and s1 += that of
-// block 2i + 1 (b0, b1) with the activation codes in x = x16[i] (dwords 0..7
-// of the row are block 2i, 8..15 block 2i + 1), each code dword broadcast by
-// DPP straight into v_dot4c.  The two chains are interleaved.  The compiler
-// does not see inside the asm, so it carries its own wait states: 2 before
-// the first DPP read of x (written by VALU just before), and 3 after the last
-// dot, which another VALU instruction may otherwise read before the result is
-// written (a dot-write hazard of this chip family).
-__device__ __forceinline__ void dot_pair(int &s0, int &s1, uint32_t x, const uint4 &a0, const uint4 &a1,
-                                         const uint4 &b0, const uint4 &b1) {
-    asm("s_nop 1\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %13 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %6 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %14 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %7 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %15 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %8 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %9 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %10 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %1, %2, %18 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2"
-        : "+v"(s0), "+v"(s1)
-        : "v"(x), "v"(a0.x), "v"(a0.y), "v"(a0.z), "v"(a0.w), "v"(a1.x), "v"(a1.y), "v"(a1.z), "v"(a1.w),
-          "v"(b0.x), "v"(b0.y), "v"(b0.z), "v"(b0.w), "v"(b1.x), "v"(b1.y), "v"(b1.z), "v"(b1.w));
+// The block terms t0 = fp32(s0) * (Dw0 * Dx0) and t1 of blocks 2i and 2i + 1:
+// s0, s1 are their int8 dots with the activation codes in x = x16[i]
+// (dwords 0..7 of each row are block 2i, 8..15 block 2i + 1; weight chunks
+// a0, a1 and b0, b1), each code dword broadcast by DPP straight into
+// v_dot4c, the two chains interleaved; Dx comes by DPP from dx8, which holds
+// block j's activation scale in lane j of every row.  The compiler does not
+// see inside the asm, so it keeps its own wait states: the two moves give a
+// DPP read of x 2 after its last VALU write, and the two multiplies plus a
+// convert put 3 between each dot chain's last write and the convert that
+// reads it (a dot result read too early by another VALU instruction is stale
+// on this chip family).
+__device__ __forceinline__ void block_pair_terms(float &t0, float &t1, uint32_t x, float dx8, float dw0, float dw1,
+                                                 int i, const uint4 &a0, const uint4 &a1, const uint4 &b0,
+                                                 const uint4 &b1) {
+    int s0, s1;
+    float p0, p1;
+#define Q8_PAIR_ASM(BC0, BC1)                                                                           \
+    asm("v_mov_b32 %2, 0\n\t"                                                                          \
+        "v_mov_b32 %3, 0\n\t"                                                                          \
+        "v_dot4c_i32_i8_dpp %2, %6, %10 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %18 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %2, %6, %11 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %19 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %2, %6, %12 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %20 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_dot4c_i32_i8_dpp %2, %6, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %21 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_dot4c_i32_i8_dpp %2, %6, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %22 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_dot4c_i32_i8_dpp %2, %6, %15 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %23 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_dot4c_i32_i8_dpp %2, %6, %16 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %24 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_dot4c_i32_i8_dpp %2, %6, %17 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_dot4c_i32_i8_dpp %3, %6, %25 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %4, %7, %8 row_newbcast:" #BC0 " row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_mul_f32_dpp %5, %7, %9 row_newbcast:" #BC1 " row_mask:0xf bank_mask:0xf\n\t"                 \
+        "v_cvt_f32_i32 %0, %2\n\t"                                                                     \
+        "v_cvt_f32_i32 %1, %3\n\t"                                                                     \
+        "v_mul_f32 %0, %0, %4\n\t"                                                                     \
+        "v_mul_f32 %1, %1, %5"                                                                         \
+        : "=&v"(t0), "=&v"(t1), "=&v"(s0), "=&v"(s1), "=&v"(p0), "=&v"(p1)                             \
+        : "v"(x), "v"(dx8), "v"(dw0), "v"(dw1), "v"(a0.x), "v"(a0.y), "v"(a0.z), "v"(a0.w), "v"(a1.x),  \
+          "v"(a1.y), "v"(a1.z), "v"(a1.w), "v"(b0.x), "v"(b0.y), "v"(b0.z), "v"(b0.w), "v"(b1.x),       \
+          "v"(b1.y), "v"(b1.z), "v"(b1.w))
+    switch (i) {
+        case 0: Q8_PAIR_ASM(0, 1); break;
+        case 1: Q8_PAIR_ASM(2, 3); break;
+        case 2: Q8_PAIR_ASM(4, 5); break;
+        default: Q8_PAIR_ASM(6, 7); break;
+    }
+#undef Q8_PAIR_ASM
 }
 
 // Group sums with the activation quantization fused in: xv[m] holds lane l's
@@ -194,8 +216,8 @@ __device__ __forceinline__ void dot_pair(int &s0, int &s1, uint32_t x, const uin
 // Lane l quantizes values 4l..4l+3 (block l / 8) with exactly the arithmetic
 // of the standalone quantizer (bit-identical codes and scales, see
 // quantize4).  The packed codes are copied into every 16-lane row and fed to
-// v_dot4c by DPP broadcast; each block's activation scale comes from its
-// lane by v_readlane.
+// v_dot4c by DPP broadcast, and so are the blocks' activation scales to the
+// multiplies of the block terms.
 template <int M>
 __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 (&xv)[M], float (&u)[M]) {
     float dw[8];
@@ -207,17 +229,14 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 
         uint32_t x16[4];
         replicate_rows(quantize4(xv[m], d), x16);
         const float dxl = half_bits_to_float(float_to_half_bits(d));
+        // lane j of every row gets block (j & 7)'s scale, held by lane 8 (j & 7)
+        const float dx8 = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(32 * (int)(threadIdx.x & 7), __builtin_bit_cast(int, dxl)));
         float t[8];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            int s0 = 0, s1 = 0;
-            dot_pair(s0, s1, x16[i], g.c[4 * i], g.c[4 * i + 1], g.c[4 * i + 2], g.c[4 * i + 3]);
-            const float dx0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dxl), 16 * i));
-            const float dx1 =
-                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dxl), 16 * i + 8));
-            t[2 * i] = (float)s0 * (dw[2 * i] * dx0);
-            t[2 * i + 1] = (float)s1 * (dw[2 * i + 1] * dx1);
-        }
+        for (int i = 0; i < 4; i++)
+            block_pair_terms(t[2 * i], t[2 * i + 1], x16[i], dx8, dw[2 * i], dw[2 * i + 1], i, g.c[4 * i],
+                             g.c[4 * i + 1], g.c[4 * i + 2], g.c[4 * i + 3]);
         u[m] = tree8(t);
     }
 }
