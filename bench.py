@@ -137,7 +137,10 @@ def hbm_roofline(kernel, bytes_per_launch, avg_ms):
 
 # Kernel sources whose sha256 a committed profile summary must match before its
 # counter-derived traffic is reported.
-SEQ_SOURCES = ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp", "decode_q8_amd/csrc/layout.hpp"]
+SEQ_SOURCES = ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.hpp", "decode_q8_amd/csrc/layout.hpp",
+               "decode_q8_amd/csrc/device.hpp"]
+GEMV_SOURCES = ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp", "decode_q8_amd/csrc/layout.hpp",
+                "decode_q8_amd/csrc/device.hpp"]
 GEMM_SOURCES = ["decode_q8_amd/csrc/gemm.hip", "decode_q8_amd/csrc/gemm_loop.inc", "decode_q8_amd/csrc/gemm_strip.inc"]
 
 # Spread of the per-replay times of the most recent graph_time call (ms at the
@@ -550,8 +553,7 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
         roof["timing"] = ("one event pair around all launches of the step, queued ahead; per launch = total / "
                           "launches" if seq_ms is not None else "one event pair per launch, queued ahead")
         if step.fused and m == 1 and len(mats) == 65 and not rows:
-            roof["traffic"] = profiled_traffic("gemv_decode_step_llama1b.txt",
-                                               ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
+            roof["traffic"] = profiled_traffic("gemv_decode_step_llama1b.txt", GEMV_SOURCES)
     return base_record(args, metric, value, "GB/s", ms_per_step, "int8xint8->int32, fp32 scale/sum", config,
                        roof, cpu)
 
@@ -833,8 +835,7 @@ def bench_moe(args):
         "hip_graph": True,
     }
     roof = hbm_roofline("q8k::grouped_gemv_kernel", gu_bytes, float(ms[1]))
-    roof["traffic"] = profiled_traffic("grouped_gemv_moe.txt",
-                                       ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp"])
+    roof["traffic"] = profiled_traffic("grouped_gemv_moe.txt", GEMV_SOURCES)
     roof["note"] = ("the fused gate||up launch; its time includes the expert-grouping kernel that precedes the "
                     "GEMV in each call")
     return base_record(args, "Q8_0 routed-expert GEMV weight GB/s (%HBM peak)", value, "GB/s", ms_per_step,

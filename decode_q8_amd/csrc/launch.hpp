@@ -30,7 +30,9 @@ struct GemvPlan {
     size_t lds;        // dynamic LDS bytes per workgroup
     size_t workspace;  // bytes: tile counters + segment sums when wgs_per_tile > 1
 };
-GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k);
+// mf_min_rows: the threshold of the kernel that runs the plan (it decides
+// whether the MFMA form's LDS scratch is reserved).
+GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int mf_min_rows = GEMV_MF_MIN_ROWS);
 size_t gemv_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 hipError_t launch_gemv(const void *x_q, int64_t m, const void *w, int layout, int64_t n, int64_t k, float *y,

@@ -24,13 +24,16 @@ constexpr int GEMV_MAX_WAVES = 8;
 constexpr int64_t GEMV_LDS_LIMIT = 64 * 1024;
 // Activation rows from which a GEMV on packed weights takes the MFMA form
 // (the int8 block dots of all rows from one MFMA per block and 32 weight
-// rows) instead of a lane per weight row with every activation code
-// broadcast: from 3 rows in the per-matrix kernel and from 4 in the sequence
+// rows) instead of a lane per weight row with the activation codes broadcast
+// by DPP: from 7 rows in the per-matrix kernel and from 5 in the sequence
 // kernel, where the MFMA form runs with up to 256 registers (one workgroup per
-// CU, no spills) and the lane form with 128 (two per CU).  Measured; only
-// speed depends on it.
-constexpr int GEMV_MF_MIN_ROWS = 3;
-constexpr int SEQ_MF_MIN_ROWS = 4;
+// CU) and the lane form with 128 (two per CU, spilling more with every row).
+// Measured (decode step at m = 4 / 5: lane form 515 / 684 us, MFMA form
+// 596 / 614 us; one launch per matrix, the lane form is ahead up to m = 6);
+// only speed depends on it.  Each kernel's plan reserves the MFMA form's LDS
+// scratch from its own threshold.
+constexpr int GEMV_MF_MIN_ROWS = 7;
+constexpr int SEQ_MF_MIN_ROWS = 5;
 
 // Sequence workspace: [0, 4) status word; from byte 256 SEQ_CTR_PER_STEP
 // counters of SEQ_CTR_LINE bytes per step (the step's counter, then its

@@ -4,8 +4,6 @@
 #include "launch.hpp"
 #include "layout.hpp"
 
-static_assert(q8k::SEQ_MF_MIN_ROWS >= q8k::GEMV_MF_MIN_ROWS, "the plan reserves scratch from GEMV_MF_MIN_ROWS");
-
 namespace q8k {
 
 // Execution plan of a GEMV.  Only speed depends on it; every plan produces
@@ -13,7 +11,7 @@ namespace q8k {
 // tiles of narrow matrices are spread over one workgroup per segment so that
 // at least ~256 workgroups run; the group sums a workgroup keeps in LDS must
 // fit in 64 KB.
-GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k) {
+GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int mf_min_rows) {
     GemvPlan p;
     p.tiles = (n + TILE_ROWS - 1) / TILE_ROWS;
     p.groups = k / GROUP_K;
@@ -37,10 +35,10 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k) {
     if (waves < m) waves = m;
     p.waves = (int)waves;
     p.lds = (size_t)(gpw * m * TILE_ROWS) * sizeof(float);
-    // the MFMA form (packed weights, m >= GEMV_MF_MIN_ROWS): each of up to 8
-    // waves keeps the group's m rows of packed codes (m x 64 dwords) and 8 x 8
+    // the MFMA form (packed weights, m >= mf_min_rows): each of up to 8 waves
+    // keeps the group's m rows of packed codes (m x 64 dwords) and 8 x 8
     // activation scales after the group slots
-    if (m >= GEMV_MF_MIN_ROWS && m >= 2)
+    if (m >= mf_min_rows && m >= 2)
         p.lds += (size_t)GEMV_MAX_WAVES * (m * 64 + GROUP_BLOCKS * 8) * sizeof(uint32_t);
     p.workspace = 0;
     if (wgs > 1) p.workspace = (size_t)((p.tiles * 4 + 255) / 256 * 256) + (size_t)(S * m * n) * sizeof(float);
@@ -69,7 +67,7 @@ void seq_plan(const SeqHostStep *steps, int count, int64_t m, SeqPlan &P) {
     size_t off = flag_off + (size_t)SEQ_FLAG_LINES * SEQ_FLAG_LINE_BYTES;
     P.flag_off = (int32_t)flag_off;
     for (int i = 0; i < count; i++) {
-        const GemvPlan p = gemv_plan(m, steps[i].n, steps[i].k);
+        const GemvPlan p = gemv_plan(m, steps[i].n, steps[i].k, SEQ_MF_MIN_ROWS);
         const int64_t gpw = (int64_t)p.segs_per_wg * SEG_GROUPS < p.groups ? (int64_t)p.segs_per_wg * SEG_GROUPS
                                                                            : p.groups;
         if (gpw > SEQ_THREADS / 64) P.one = false;
