@@ -331,6 +331,16 @@ def oracle_rows(w: np.ndarray, threads: int) -> np.ndarray:
     return out
 
 
+def outputs_sha256(tensors) -> str:
+    """sha256 of the outputs' bytes, in order (the Ember post's trial method
+    records a hash of each mode's outputs next to its timing)."""
+    import hashlib
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.detach().contiguous().cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
 def cpu_model() -> str:
     """The host CPU's model name (/proc/cpuinfo), for the CPU baseline."""
     try:
@@ -461,6 +471,7 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
         step.run(stream)
     torch.cuda.synchronize()
     eager = [y.clone() for y in step.y]
+    eager_sha = outputs_sha256(eager)
     ms_per_step, graph = graph_time(step.run, stream, args.steps, args.warmup)
     for i, y in enumerate(step.y):
         if not torch.equal(y.view(torch.int32), eager[i].view(torch.int32)):
@@ -535,6 +546,11 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
     # of this run (per-launch breakdown, oracle, read ceiling) ran in between;
     # a spread above 2% flags the run as unstable
     controls = [ms_per_step, ctrl_ms, replay_ms(graph, args.steps)]
+    torch.cuda.synchronize()
+    final_sha = outputs_sha256(step.y)
+    if final_sha != eager_sha:
+        raise RuntimeError("the step's outputs after the timed replays differ from the first eager pass")
+    config["output_sha256"] = eager_sha
     spread = 100.0 * (max(controls) - min(controls)) / min(controls)
     config["control_ms_per_step"] = [round(c, 5) for c in controls]
     config["control_spread_pct"] = round(spread, 2)
@@ -660,8 +676,12 @@ def prefill_measure(args):
             raise RuntimeError(f"prefill M={c['m']} N={c['n']} K={c['k']}: outputs outside 1e-5*S of the oracle")
         pts.append((c, xa))
 
+    first_sha = outputs_sha256([c["y"] for c in cases])
     ms_per_step, graph = graph_time(run, stream, args.steps, args.warmup)
     ms = per_launch_ms(run, len(cases), stream, graph, reps=max(1, min(args.steps, 10)))
+    torch.cuda.synchronize()
+    if outputs_sha256([c["y"] for c in cases]) != first_sha:
+        raise RuntimeError("prefill outputs after the timed replays differ from the checked pass")
     ops = np.array([2.0 * c["m"] * c["n"] * c["k"] for c in cases])
     value = ops.sum() / (ms_per_step * 1e-3) / 1e12
     tops_by_case = {f"M{c['m']}_N{c['n']}_K{c['k']}": round(ops[i] / (ms[i] * 1e-3) / 1e12, 1)
@@ -705,6 +725,7 @@ def prefill_measure(args):
         "workload": "prefill GEMM: M in {188, 752, 2048} x (N, K) in {(2048, 2048), (8192, 2048), (2048, 8192)}, "
                     "Q8_0 packed weights, activations with 1% outlier channels x20",
         "oracle_check": "256 sampled outputs per shape within 1e-5 * sum|block terms|",
+        "output_sha256": first_sha,
         "order": [f"M{c['m']}_N{c['n']}_K{c['k']}" for c in cases], "order_seed": PREFILL_ORDER_SEED,
         "tops_by_case": tops_by_case, "rooflines": rooflines, "mfma_busy_pct": mfma_busy,
         "cpu_baseline": cpu, "step_spread_ms_p10_p50_p90": [STEP_SPREAD.get(q) for q in ("p10", "p50", "p90")],
@@ -718,7 +739,8 @@ def bench_prefill(args):
     roof["mfma_busy_pct"] = p["mfma_busy_pct"]
     config = {"workload": p["workload"], "ops_per_step": p["ops_per_step"],
               "frac_of_int8_peak": p["frac_of_int8_peak"], "tops_by_case": p["tops_by_case"],
-              "rooflines_by_kernel": p["rooflines"], "order": p["order"], "hip_graph": True}
+              "rooflines_by_kernel": p["rooflines"], "order": p["order"], "output_sha256": p["output_sha256"],
+              "hip_graph": True}
     return base_record(args, p["metric"], p["value"], "TOPS", p["ms_per_step"],
                        "int8xint8->int32 (MFMA), fp32 scale/sum", config, roof, p["cpu_baseline"])
 
