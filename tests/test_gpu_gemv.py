@@ -115,7 +115,7 @@ def test_repeatable():
 
 
 @pytest.mark.parametrize("n,k", [(64, 256), (512, 2048), (640, 7168), (2048, 8192), (65536, 256)])
-@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("m", [1, 3, 4, 6, 7, 8])
 def test_fused_quantization_bit_identical(m, n, k):
     """q8_quantize_matmul (quantization inside the GEMV) equals
     q8_quantize_rows + q8_matmul bitwise, in both layouts, with a row stride."""
