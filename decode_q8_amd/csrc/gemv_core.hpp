@@ -98,19 +98,31 @@ __device__ __forceinline__ void group_sums(const GroupRegs &g, const int8_t *con
 // sum n + 1 - 2^-25 still rounds (to nearest even) to n + 1.
 __device__ __forceinline__ int round_half_away(float q) { return (int)(q + __builtin_copysignf(0x1.fffffep-2f, q)); }
 
-// Lane l's four codes x / d, rounded half away from zero (0 when d == 0),
-// packed low byte first.  When every lane's d lies in [2^-96, 2^96] (the
-// test is wave-uniform) the four quotients share one reciprocal of d refined
-// by a Newton-Raphson step, and each is x * r corrected twice by its exact
-// fma residual (Markstein's method).  These are exactly the operations of the
-// compiler's correctly rounded fp32 division without its range-scaling steps,
-// and in this range those steps change nothing whenever the quotient can
-// round to a nonzero code (they act only on a zero or very small numerator or
-// a subnormal quotient, where both paths give code 0); so the codes equal
-// (int)roundf(x / d).  Otherwise the whole wave takes the IEEE division.
-__device__ __forceinline__ uint32_t quantize4(const float4 &v, float d) {
+// Lane l's block scale d = amax / 127 (amax over the block of the 8 aligned
+// lanes l & ~7, by an exact max butterfly) and its four codes x / d, rounded
+// half away from zero (0 when d == 0), packed low byte first.  When every
+// lane's amax lies in [2^-89, 2^96] (a wave-uniform test):
+//  - d is amax * y with y = RN(1/127), corrected once by its exact fma
+//    residual: with the correctly rounded reciprocal, one correction gives the
+//    correctly rounded quotient (Markstein's theorem; checked on the host for
+//    every fp32 significand);
+//  - the four quotients x / d share one reciprocal of d refined by a
+//    Newton-Raphson step, each corrected twice by its exact fma residual:
+//    exactly the operations of the compiler's correctly rounded fp32 division
+//    without its range-scaling steps, and for d in [2^-96, 2^89] those steps
+//    change nothing whenever the quotient can round to a nonzero code (they act
+//    only on a zero or very small numerator or a subnormal quotient, where both
+//    paths give code 0).
+// So d and the codes equal amax / 127 and (int)roundf(x / d).  Otherwise the
+// whole wave takes the IEEE divisions.
+__device__ __forceinline__ uint32_t quantize_block4(const float4 &v, float &d_out) {
+    const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    if (__builtin_amdgcn_ballot_w64(!(d >= 0x1p-96f && d <= 0x1p96f)) == 0) {
+    float d;
+    if (__builtin_amdgcn_ballot_w64(!(amax >= 0x1p-89f && amax <= 0x1p96f)) == 0) {
+        constexpr float y = 1.0f / 127.0f;
+        const float qd = amax * y;
+        d = fmaf(fmaf(-127.0f, qd, amax), y, qd);
         const float r0 = __builtin_amdgcn_rcpf(d);
         const float r = fmaf(fmaf(-d, r0, 1.0f), r0, r0);
         auto quot = [d, r](float x) {
@@ -122,22 +134,19 @@ __device__ __forceinline__ uint32_t quantize4(const float4 &v, float d) {
         q1 = round_half_away(quot(v.y));
         q2 = round_half_away(quot(v.z));
         q3 = round_half_away(quot(v.w));
-    } else if (d != 0.0f) {
-        q0 = (int)roundf(v.x / d);
-        q1 = (int)roundf(v.y / d);
-        q2 = (int)roundf(v.z / d);
-        q3 = (int)roundf(v.w / d);
+    } else {
+        d = amax / 127.0f;
+        if (d != 0.0f) {
+            q0 = (int)roundf(v.x / d);
+            q1 = (int)roundf(v.y / d);
+            q2 = (int)roundf(v.z / d);
+            q3 = (int)roundf(v.w / d);
+        }
     }
+    d_out = d;
     // low bytes of q0, q1 into bytes 0, 1 and of q2, q3 into bytes 2, 3 (v_perm_b32)
     return __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u) |
            __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x04000c0cu);
-}
-
-// Block scale of lane l's block (the 8 aligned lanes l & ~7): amax over the
-// block by an exact max butterfly, d = amax / 127 (IEEE division).
-__device__ __forceinline__ float block_scale(const float4 &v) {
-    const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    return amax / 127.0f;
 }
 
 // The wave's 64 packed code dwords (dword l in lane l) copied into every
@@ -215,7 +224,7 @@ __device__ __forceinline__ void block_pair_terms(float &t0, float &t1, uint32_t 
 // caller ahead of the weights, so the quantization does not wait for them).
 // Lane l quantizes values 4l..4l+3 (block l / 8) with exactly the arithmetic
 // of the standalone quantizer (bit-identical codes and scales, see
-// quantize4).  The packed codes are copied into every 16-lane row and fed to
+// quantize_block4).  The packed codes are copied into every 16-lane row and fed to
 // v_dot4c by DPP broadcast, and so are the blocks' activation scales to the
 // multiplies of the block terms.
 template <int M>
@@ -225,9 +234,9 @@ __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 
     for (int bb = 0; bb < 8; bb++) dw[bb] = half_bits_to_float(half_of(g.c[16], bb));
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const float d = block_scale(xv[m]);
+        float d;
         uint32_t x16[4];
-        replicate_rows(quantize4(xv[m], d), x16);
+        replicate_rows(quantize_block4(xv[m], d), x16);
         const float dxl = half_bits_to_float(float_to_half_bits(d));
         // lane j of every row gets block (j & 7)'s scale, held by lane 8 (j & 7)
         const float dx8 = __builtin_bit_cast(
@@ -446,8 +455,8 @@ __device__ __forceinline__ void quantize_group(const float4 (&xv)[M], uint32_t *
     float *sdx = reinterpret_cast<float *>(scr + M * 64);
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const float d = block_scale(xv[m]);
-        scr[m * 64 + lane] = quantize4(xv[m], d);
+        float d;
+        scr[m * 64 + lane] = quantize_block4(xv[m], d);
         if ((lane & 7) == 0) sdx[(lane >> 3) * 8 + m] = half_bits_to_float(float_to_half_bits(d));
     }
     // the wave's own LDS writes complete before its lanes read each other's
