@@ -23,8 +23,9 @@
 // counter sits in a 128-byte line of its own and is returned to zero by the
 // unit that completes it.  The unit that completes a step raises the step's
 // flag in FLAG_LINES separate lines with system-scope stores, and a waiting
-// workgroup polls "its" line (workgroup index mod FLAG_LINES, so roughly one
-// line per XCD) with system-scope loads: both bypass the per-XCD L2s, which
+// workgroup polls "its" line (workgroup index mod FLAG_LINES: with workgroups
+// dealt to the XCDs in turn, two lines per XCD and 32 pollers per line) with
+// system-scope loads: both bypass the per-XCD L2s, which
 // are not coherent with each other, and spreading the pollers over lines
 // keeps hundreds of them from queueing on one address (measured: polling the
 // counter itself with read-modify-writes made the step 2x slower).  The poll

@@ -39,7 +39,7 @@ constexpr int SEQ_MF_MIN_ROWS = 5;
 // counters of SEQ_CTR_LINE bytes per step (the step's counter, then its
 // sub-counters); SEQ_FLAG_LINES flag lines of SEQ_FLAG_LINE_BYTES from a
 // 4 KB-aligned offset; then the split steps' tile counters and segment sums.
-constexpr int SEQ_FLAG_LINES = 8;
+constexpr int SEQ_FLAG_LINES = 16;
 constexpr int SEQ_FLAG_LINE_BYTES = 4096;  // one int32 flag per step in each line
 constexpr int SEQ_NSUB = 16;               // sub-counters of a step with many units
 constexpr int SEQ_CTR_LINE = 128;          // bytes per counter
