@@ -142,6 +142,7 @@ SEQ_SOURCES = ["decode_q8_amd/csrc/gemv_seq.hip", "decode_q8_amd/csrc/gemv_core.
 GEMV_SOURCES = ["decode_q8_amd/csrc/gemv.hip", "decode_q8_amd/csrc/gemv_core.hpp", "decode_q8_amd/csrc/layout.hpp",
                 "decode_q8_amd/csrc/device.hpp"]
 GEMM_SOURCES = ["decode_q8_amd/csrc/gemm.hip", "decode_q8_amd/csrc/gemm_loop.inc", "decode_q8_amd/csrc/gemm_strip.inc"]
+READ_SOURCES = ["decode_q8_amd/csrc/measure.hip", "decode_q8_amd/csrc/device.hpp"]
 
 # Spread of the per-replay times of the most recent graph_time call (ms at the
 # 10th, 50th and 90th percentile), reported beside the mean in every record.
@@ -1070,7 +1071,8 @@ def bench_kv(args):
         "hip_graph": True,
     }
     roof = hbm_roofline("q8k::attn_partial_kernel + attn_combine_kernel", float(abytes), float(ms.mean()))
-    roof["traffic"] = profiled_traffic("attention_decode_kv.txt", "decode_q8_amd/csrc/kv.hip")
+    roof["traffic"] = profiled_traffic("attention_decode_kv.txt",
+                                       ["decode_q8_amd/csrc/kv.hip", "decode_q8_amd/csrc/device.hpp"])
     roof["note"] = "one attention call (the partial kernel and its small combine kernel), averaged over the 16 layers"
     return base_record(args, "Q8 KV-cache decode attention HBM GB/s (%HBM peak)", value, "GB/s", ms_per_step,
                        "int8 KV, fp32 softmax/accumulation", config, roof, cpu)
@@ -1132,7 +1134,8 @@ def bench_quantize(args):
     roof = hbm_roofline("q8k::quantize_kernel (row-contiguous weights)", float(bytes_q), ms_q)
     roof["timing"] = "one event pair around the graph replays of the single launch"
     roof["traffic"] = profiled_traffic("quantize_repack_lm_head.txt",
-                                       ["decode_q8_amd/csrc/quantize.hip", "decode_q8_amd/csrc/repack.hip"])
+                                       ["decode_q8_amd/csrc/quantize.hip", "decode_q8_amd/csrc/repack.hip",
+                                        "decode_q8_amd/csrc/device.hpp"])
     cpu = None
     if not args.no_cpu_baseline:
         rows = 4096
@@ -1189,7 +1192,7 @@ def bench_read(args):
     STEP_SPREAD.clear()
     STEP_SPREAD.update(spread)
     roof = hbm_roofline("q8k::stream_read_kernel", float(n), ms_per_step)
-    roof["traffic"] = profiled_traffic("stream_read_ceiling.txt", "decode_q8_amd/csrc/measure.hip")
+    roof["traffic"] = profiled_traffic("stream_read_ceiling.txt", READ_SOURCES)
     return base_record(args, "streaming-read GB/s", value, "GB/s", ms_per_step, "u8",
                        {"workload": "plain streaming read of 1 GiB (each byte once, 16-byte loads)",
                         "bytes_read": n, "other_sizes_GBs": others}, roof, None)

@@ -26,6 +26,24 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int c) {
     return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
 }
 
+// A 16-byte load with the non-temporal hint (global_load_dwordx4 ... nt), for
+// data read once per call, the weight stream: its lines are then the first
+// the caches give up, so they do not displace what many workgroups share
+// (activations, step counters and flags).  Measured on the decode step: 318
+// -> 306 us (m = 1), 637 -> 622 us (m = 8).  It lost where each 128-byte line
+// is read by several load instructions of one lane or wave, since the line
+// can then go between them: the row-layout weights (2x slower with it) and
+// the weight quantizer's input (10%) keep plain loads.
+__device__ __forceinline__ uint4 load_nt(const void *p) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The same hint as the cache-policy operand of __builtin_amdgcn_global_load_lds
+// (global_load_lds_dwordx4 ... nt).
+constexpr int CPOL_NT = 2;
+
 // Index of this wave in its workgroup, as a wave-uniform (SGPR) value so that
 // everything derived from it stays scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }

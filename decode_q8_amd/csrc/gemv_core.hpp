@@ -18,9 +18,12 @@ template <int LAYOUT>
 __device__ __forceinline__ void load_group(GroupRegs &g, const uint8_t *p) {
     if (LAYOUT == 1) {  // packed: p = record + lane * 16
 #pragma unroll
-        for (int i = 0; i < 16; i++) g.c[i] = *reinterpret_cast<const uint4 *>(p + i * 1024);
-        g.c[16] = *reinterpret_cast<const uint4 *>(p + RECORD_Q_BYTES);
+        for (int i = 0; i < 16; i++) g.c[i] = load_nt(p + i * 1024);
+        g.c[16] = load_nt(p + RECORD_Q_BYTES);
     } else {  // rows: p = this row's 272 bytes of the group (8 blocks of 34 bytes)
+        // plain loads: a lane reads each 128-byte line in eight 16-byte loads,
+        // and with the non-temporal hint the line is given up between them
+        // (measured: the decode step's GEMVs took twice as long)
 #pragma unroll
         for (int i = 0; i < 17; i++) g.c[i] = *reinterpret_cast<const uint4 *>(p + i * 16);
     }
@@ -355,10 +358,10 @@ __device__ __forceinline__ void load_group_mf(GroupRegsMF &g, const uint8_t *rec
 #pragma unroll
     for (int bb = 0; bb < GROUP_BLOCKS; bb++)
 #pragma unroll
-        for (int th = 0; th < 2; th++) g.c[2 * bb + th] = *reinterpret_cast<const uint4 *>(p + bb * 2048 + th * 512);
+        for (int th = 0; th < 2; th++) g.c[2 * bb + th] = load_nt(p + bb * 2048 + th * 512);
 #pragma unroll
     for (int th = 0; th < 2; th++)
-        g.c[16 + th] = *reinterpret_cast<const uint4 *>(rec + RECORD_Q_BYTES + (32 * th + (lane & 31)) * 16);
+        g.c[16 + th] = load_nt(rec + RECORD_Q_BYTES + (32 * th + (lane & 31)) * 16);
 }
 
 // Per-wave LDS scratch of the MFMA form: the M rows' packed codes as the lanes

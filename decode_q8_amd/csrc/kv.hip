@@ -228,6 +228,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
     const bool valid = lane < nv;
     // coalesced direct-to-LDS loads: each instruction moves 1 KB of whole rows
     // (rows past the valid ones repeat the last valid row: in bounds, masked).
+    // All four carry the non-temporal hint (the cache is read once per call):
+    // a decode step's attention 498 -> 461 us; on the code loads alone 466.
     // K and its scales first; V and its scales are issued once the lanes hold
     // their K rows, so they arrive while the scores are computed.
 #pragma unroll
@@ -236,11 +238,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
         const int r = p16 / W16, slot = p16 % W16;
         const int chunk = slot ^ (r & (W16 - 1));      // the K row chunk stored at this slot
         __builtin_amdgcn_global_load_lds(k_cache + (r0 + min(r, last)) * HD + chunk * 16,
-                                         (lds_ptr)(&kv[w][0] + 1024 * t), 16, 0, 0);
+                                         (lds_ptr)(&kv[w][0] + 1024 * t), 16, 0, CPOL_NT);
     }
 #pragma unroll
     for (int b = 0; b < NB; b++)
-        __builtin_amdgcn_global_load_lds(k_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&ksv[w][b][0]), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(k_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&ksv[w][b][0]), 4, 0, CPOL_NT);
     // the wave's own K loads have landed in LDS (nothing else touches its tiles)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
@@ -258,11 +260,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const float *__restri
         const int p16 = 64 * t + lane;
         const int r = p16 / W16, slot = p16 % W16;
         __builtin_amdgcn_global_load_lds(v_cache + (r0 + min(r, last)) * HD + slot * 16,
-                                         (lds_ptr)(&kv[w][0] + 1024 * t), 16, 0, 0);
+                                         (lds_ptr)(&kv[w][0] + 1024 * t), 16, 0, CPOL_NT);
     }
 #pragma unroll
     for (int b = 0; b < NB; b++)
-        __builtin_amdgcn_global_load_lds(v_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&ksv[w][b][0]), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(v_scale + (r0 + min(lane, last)) * NB + b, (lds_ptr)(&ksv[w][b][0]), 4, 0, CPOL_NT);
 
     // scores of this lane's key for the G heads, per 32-value block then scaled
     float sc[G];

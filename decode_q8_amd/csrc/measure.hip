@@ -14,9 +14,12 @@
 // span, so a 1 GiB read is 32,768 waves, many more than the GPU holds at once.
 // Measured shapes (waves per workgroup 4/8/16, spans of 16-64 KB) stay within
 // about 5% of each other at 36 MB, 279 MB and 1 GiB, none best at every size;
-// this one is within 1% of the best at 1 GiB.
+// this one is within 1% of the best at 1 GiB.  The loads carry the non-temporal hint, as the
+// weight loads of the GEMVs do: ~5% faster at 1 GiB (6.28 against 5.98 TB/s
+// by graph replay), so the ceiling is the faster form.
 #include <hip/hip_runtime.h>
 
+#include "device.hpp"
 #include "launch.hpp"
 
 namespace q8k {
@@ -37,7 +40,7 @@ __global__ __launch_bounds__(READ_THREADS) void stream_read_kernel(const uint4 *
 #pragma unroll
         for (int u = 0; u < READ_UNROLL; u++) {
             const int64_t i = base + (int64_t)(it * READ_UNROLL + u) * 64;
-            v[u] = i < chunks ? p[i] : make_uint4(0u, 0u, 0u, 0u);
+            v[u] = i < chunks ? load_nt(p + i) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < READ_UNROLL; u++) {

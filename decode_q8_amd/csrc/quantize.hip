@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
     float v[8];
     if (valid) {
         const float4 *p = reinterpret_cast<const float4 *>(x + r * ld_x + b * QK + sub * 8);
-        const float4 a0 = p[0], a1 = p[1];
+        const float4 a0 = p[0], a1 = p[1];  // plain loads: a line spans both (see load_nt)
         v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
         v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
     } else {
