@@ -57,7 +57,23 @@ namespace q8k {
 
 constexpr uint32_t SEQ_SPIN_LIMIT = 1u << 18;  // polls of roughly 1 us each
 constexpr int SEQ_SUB_MIN_UNITS = 64;  // more units than this: two-level counting
-constexpr uint32_t SEQ_PACE_TICKS = 150;  // prefetch stagger per wave, in 10 ns ticks of s_memrealtime
+// Prefetch stagger per wave, in 10 ns ticks of s_memrealtime: 0.75 us with
+// one activation row, 1.5 us with more (measured per row count: m = 1 306 ->
+// 301 us per decode step at 0.75 us; m = 2 and 4 slower by 2-3% there, m = 8
+// unchanged).
+template <int M>
+constexpr uint32_t seq_pace_ticks() { return M == 1 ? 75u : 150u; }
+
+// Whether a workgroup paces the weight loads of its unit of step p (its
+// previous unit was of step prev_p, -1 for none): when the unit is needed two
+// or more steps after the previous one, and with one activation row also for
+// the workgroup's first unit past step 0 (every workgroup fetches its first
+// unit at once at the start: 300.6 -> 299.4 us per decode step; with 4 rows
+// it cost 3%).
+template <int M>
+__device__ __forceinline__ bool paced(int prev_p, int p) {
+    return prev_p >= 0 ? p > prev_p + 1 : (M == 1 && p > 0);
+}
 constexpr int FLAG_LINES = SEQ_FLAG_LINES;
 constexpr int FLAG_LINE_BYTES = SEQ_FLAG_LINE_BYTES;
 constexpr int CTR_LINE = SEQ_CTR_LINE;
@@ -158,12 +174,12 @@ struct SeqHooks {
     const SeqArgs &a;
     int p, wg, u, units;
     bool ready;
-    bool pace;  // this unit's weights are needed a step or more after the workgroup's previous unit
+    bool pace;  // stagger this unit's weight loads over the waves (see paced())
     uint64_t t0;  // s_memrealtime when the workgroup took up the unit
     int32_t *status;
     __device__ void before() const {
-        if (pace) {  // wave w issues its weight loads w * SEQ_PACE_TICKS after the unit was taken up
-            const uint64_t until = t0 + (uint64_t)SEQ_PACE_TICKS * (threadIdx.x >> 6);
+        if (pace) {  // wave w issues its weight loads w * seq_pace_ticks<M>() after the unit was taken up
+            const uint64_t until = t0 + (uint64_t)seq_pace_ticks<M>() * (threadIdx.x >> 6);
             for (int i = 0; i < 4096 && __builtin_amdgcn_s_memrealtime() < until; i++) __builtin_amdgcn_s_sleep(2);
         }
     }
@@ -209,7 +225,7 @@ gemv_sequence_kernel(const SeqArgs a) {
             tile_unit<M, 1, float, ONE, SEQ_MF_MIN_ROWS>(st.x, st.ld_x, nullptr, st.w, st.n, st.k, st.y, st.ld_y, T, wi,
                                                         st.wgs,
                                         st.segs, ctr, part, lds_u, &last_wg, handover,
-                                        SeqHooks<M>{a, p, wg, u, units, ready, prev_p >= 0 && p > prev_p + 1,
+                                        SeqHooks<M>{a, p, wg, u, units, ready, paced<M>(prev_p, p),
                                                     __builtin_amdgcn_s_memrealtime(), status});
             prev_p = p;
             if constexpr (M > 1) finish_previous<M>(a, p, u, units);
