@@ -78,7 +78,7 @@ constexpr int FLAG_LINES = SEQ_FLAG_LINES;
 constexpr int FLAG_LINE_BYTES = SEQ_FLAG_LINE_BYTES;
 constexpr int CTR_LINE = SEQ_CTR_LINE;
 constexpr int CTR_PER_STEP = SEQ_CTR_PER_STEP;
-static_assert(SEQ_MAX_STEPS * 4 <= FLAG_LINE_BYTES, "a flag line holds every step's flag");
+static_assert(SEQ_MAX_STEPS * SEQ_FLAG_SLOT_BYTES <= FLAG_LINE_BYTES, "a flag line holds every step's flag");
 static_assert((SEQ_NSUB & (SEQ_NSUB - 1)) == 0 && SEQ_NSUB <= SEQ_SUB_MIN_UNITS, "every sub-counter has units");
 
 struct SeqStep {
@@ -105,7 +105,7 @@ __device__ __forceinline__ uint32_t *step_counter(uint8_t *ws, int p, int c) {
 }
 
 __device__ __forceinline__ uint32_t *step_flag(const SeqArgs &a, int line, int p) {
-    return reinterpret_cast<uint32_t *>(a.ws + a.flag_off + FLAG_LINE_BYTES * line + 4 * p);
+    return reinterpret_cast<uint32_t *>(a.ws + a.flag_off + FLAG_LINE_BYTES * line + SEQ_FLAG_SLOT_BYTES * p);
 }
 
 __device__ __forceinline__ uint32_t atomic_inc_old(uint32_t *c) {

@@ -39,8 +39,13 @@ constexpr int SEQ_MF_MIN_ROWS = 5;
 // counters of SEQ_CTR_LINE bytes per step (the step's counter, then its
 // sub-counters); SEQ_FLAG_LINES flag lines of SEQ_FLAG_LINE_BYTES from a
 // 4 KB-aligned offset; then the split steps' tile counters and segment sums.
+// A flag line holds one int32 flag per step, each alone in its own
+// SEQ_FLAG_SLOT_BYTES cache line: with the flags of consecutive steps packed
+// into one line, the polls of one step and the raising of the next met on it
+// (300.0 -> 291.7 us per decode step once spread).
 constexpr int SEQ_FLAG_LINES = 16;
-constexpr int SEQ_FLAG_LINE_BYTES = 4096;  // one int32 flag per step in each line
+constexpr int SEQ_FLAG_SLOT_BYTES = 128;
+constexpr int SEQ_FLAG_LINE_BYTES = 72 * SEQ_FLAG_SLOT_BYTES;  // every step of the longest sequence
 constexpr int SEQ_NSUB = 16;               // sub-counters of a step with many units
 constexpr int SEQ_CTR_LINE = 128;          // bytes per counter
 constexpr int SEQ_CTR_PER_STEP = SEQ_NSUB + 1;

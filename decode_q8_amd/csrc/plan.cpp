@@ -63,7 +63,7 @@ void seq_plan(const SeqHostStep *steps, int count, int64_t m, SeqPlan &P) {
     P.one = true;
     P.lds = 0;
     const size_t ctr_end = 256 + (size_t)SEQ_CTR_LINE * SEQ_CTR_PER_STEP * count;
-    const size_t flag_off = (ctr_end + SEQ_FLAG_LINE_BYTES - 1) / SEQ_FLAG_LINE_BYTES * SEQ_FLAG_LINE_BYTES;
+    const size_t flag_off = (ctr_end + 4095) / 4096 * 4096;
     size_t off = flag_off + (size_t)SEQ_FLAG_LINES * SEQ_FLAG_LINE_BYTES;
     P.flag_off = (int32_t)flag_off;
     for (int i = 0; i < count; i++) {
