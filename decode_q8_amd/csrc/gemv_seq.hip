@@ -60,9 +60,8 @@ constexpr int SEQ_SUB_MIN_UNITS = 64;  // more units than this: two-level counti
 // Prefetch stagger per wave, in 10 ns ticks of s_memrealtime: 0.65 us with
 // one activation row, 1.5 us with more.  Measured per row count (decode step,
 // same-box sweeps): m = 1 at 0.25 / 0.35 / 0.5 / 0.55 / 0.6 / 0.65 / 0.7 /
-// 0.75 / 1.0 / 1.5 us took 302 / 304 / 288 / 287 / 285.2 / 285.0 / 288 / 292
-// / 296 / 300 us; m = 2 and 4 were 3-4% slower at 0.75 us than at 1.5, m = 8
-// unchanged.
+// 0.75 / 1.0 us took 302 / 304 / 288 / 287 / 285.2 / 285.0 / 288 / 292 / 296
+// us; m = 2 and 4 were 3-4% slower at 0.75 us than at 1.5, m = 8 unchanged.
 template <int M>
 constexpr uint32_t seq_pace_ticks() { return M == 1 ? 65u : 150u; }
 
