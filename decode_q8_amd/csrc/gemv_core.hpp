@@ -118,38 +118,58 @@ __device__ __forceinline__ int round_half_away(float q) { return (int)(q + __bui
 //    paths give code 0).
 // So d and the codes equal amax / 127 and (int)roundf(x / d).  Otherwise the
 // whole wave takes the IEEE divisions.
-__device__ __forceinline__ uint32_t quantize_block4(const float4 &v, float &d_out) {
-    const float amax = max_over_8_lanes(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    float d;
-    if (__builtin_amdgcn_ballot_w64(!(amax >= 0x1p-89f && amax <= 0x1p96f)) == 0) {
+// quantize_rows4 does this for M activation rows at once (row m's values in
+// v[m]) with one range test over all of them, so the rows' dependency chains
+// have no branch between them and interleave; any row out of range sends all
+// M rows to the IEEE divisions, which give the same codes and scales where
+// the fast path applies.
+template <int M>
+__device__ __forceinline__ void quantize_rows4(const float4 (&v)[M], uint32_t (&q_out)[M], float (&d_out)[M]) {
+    float amax[M];
+    bool out_of_range = false;
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        amax[m] = max_over_8_lanes(fmaxf(fmaxf(fabsf(v[m].x), fabsf(v[m].y)), fmaxf(fabsf(v[m].z), fabsf(v[m].w))));
+        out_of_range |= !(amax[m] >= 0x1p-89f && amax[m] <= 0x1p96f);
+    }
+    int q[M][4];
+    if (__builtin_amdgcn_ballot_w64(out_of_range) == 0) {
         constexpr float y = 1.0f / 127.0f;
-        const float qd = amax * y;
-        d = fmaf(fmaf(-127.0f, qd, amax), y, qd);
-        const float r0 = __builtin_amdgcn_rcpf(d);
-        const float r = fmaf(fmaf(-d, r0, 1.0f), r0, r0);
-        auto quot = [d, r](float x) {
-            const float qa = x * r;
-            const float qb = fmaf(fmaf(-d, qa, x), r, qa);
-            return fmaf(fmaf(-d, qb, x), r, qb);
-        };
-        q0 = round_half_away(quot(v.x));
-        q1 = round_half_away(quot(v.y));
-        q2 = round_half_away(quot(v.z));
-        q3 = round_half_away(quot(v.w));
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float qd = amax[m] * y;
+            const float d = fmaf(fmaf(-127.0f, qd, amax[m]), y, qd);
+            const float r0 = __builtin_amdgcn_rcpf(d);
+            const float r = fmaf(fmaf(-d, r0, 1.0f), r0, r0);
+            auto quot = [d, r](float x) {
+                const float qa = x * r;
+                const float qb = fmaf(fmaf(-d, qa, x), r, qa);
+                return fmaf(fmaf(-d, qb, x), r, qb);
+            };
+            q[m][0] = round_half_away(quot(v[m].x));
+            q[m][1] = round_half_away(quot(v[m].y));
+            q[m][2] = round_half_away(quot(v[m].z));
+            q[m][3] = round_half_away(quot(v[m].w));
+            d_out[m] = d;
+        }
     } else {
-        d = amax / 127.0f;
-        if (d != 0.0f) {
-            q0 = (int)roundf(v.x / d);
-            q1 = (int)roundf(v.y / d);
-            q2 = (int)roundf(v.z / d);
-            q3 = (int)roundf(v.w / d);
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float d = amax[m] / 127.0f;
+            q[m][0] = q[m][1] = q[m][2] = q[m][3] = 0;
+            if (d != 0.0f) {
+                q[m][0] = (int)roundf(v[m].x / d);
+                q[m][1] = (int)roundf(v[m].y / d);
+                q[m][2] = (int)roundf(v[m].z / d);
+                q[m][3] = (int)roundf(v[m].w / d);
+            }
+            d_out[m] = d;
         }
     }
-    d_out = d;
-    // low bytes of q0, q1 into bytes 0, 1 and of q2, q3 into bytes 2, 3 (v_perm_b32)
-    return __builtin_amdgcn_perm((uint32_t)q1, (uint32_t)q0, 0x0c0c0400u) |
-           __builtin_amdgcn_perm((uint32_t)q3, (uint32_t)q2, 0x04000c0cu);
+#pragma unroll
+    for (int m = 0; m < M; m++)  // low bytes of q0, q1 into bytes 0, 1 and of q2, q3 into bytes 2, 3 (v_perm_b32)
+        q_out[m] = __builtin_amdgcn_perm((uint32_t)q[m][1], (uint32_t)q[m][0], 0x0c0c0400u) |
+                   __builtin_amdgcn_perm((uint32_t)q[m][3], (uint32_t)q[m][2], 0x04000c0cu);
 }
 
 // The wave's 64 packed code dwords (dword l in lane l) copied into every
@@ -227,20 +247,38 @@ __device__ __forceinline__ void block_pair_terms(float &t0, float &t1, uint32_t 
 // caller ahead of the weights, so the quantization does not wait for them).
 // Lane l quantizes values 4l..4l+3 (block l / 8) with exactly the arithmetic
 // of the standalone quantizer (bit-identical codes and scales, see
-// quantize_block4).  The packed codes are copied into every 16-lane row and fed to
+// quantize_rows4).  The packed codes are copied into every 16-lane row and fed to
 // v_dot4c by DPP broadcast, and so are the blocks' activation scales to the
 // multiplies of the block terms.
+constexpr int JOINT_QUANT_MAX_ROWS = 3;
+
 template <int M>
 __device__ __forceinline__ void group_sums_f32(const GroupRegs &g, const float4 (&xv)[M], float (&u)[M]) {
     float dw[8];
 #pragma unroll
     for (int bb = 0; bb < 8; bb++) dw[bb] = half_bits_to_float(half_of(g.c[16], bb));
+    // the rows' quantizations together (their chains interleave) where the
+    // registers allow it (m = 2 / 3 decode step 334 -> 330 / 378.5 -> 371 us);
+    // with 4 rows under the lane form's 128-register cap that spilled more and
+    // was slower (457 -> 470 us), so there each row is quantized right before
+    // its dots
+    constexpr int MQ = M <= JOINT_QUANT_MAX_ROWS ? M : 1;
+    uint32_t qm[M];
+    float dm[M];
+    if constexpr (MQ == M) quantize_rows4<M>(xv, qm, dm);
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        float d;
+        if constexpr (MQ != M) {
+            const float4 v1[1] = {xv[m]};
+            uint32_t q1[1];
+            float d1[1];
+            quantize_rows4<1>(v1, q1, d1);
+            qm[m] = q1[0];
+            dm[m] = d1[0];
+        }
         uint32_t x16[4];
-        replicate_rows(quantize_block4(xv[m], d), x16);
-        const float dxl = half_bits_to_float(float_to_half_bits(d));
+        replicate_rows(qm[m], x16);
+        const float dxl = half_bits_to_float(float_to_half_bits(dm[m]));
         // lane j of every row gets block (j & 7)'s scale, held by lane 8 (j & 7)
         const float dx8 = __builtin_bit_cast(
             float, __builtin_amdgcn_ds_bpermute(32 * (int)(threadIdx.x & 7), __builtin_bit_cast(int, dxl)));
@@ -456,11 +494,13 @@ __device__ __forceinline__ void quantize_group(const float4 (&xv)[M], uint32_t *
     // every lane has read the previous group's operands before they are overwritten
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     float *sdx = reinterpret_cast<float *>(scr + M * 64);
+    uint32_t qm[M];
+    float dm[M];
+    quantize_rows4<M>(xv, qm, dm);
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        float d;
-        scr[m * 64 + lane] = quantize_block4(xv[m], d);
-        if ((lane & 7) == 0) sdx[(lane >> 3) * 8 + m] = half_bits_to_float(float_to_half_bits(d));
+        scr[m * 64 + lane] = qm[m];
+        if ((lane & 7) == 0) sdx[(lane >> 3) * 8 + m] = half_bits_to_float(float_to_half_bits(dm[m]));
     }
     // the wave's own LDS writes complete before its lanes read each other's
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
