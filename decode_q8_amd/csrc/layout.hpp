@@ -51,7 +51,7 @@ constexpr int SEQ_CTR_LINE = 128;          // bytes per counter
 constexpr int SEQ_CTR_PER_STEP = SEQ_NSUB + 1;
 constexpr int SEQ_THREADS = 512;
 // The allocation-free sequence entry point's own workspace, per GPU (holds
-// the Llama-3.2-1B-shaped decode step's workspace up to m = 8, ~4.4 MB).
+// the Llama-3.2-1B-shaped decode step's workspace up to m = 8, ~4.5 MB).
 constexpr int64_t SEQ_SCRATCH_BYTES = 8ll << 20;
 
 // Decode attention: cached positions per workgroup
