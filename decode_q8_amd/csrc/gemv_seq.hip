@@ -22,7 +22,9 @@
 // incrementing one address queue up behind each other, sixteen do not.  Every
 // counter sits in a 128-byte line of its own and is returned to zero by the
 // unit that completes it.  The unit that completes a step raises the step's
-// flag in FLAG_LINES separate lines with system-scope stores, and a waiting
+// flag in FLAG_LINES separate lines with system-scope stores (in each line
+// every step's flag sits alone in a 128-byte slot, so the polls of one step
+// and the raising of the next never meet on a cache line), and a waiting
 // workgroup polls "its" line (workgroup index mod FLAG_LINES: with workgroups
 // dealt to the XCDs in turn, two lines per XCD and 32 pollers per line) with
 // system-scope loads: both bypass the per-XCD L2s, which
