@@ -459,6 +459,8 @@ class DecodeStep:
 
 def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
     import torch
+
+    from decode_q8_amd import q8
     t0 = time.time()
     rows = args.layout == "rows"
     mode = ("unfused" if args.unfused else
@@ -479,7 +481,7 @@ def bench_gemv_workload(args, mats, workload, m, label, allow_sequence=True):
             raise RuntimeError(f"graph replay output {i} differs from the eager step")
     if mode == "sequence":
         # a non-zero status word means a wait timed out: the outputs are undefined
-        status = int(step.seq_ws[:4].view(torch.int32).cpu()[0])
+        status = q8.sequence_status(step.seq_ws)
         if status != 0:
             raise RuntimeError(f"sequence status word {status}: a wait timed out, outputs undefined")
         # the one-launch step must equal the per-matrix launches bit for bit

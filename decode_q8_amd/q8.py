@@ -174,6 +174,19 @@ def q8_quantize_matmul_sequence(steps, m: int, workspace, workspace_bytes: int, 
                                                     _stream(stream)), "q8_quantize_matmul_sequence")
 
 
+def sequence_status(workspace) -> int:
+    """The status word a q8_quantize_matmul_sequence call left at byte 0 of its
+    workspace (waits for the current stream): 0, or Q8_ERR_LAUNCH when one of
+    the call's internal waits timed out, in which case its outputs are
+    undefined and the workspace must be zero-filled again before reuse."""
+    return int(workspace[:4].view(__import__("torch").int32).cpu()[0])
+
+
+def check_sequence(workspace, what: str = "q8_quantize_matmul_sequence") -> None:
+    """Raise Q8Error if the sequence call on this workspace reported a timeout."""
+    _check(sequence_status(workspace), what)
+
+
 def q8_quantize_matmul_sequence_noalloc(steps, m: int, status=None, stream=None) -> int:
     """steps: sequence of (x, ld_x, w, n, k, y, ld_y); the library's own
     per-GPU workspace; status: optional device int32 receiving the status word."""

@@ -43,6 +43,7 @@ def _run(steps, m, ws=None):
     if ws is None:
         ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     q8.q8_quantize_matmul_sequence(t, m, ws, ws.numel())
+    q8.check_sequence(ws)
     return ws
 
 
