@@ -439,3 +439,18 @@ def test_stream_read_validation():
     assert _raw(f, A, 1024, B + 2, None) == q8.Q8_ERR_ALIGN
     assert _raw(f, A, 1024, A + 512, None) == q8.Q8_ERR_ARG      # sink inside the buffer
     assert _raw(f, A, 0, B, None) == q8.Q8_OK                    # nothing to read: no-op, no launch
+
+
+def test_sequence_status_word_helpers():
+    """sequence_status reads the int32 at byte 0 of a sequence workspace;
+    check_sequence passes on 0 and raises Q8Error (Q8_ERR_LAUNCH) on a
+    timed-out wait (host tensors stand in for the device workspace)."""
+    import torch
+    ws = torch.zeros(256, dtype=torch.uint8)
+    assert q8.sequence_status(ws) == 0
+    q8.check_sequence(ws)
+    ws[:4].view(torch.int32)[0] = q8.Q8_ERR_LAUNCH
+    assert q8.sequence_status(ws) == q8.Q8_ERR_LAUNCH
+    with pytest.raises(q8.Q8Error) as e:
+        q8.check_sequence(ws)
+    assert e.value.status == q8.Q8_ERR_LAUNCH
