@@ -19,7 +19,7 @@
 // the step's counter when the step has at most SEQ_SUB_MIN_UNITS units, else
 // first in one of SEQ_NSUB sub-counters (unit u in sub-counter u mod SEQ_NSUB)
 // whose last unit then counts the sub-counter in -- hundreds of units
-// incrementing one address queue up behind each other, sixteen do not.  Every
+// incrementing one address queue up behind each other, a few do not.  Every
 // counter sits in a 128-byte line of its own and is returned to zero by the
 // unit that completes it.  The unit that completes a step raises the step's
 // flag in FLAG_LINES separate lines with system-scope stores (in each line

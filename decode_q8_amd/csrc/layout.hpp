@@ -46,12 +46,12 @@ constexpr int SEQ_MF_MIN_ROWS = 5;
 constexpr int SEQ_FLAG_LINES = 16;
 constexpr int SEQ_FLAG_SLOT_BYTES = 128;
 constexpr int SEQ_FLAG_LINE_BYTES = 72 * SEQ_FLAG_SLOT_BYTES;  // every step of the longest sequence
-constexpr int SEQ_NSUB = 16;               // sub-counters of a step with many units
+constexpr int SEQ_NSUB = 32;               // sub-counters of a step with many units (16: +1 us per decode step)
 constexpr int SEQ_CTR_LINE = 128;          // bytes per counter
 constexpr int SEQ_CTR_PER_STEP = SEQ_NSUB + 1;
 constexpr int SEQ_THREADS = 512;
 // The allocation-free sequence entry point's own workspace, per GPU (holds
-// the Llama-3.2-1B-shaped decode step's workspace up to m = 8, ~4.5 MB).
+// the Llama-3.2-1B-shaped decode step's workspace up to m = 8, ~4.6 MB).
 constexpr int64_t SEQ_SCRATCH_BYTES = 8ll << 20;
 
 // Decode attention: cached positions per workgroup

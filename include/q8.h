@@ -238,7 +238,7 @@ int q8_quantize_matmul_sequence(const q8_gemv_step *steps, int count, int64_t m,
  *            rules; q8_sequence_workspace_bytes(steps, count, m) must not
  *            exceed Q8_SEQUENCE_SCRATCH_BYTES (else Q8_ERR_WORKSPACE, before
  *            any HIP call).  The Llama-3.2-1B-shaped decode step needs about
- *            0.8 MB at m = 1 and 4.5 MB at m = 8.
+ *            1.0 MB at m = 1 and 4.6 MB at m = 8.
  *  status    device int32 or NULL: receives the call's status word (0, or
  *            Q8_ERR_LAUNCH if an internal wait timed out, which leaves the
  *            outputs undefined) when the call completes.  4-byte aligned,

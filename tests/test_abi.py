@@ -162,18 +162,18 @@ def _seq(steps, m, ws=D, wsb=1 << 30):
 def test_sequence_workspace_and_validation():
     down = (A, 8192, B, 2048, 8192, C, 2048)
     o = (A, 2048, B, 2048, 2048, C, 2048)
-    # status line, then 17 counters of 128 bytes per step (rounded up to 4 KB),
+    # status line, then 33 counters of 128 bytes per step (rounded up to 4 KB),
     # sixteen flag lines of 72 steps x 128 bytes (each step's flag in a cache
     # line of its own), then each split step's tile counters (256-byte
     # aligned) and segment sums
 
     def head(count):
-        return (256 + 17 * 128 * count + 4095) // 4096 * 4096 + 16 * 72 * 128
+        return (256 + 33 * 128 * count + 4095) // 4096 * 4096 + 16 * 72 * 128
 
-    assert q8.q8_sequence_workspace_bytes([o], 1) == head(1) == 4096 + 16 * 9216
+    assert q8.q8_sequence_workspace_bytes([o], 1) == head(1) == 8192 + 16 * 9216
     assert q8.q8_sequence_workspace_bytes([down], 1) == head(1) + 256 + 4 * 1 * 2048 * 4
     assert q8.q8_sequence_workspace_bytes([o, down, o], 2) == head(3) + 256 + 4 * 2 * 2048 * 4
-    assert q8.q8_sequence_workspace_bytes([o] * 16, 1) == head(16) == 36864 + 16 * 9216
+    assert q8.q8_sequence_workspace_bytes([o] * 16, 1) == head(16) == 69632 + 16 * 9216
     assert q8.q8_sequence_workspace_bytes([], 1) == 0
     assert q8.q8_sequence_workspace_bytes([o], 9) == 0
     assert _seq([], 1) == q8.Q8_ERR_ARG
